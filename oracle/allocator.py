@@ -1,0 +1,162 @@
+"""Block allocator model (oracle; test infrastructure only).
+
+What the pages fix:
+
+* The cache is split into fixed-size blocks of ``block_size`` token slots; a request's
+  tokens go into whatever blocks are free, and a per-request block table maps logical
+  block j to a physical block, like an OS page table ("KV Cache Optimization and
+  PagedAttention", prose on paging; "PagedAttention: Optimizing KV Cache Utilization in
+  Large Language Models", "The Mechanics of PagedAttention").
+* Blocks are granted on demand: a request holds one block and gets the next when that one
+  fills; the next need not be adjacent ("KV Cache Management", "The Solution:
+  PagedAttention (vLLM)").
+* Requests can point at the same physical blocks for a shared prefix, with
+  copy-on-write ("KV Cache Optimization and PagedAttention", prose on sharing;
+  "KV Cache Management", "The Bonus: Zero-Copy Sharing").
+* A batch can run out of blocks mid-generation; the caller must handle it
+  ("PagedAttention: ...", "Conclusion").
+
+Readings where the pages are silent (the plainest ones the rest supports):
+
+* Which free block is granted: a FIFO queue; grants pop the head, releases push to the
+  tail.  The initial order is given by the caller.
+* Slot of a token: ``physical_block * block_size + (position mod block_size)``.
+* Copy-on-write: when a token is appended into a partially filled last block that other
+  sequences also hold (refcount > 1), a fresh block is granted, the pair (old, new) is
+  reported so the caller copies the whole block, the old block loses one reference and the
+  new one replaces it in this sequence's table.  A shared block is never written.
+* Fork shares the parent's whole current block list (every block gains one reference).
+* Release walks the sequence's blocks in logical order; blocks whose refcount reaches 0
+  join the free queue tail in that order.
+* A multi-token append is all-or-nothing: if the free queue cannot cover it, nothing
+  changes and the exhaustion counter is incremented.
+"""
+
+from __future__ import annotations
+
+from collections import deque
+from dataclasses import dataclass, field
+
+
+class NoBlocks(Exception):
+    """Raised when the free queue cannot cover an append; the state is unchanged."""
+
+
+class InvalidOp(Exception):
+    """Raised for unknown/duplicate sequence ids; the state is unchanged."""
+
+
+@dataclass
+class _Seq:
+    blocks: list = field(default_factory=list)
+    n: int = 0
+
+
+class Allocator:
+    def __init__(self, num_blocks: int, block_size: int, initial_free_order=None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise InvalidOp("num_blocks and block_size must be positive")
+        order = list(range(num_blocks)) if initial_free_order is None else [int(b) for b in initial_free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise InvalidOp("initial free order must be a permutation of 0..num_blocks-1")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self.free = deque(order)
+        self.refcount = [0] * num_blocks
+        self.seqs: dict[int, _Seq] = {}
+        self.exhaustion_events = 0
+
+    # -- operations -------------------------------------------------------------------
+    def add(self, seq_id: int) -> None:
+        if seq_id in self.seqs:
+            raise InvalidOp(f"sequence {seq_id} already exists")
+        self.seqs[seq_id] = _Seq()
+
+    def _blocks_needed(self, s: _Seq, n_tokens: int) -> int:
+        bs = self.block_size
+        need = 0
+        if n_tokens > 0 and s.n % bs != 0 and self.refcount[s.blocks[-1]] > 1:
+            need += 1                                   # copy-on-write of the shared tail
+        for t in range(n_tokens):
+            if (s.n + t) % bs == 0:
+                need += 1                               # a fresh block for this token
+        return need
+
+    def append(self, seq_id: int, n_tokens: int):
+        """Append n_tokens to a sequence.  Returns (slots, cow_pairs)."""
+        if seq_id not in self.seqs:
+            raise InvalidOp(f"unknown sequence {seq_id}")
+        if n_tokens < 0:
+            raise InvalidOp("negative token count")
+        s = self.seqs[seq_id]
+        if self._blocks_needed(s, n_tokens) > len(self.free):
+            self.exhaustion_events += 1
+            raise NoBlocks(f"sequence {seq_id}: not enough free blocks")
+        bs = self.block_size
+        slots, cow = [], []
+        for _ in range(n_tokens):
+            if s.n % bs == 0:
+                b = self.free.popleft()
+                self.refcount[b] = 1
+                s.blocks.append(b)
+            elif self.refcount[s.blocks[-1]] > 1:
+                old = s.blocks[-1]
+                new = self.free.popleft()
+                self.refcount[old] -= 1
+                self.refcount[new] = 1
+                s.blocks[-1] = new
+                cow.append((old, new))
+            slots.append(s.blocks[-1] * bs + s.n % bs)
+            s.n += 1
+        return slots, cow
+
+    def fork(self, parent: int, child: int) -> None:
+        if parent not in self.seqs:
+            raise InvalidOp(f"unknown sequence {parent}")
+        if child in self.seqs:
+            raise InvalidOp(f"sequence {child} already exists")
+        p = self.seqs[parent]
+        for b in p.blocks:
+            self.refcount[b] += 1
+        self.seqs[child] = _Seq(blocks=list(p.blocks), n=p.n)
+
+    def release(self, seq_id: int) -> None:
+        if seq_id not in self.seqs:
+            raise InvalidOp(f"unknown sequence {seq_id}")
+        s = self.seqs.pop(seq_id)
+        for b in s.blocks:
+            self.refcount[b] -= 1
+            if self.refcount[b] == 0:
+                self.free.append(b)
+
+    # -- views ------------------------------------------------------------------------
+    def block_table(self, seq_ids, max_blocks: int):
+        """Rows of physical block ids padded with -1, and the token counts."""
+        tables, lens = [], []
+        for sid in seq_ids:
+            if sid not in self.seqs:
+                raise InvalidOp(f"unknown sequence {sid}")
+            s = self.seqs[sid]
+            if len(s.blocks) > max_blocks:
+                raise InvalidOp(f"sequence {sid} holds {len(s.blocks)} blocks > {max_blocks}")
+            tables.append(list(s.blocks) + [-1] * (max_blocks - len(s.blocks)))
+            lens.append(s.n)
+        return tables, lens
+
+    def stats(self) -> dict:
+        bs = self.block_size
+        used = sum(1 for r in self.refcount if r > 0)
+        waste = 0
+        for s in self.seqs.values():
+            waste += -(-s.n // bs) * bs - s.n            # final-block waste per holder
+        return {
+            "free": len(self.free),
+            "used": used,
+            "refs": sum(self.refcount),
+            "exhaustion_events": self.exhaustion_events,
+            "waste_slots": waste,
+        }
+
+    def dump(self):
+        """(refcounts, free queue in order) for bit-exact comparison."""
+        return list(self.refcount), list(self.free)

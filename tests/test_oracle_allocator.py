@@ -1,0 +1,139 @@
+"""Pins of the oracle's block allocator (CPU only): a hand-traced example of the rules,
+the invariants of refcounted sharing after every operation on seeded random traces, and
+all-or-nothing exhaustion."""
+
+import numpy as np
+import pytest
+
+from oracle import measures as M
+from oracle.allocator import Allocator, InvalidOp, NoBlocks
+
+
+def test_hand_traced_example():
+    """4 blocks of 2 slots, free order [2, 0, 3, 1]; every value below worked out by hand
+    from the rules (one block at a time, non-adjacent blocks, slot = block*bs + offset,
+    copy-on-write of a shared partial tail, release in logical order)."""
+    a = Allocator(4, 2, [2, 0, 3, 1])
+    a.add(1)
+    slots, cow = a.append(1, 3)          # block 2 (slots 4, 5), then block 0 (slot 0)
+    assert slots == [4, 5, 0] and cow == []
+    assert a.dump() == ([1, 0, 1, 0], [3, 1])
+    a.fork(1, 2)                         # both blocks now held twice
+    assert a.dump() == ([2, 0, 2, 0], [3, 1])
+    slots, cow = a.append(2, 1)          # tail block 0 is shared and partial -> COW to 3
+    assert slots == [7] and cow == [(0, 3)]
+    assert a.dump() == ([1, 0, 2, 1], [1])
+    slots, cow = a.append(1, 1)          # block 0 is private again: no copy
+    assert slots == [1] and cow == []
+    slots, cow = a.append(1, 1)          # block 0 full -> next free block 1
+    assert slots == [2] and cow == []
+    assert a.dump() == ([1, 1, 2, 1], [])
+    with pytest.raises(NoBlocks):
+        a.append(2, 2)                   # needs one more block, none free
+    assert a.dump() == ([1, 1, 2, 1], []) and a.stats()["exhaustion_events"] == 1
+    a.release(1)                         # blocks 2, 0, 1 lose a reference in logical order
+    assert a.dump() == ([0, 0, 1, 1], [0, 1])
+    t, L = a.block_table([2], 3)
+    assert t == [[2, 3, -1]] and L == [4]
+    a.release(2)
+    assert a.dump() == ([0, 0, 0, 0], [0, 1, 2, 3])
+
+
+def test_first_token_takes_one_block_next_block_when_full():
+    """A request is given one block; when it fills it gets a second, which need not be
+    adjacent to the first."""
+    a = Allocator(8, 16, [5, 2, 7, 0, 1, 3, 4, 6])
+    a.add(0)
+    s, _ = a.append(0, 1)
+    assert s == [5 * 16] and a.stats()["used"] == 1
+    s, _ = a.append(0, 15)
+    assert s == list(range(81, 96)) and a.stats()["used"] == 1
+    s, _ = a.append(0, 1)
+    assert s == [2 * 16] and a.stats()["used"] == 2
+
+
+def test_waste_stat_is_sum_of_paged_waste():
+    a = Allocator(100, 16)
+    lens = [1, 16, 17, 200, 31]
+    for i, L in enumerate(lens):
+        a.add(i)
+        a.append(i, L)
+    assert a.stats()["waste_slots"] == sum(M.paged_waste(L, 16) for L in lens)
+    assert a.stats()["waste_slots"] == 15 + 0 + 15 + 8 + 1
+
+
+def test_invalid_ops_leave_state_unchanged():
+    a = Allocator(4, 4)
+    a.add(0)
+    a.append(0, 5)
+    before = (a.dump(), {k: (list(v.blocks), v.n) for k, v in a.seqs.items()})
+    for bad in (lambda: a.add(0), lambda: a.append(9, 1), lambda: a.fork(9, 1),
+                lambda: a.fork(0, 0), lambda: a.release(9)):
+        with pytest.raises(InvalidOp):
+            bad()
+    assert before == (a.dump(), {k: (list(v.blocks), v.n) for k, v in a.seqs.items()})
+
+
+def check_invariants(a: Allocator):
+    bs = a.block_size
+    held = [b for s in a.seqs.values() for b in s.blocks]
+    # every reference is a block-table entry of some sequence
+    assert sum(a.refcount) == len(held)
+    for b in range(a.num_blocks):
+        assert a.refcount[b] == held.count(b)
+    # free and used partition the pool
+    free = list(a.free)
+    assert len(set(free)) == len(free)
+    assert set(free) == {b for b in range(a.num_blocks) if a.refcount[b] == 0}
+    # a sequence holds exactly ceil(n / bs) blocks
+    for s in a.seqs.values():
+        assert len(s.blocks) == -(-s.n // bs)
+        assert len(set(s.blocks)) == len(s.blocks)
+
+
+def random_trace(seed, n_ops=400, num_blocks=48, bs=4):
+    """Seeded random operations; returns the list of (op, args, outcome)."""
+    rng = np.random.default_rng(seed)
+    a = Allocator(num_blocks, bs, rng.permutation(num_blocks))
+    live, next_id, log = [], 0, []
+    for _ in range(n_ops):
+        r = rng.random()
+        try:
+            if r < 0.15 or not live:
+                a.add(next_id); live.append(next_id); log.append(("add", next_id, None)); next_id += 1
+            elif r < 0.65:
+                s = int(rng.choice(live)); n = int(rng.integers(1, 3 * bs))
+                slots, cow = a.append(s, n)
+                log.append(("append", (s, n), (slots, cow)))
+                # written slots are never in a block held by another sequence
+                for sl in slots:
+                    assert a.refcount[sl // bs] == 1
+            elif r < 0.8:
+                p = int(rng.choice(live)); a.fork(p, next_id); live.append(next_id)
+                log.append(("fork", (p, next_id), None)); next_id += 1
+            else:
+                s = int(rng.choice(live)); a.release(s); live.remove(s); log.append(("free", s, None))
+        except NoBlocks:
+            log.append(("noblocks", None, a.dump()))
+        check_invariants(a)
+    return a, log
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_traces_keep_invariants(seed):
+    a, log = random_trace(seed)
+    assert any(op == "noblocks" for op, _, _ in log) or seed > 2  # small pools hit exhaustion
+    assert any(op == "append" and out[1] for op, _, out in log)    # some copy-on-write happened
+
+
+def test_slots_are_unique_among_live_tokens():
+    """No two live (sequence, position) pairs that are not shared map to one slot: every
+    sequence's slots for positions it wrote privately are distinct from all others'."""
+    a = Allocator(64, 4, np.random.default_rng(0).permutation(64))
+    owner = {}
+    for s in range(6):
+        a.add(s)
+        slots, _ = a.append(s, 7 + s)
+        for sl in slots:
+            assert sl not in owner
+            owner[sl] = s
