@@ -1,0 +1,224 @@
+/*
+ * pagedkv.h -- C ABI of the paged KV-cache library for AMD Instinct MI355X (gfx950).
+ *
+ * The method (web pages, cited by title and section):
+ *  - "KV Cache Optimization and PagedAttention" (cracklab.in): each token's K and V are
+ *    stored once and reused by every later token; the cache is split into small
+ *    fixed-size blocks held in whatever physical blocks are free, with a per-request block
+ *    table mapping logical to physical blocks like an OS page table; requests with a common
+ *    prefix can point at the same physical blocks (copy-on-write).
+ *  - "PagedAttention: Optimizing KV Cache Utilization in Large Language Models"
+ *    (fromzero2ai.dev): "The Mechanics of PagedAttention" (logical blocks, physical
+ *    blocks, page table; blocks granted as tokens are generated, K/V written into scattered
+ *    blocks), "The Math: Block Attention Calculation" (softmax(q.K^T / sqrt(d_k)) with the
+ *    keys located through the page table), "Conclusion" (blocks can run out
+ *    mid-generation; block size trades table lookups against final-block waste).
+ *  - "KV Cache Management" (ai360xpert.com): "The Solution: PagedAttention (vLLM)" (one
+ *    block at a time, the next need not be adjacent), "The Bonus: Zero-Copy Sharing",
+ *    "What to Read Next" (8-bit KV cache).
+ *
+ * Conventions shared by every entry point
+ *  - All functions return PA_OK (0) or a negative status; on a negative status
+ *    pa_last_error() returns a message for the calling thread and nothing was enqueued
+ *    (device calls) or changed (allocator calls).
+ *  - Device pointers are borrowed for the duration of the enqueued work only; the caller
+ *    owns every buffer and keeps it alive until the stream has passed the call.  The
+ *    library allocates no device memory.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the null stream.  Work is enqueued
+ *    asynchronously; launch failures return PA_ERR_DEVICE.
+ *  - Tensors are dense and row-major (C order) in the shapes stated; device pointers must
+ *    be 16-byte aligned.
+ *
+ * Cache layout (the pages fix none): k_cache and v_cache are each
+ *     [num_blocks][num_kv_heads][block_size][head_dim]
+ * of the cache storage type; token slot s lives in block s / block_size at row
+ * s % block_size.  One (block, head) tile is one contiguous span of
+ * block_size * head_dim elements.
+ *
+ * Supported combinations (others return PA_ERR_UNSUPPORTED):
+ *   (q / K,V input / out, cache) in {(f32, f32), (bf16, bf16), (bf16, fp8 e4m3)},
+ *   head_dim in {64, 128}, block_size in {8, 16, 32, 128},
+ *   num_q_heads / num_kv_heads in {1, 4, 8}.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status and types */
+
+#define PA_OK               0
+#define PA_ERR_INVALID     -1   /* bad argument: shape, pointer, id, contract violation  */
+#define PA_ERR_UNSUPPORTED -2   /* valid but not built: dtype / head_dim / block / group */
+#define PA_ERR_NO_BLOCKS   -3   /* the allocator's free queue cannot cover the request   */
+#define PA_ERR_DEVICE      -4   /* a HIP runtime call or kernel launch failed            */
+
+#define PA_DTYPE_F32      0     /* IEEE binary32                                          */
+#define PA_DTYPE_BF16     1     /* bfloat16                                               */
+#define PA_DTYPE_FP8_E4M3 2     /* OCP FP8 E4M3FN (bias 7, max 448, no inf), cache only   */
+
+/* Message describing the last non-OK status returned on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/* Library ABI version; bumped on any signature change. */
+int32_t pa_abi_version(void);
+
+/* ---------------------------------------------------------------- KV write
+ *
+ * Slot-mapped write of new tokens' K and V into their physical blocks ("The Mechanics of
+ * PagedAttention": the K/V vectors are written into the blocks even when those are
+ * scattered).  For every token t with slot_mapping[t] >= 0 and every KV head h:
+ *     k_cache[s / block_size][h][s % block_size][:] = enc_h(k[t][h][:]),  s = slot_mapping[t]
+ * and the same for v.  enc is a bit copy when cache_dtype == in_dtype; for an fp8 cache
+ * (in_dtype bf16) enc_h(x) = e4m3_round_nearest_even_saturate(float32(x / k_scale[h]))
+ * (v_scale for v): the float32 quotient is correctly rounded, magnitudes beyond 448
+ * saturate to 448, NaN stays NaN.
+ *
+ *  k, v          device, [num_tokens][num_kv_heads][head_dim] of in_dtype
+ *  slot_mapping  device, int64 [num_tokens]; < 0 means "skip this token" (padding)
+ *  k_cache, v_cache  device, cache layout above, of cache_dtype
+ *  k_scale, v_scale  device, float32 [num_kv_heads]; required for an fp8 cache, else NULL
+ *
+ * Contract (not checked on the device; out-of-range slots are skipped, never written):
+ * slots are < num_blocks * block_size and pairwise distinct within one call.  The write
+ * never touches a slot that is not listed.
+ */
+int pa_kv_write(const void* k, const void* v, const int64_t* slot_mapping, int64_t num_tokens,
+                void* k_cache, void* v_cache, int64_t num_blocks, int32_t num_kv_heads,
+                int32_t head_dim, int32_t block_size, int32_t in_dtype, int32_t cache_dtype,
+                const float* k_scale, const float* v_scale, void* stream);
+
+/* ---------------------------------------------------------------- decode attention
+ *
+ * Decode attention through the block table ("The Math: Block Attention Calculation").
+ * For request b with L = seq_lens[b] cached tokens (the new token included) and query head
+ * h, with KV head g = h / (num_q_heads / num_kv_heads):
+ *     K_j = dec(k_cache[block_tables[b][j / block_size]][g][j % block_size][:]),  j < L
+ *     s_j = scale * <q[b][h][:], K_j>
+ *     out[b][h][:] = sum_j softmax(s)_j * V_j            (one softmax over all L keys)
+ * dec is exact (fp8: e4m3 value times k_scale[g] / v_scale[g]).  Scores, softmax and the
+ * weighted sum are accumulated in float32; out is rounded to nearest even in q's dtype.
+ * L = 0 gives out = 0.  Slots at positions >= L are never read (they may hold anything).
+ *
+ * Long contexts are split into partitions of `partition_tokens` logical tokens (rounded up
+ * to a multiple of max(64, block_size); 0 means 512); each partition is reduced to
+ * (max score, sum of exponentials, unnormalised weighted sum) and the partitions are
+ * merged by rescaling to the largest maximum (log-sum-exp).  The result depends only on
+ * logical positions, so it is bit-identical under any physical placement of the blocks.
+ *
+ *  out           device, [num_seqs][num_q_heads][head_dim] of q_dtype
+ *  q             device, [num_seqs][num_q_heads][head_dim] of q_dtype
+ *  k_cache, v_cache  device, cache layout above, num_blocks blocks, of cache_dtype
+ *  block_tables  device, int32 [num_seqs][max_blocks_per_seq]; entries past
+ *                ceil(L / block_size) are ignored
+ *  seq_lens      device, int32 [num_seqs]
+ *  max_seq_len   host upper bound of seq_lens (sizes the grid and the workspace)
+ *  workspace     device scratch of at least pa_decode_workspace_bytes(...) bytes, or NULL
+ *                (then each request is reduced in a single partition, which is correct but
+ *                slow for long contexts)
+ *
+ * Device-side faults are turned into loud results instead of out-of-bounds accesses: a
+ * request whose L exceeds max_seq_len or max_blocks_per_seq * block_size, or whose table
+ * holds a block id outside [0, num_blocks) within its first ceil(L / block_size) entries,
+ * gets out = NaN for all its heads.
+ */
+int64_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_seq_len, int32_t partition_tokens,
+                                  int32_t block_size);
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* seq_lens, float scale,
+              int32_t block_size, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+              int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq,
+              int32_t max_seq_len, int32_t q_dtype, int32_t cache_dtype,
+              const float* k_scale, const float* v_scale,
+              void* workspace, int64_t workspace_bytes, int32_t partition_tokens, void* stream);
+
+/* ---------------------------------------------------------------- block copy
+ *
+ * Whole-block copies for copy-on-write ("KV Cache Optimization and PagedAttention", prose
+ * on shared prefix blocks and copy-on-write): for each pair i,
+ *     k_cache[src_dst[2i+1]] = k_cache[src_dst[2i]]   (all heads, rows and dims), same for v.
+ *  src_dst  device, int64 [num_pairs][2] (src, dst); destinations pairwise distinct and
+ *           never a source of another pair in the same call; pairs with an id outside
+ *           [0, num_blocks) are skipped.
+ */
+int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst, int32_t num_pairs,
+                   int64_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t block_size, int32_t cache_dtype, void* stream);
+
+/* ---------------------------------------------------------------- host block allocator
+ *
+ * CPU-only bookkeeping of the block pool; never touches the device.  One handle is used
+ * by one thread at a time.  Rules:
+ *  - a free FIFO queue (initial order given, identity if NULL); grants pop the head,
+ *    releases push to the tail ("whatever blocks are free");
+ *  - blocks are granted on demand: appending token n of a sequence takes a new block when
+ *    n % block_size == 0 ("The Solution: PagedAttention (vLLM)");
+ *  - slot of token n = block * block_size + n % block_size;
+ *  - fork(parent, child) makes child share all of parent's blocks (refcount + 1 each)
+ *    ("The Bonus: Zero-Copy Sharing");
+ *  - copy-on-write: appending into a partially filled last block with refcount > 1 first
+ *    moves the sequence to a fresh block and reports the (old, new) pair, which the caller
+ *    copies with pa_copy_blocks before writing; shared blocks are never written;
+ *  - free(seq) drops one reference of each of its blocks in logical order; blocks reaching
+ *    zero join the free queue tail in that order;
+ *  - any operation that cannot be completed (PA_ERR_NO_BLOCKS, unknown or duplicate ids)
+ *    changes nothing; PA_ERR_NO_BLOCKS also counts one exhaustion event ("Conclusion":
+ *    blocks can run out mid-generation; preemption is the caller's decision).
+ */
+typedef struct pa_allocator pa_allocator;
+
+typedef struct {
+    int64_t free_blocks;        /* blocks in the free queue                              */
+    int64_t used_blocks;        /* blocks with refcount > 0                              */
+    int64_t total_refs;         /* sum of refcounts = total block-table entries          */
+    int64_t exhaustion_events;  /* appends refused with PA_ERR_NO_BLOCKS                 */
+    int64_t waste_slots;        /* sum over sequences of ceil(n/bs)*bs - n               */
+    int64_t num_seqs;           /* live sequences                                        */
+} pa_alloc_stats_t;
+
+/* num_blocks > 0, block_size > 0; initial_free_order: host int32 [num_blocks], a
+ * permutation of 0..num_blocks-1, or NULL.  *out receives a handle owned by the caller. */
+int pa_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* initial_free_order,
+                    pa_allocator** out);
+void pa_alloc_destroy(pa_allocator* a);
+
+int pa_seq_add(pa_allocator* a, int64_t seq_id);
+
+/* Append n_tokens to one sequence.  slots_out: host int64 [n_tokens]; cow_out: host int64
+ * [2] receiving (src, dst) when *n_cow_out == 1 (at most one copy per append). */
+int pa_seq_append(pa_allocator* a, int64_t seq_id, int32_t n_tokens, int64_t* slots_out,
+                  int64_t* cow_out, int32_t* n_cow_out);
+
+/* Append n_tokens[i] to each of n_seqs distinct sequences, in order, all or nothing.
+ * slots_out: host int64 [sum n_tokens] (sequence-major); cow_out: host int64
+ * [2 * n_seqs]; *n_cow_out receives the number of (src, dst) pairs written. */
+int pa_batch_append(pa_allocator* a, const int64_t* seq_ids, const int32_t* n_tokens,
+                    int32_t n_seqs, int64_t* slots_out, int64_t* cow_out, int32_t* n_cow_out);
+
+int pa_seq_fork(pa_allocator* a, int64_t parent, int64_t child);
+int pa_seq_free(pa_allocator* a, int64_t seq_id);
+
+/* Rows of physical block ids for the given sequences, padded with -1, and their token
+ * counts.  tables_out: host int32 [n_seqs][max_blocks]; seq_lens_out: host int32 [n_seqs].
+ * PA_ERR_INVALID if a sequence holds more than max_blocks blocks. */
+int pa_block_tables(const pa_allocator* a, const int64_t* seq_ids, int32_t n_seqs,
+                    int32_t max_blocks, int32_t* tables_out, int32_t* seq_lens_out);
+
+int pa_alloc_stats(const pa_allocator* a, pa_alloc_stats_t* out);
+
+/* Full state for comparison: refcounts [num_blocks], free queue in order (n_free entries
+ * of a buffer of num_blocks). */
+int pa_alloc_dump(const pa_allocator* a, int32_t* refcounts, int32_t* free_order,
+                  int32_t* n_free);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

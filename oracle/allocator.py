@@ -110,6 +110,25 @@ class Allocator:
             s.n += 1
         return slots, cow
 
+    def append_batch(self, seq_ids, n_tokens):
+        """Appends to several distinct sequences in order, all or nothing: the appends are
+        tried on a copy of the state, which replaces the state only if all succeed."""
+        import copy
+        if len(set(seq_ids)) != len(seq_ids):
+            raise InvalidOp("a sequence is listed twice")
+        trial = copy.deepcopy(self)
+        slots, cow = [], []
+        try:
+            for s, n in zip(seq_ids, n_tokens):
+                sl, cw = trial.append(s, n)
+                slots += sl
+                cow += cw
+        except NoBlocks:
+            self.exhaustion_events += 1
+            raise
+        self.__dict__.update(trial.__dict__)
+        return slots, cow
+
     def fork(self, parent: int, child: int) -> None:
         if parent not in self.seqs:
             raise InvalidOp(f"unknown sequence {parent}")

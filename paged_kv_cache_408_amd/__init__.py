@@ -1,0 +1,13 @@
+"""Paged KV cache for AMD Instinct MI355X (gfx950): slot-mapped KV write, split-K paged
+decode attention, whole-block copy-on-write and a host block allocator, behind the C ABI
+of include/pagedkv.h (libpagedkv.so, built in-tree by ``_build.py``).
+
+The names below are the C ABI's; the binding only marshals arguments.
+"""
+
+from ._lib import (  # noqa: F401
+    EXPORTED, LIB_PATH, PA_DTYPE_BF16, PA_DTYPE_F32, PA_DTYPE_FP8_E4M3, Allocator, NoBlocksError,
+    PagedKVError, UnsupportedError, load, pa_alloc_create, pa_alloc_destroy, pa_alloc_dump,
+    pa_alloc_stats, pa_batch_append, pa_block_tables, pa_copy_blocks, pa_decode,
+    pa_decode_workspace_bytes, pa_kv_write, pa_seq_add, pa_seq_append, pa_seq_fork, pa_seq_free,
+)

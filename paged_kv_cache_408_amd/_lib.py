@@ -1,0 +1,331 @@
+"""ctypes binding of libpagedkv.so: the C ABI of include/pagedkv.h under the same names.
+
+Argument marshalling only: tensors become (data pointer, sizes); the stream is torch's
+current HIP stream; every step of the computation runs in the library's kernels.  Loading
+fails loudly when the library has not been built; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_NO_BLOCKS, PA_ERR_DEVICE = 0, -1, -2, -3, -4
+PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_FP8_E4M3 = 0, 1, 2
+
+EXPORTED = [
+    "pa_last_error", "pa_abi_version", "pa_kv_write", "pa_decode_workspace_bytes", "pa_decode",
+    "pa_copy_blocks", "pa_alloc_create", "pa_alloc_destroy", "pa_seq_add", "pa_seq_append",
+    "pa_batch_append", "pa_seq_fork", "pa_seq_free", "pa_block_tables", "pa_alloc_stats",
+    "pa_alloc_dump",
+]
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+class NoBlocksError(PagedKVError):
+    """The allocator's free queue cannot cover the request (state unchanged)."""
+
+
+class UnsupportedError(PagedKVError):
+    pass
+
+
+class pa_alloc_stats_t(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in
+                ("free_blocks", "used_blocks", "total_refs", "exhaustion_events", "waste_slots", "num_seqs")]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load (once) and return the library handle; raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m paged_kv_cache_408_amd._build` "
+                          "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    sig = {
+        "pa_last_error": (ctypes.c_char_p, []),
+        "pa_abi_version": (I32, []),
+        "pa_kv_write": (ctypes.c_int, [P, P, P, I64, P, P, I64, I32, I32, I32, I32, I32, P, P, P]),
+        "pa_decode_workspace_bytes": (I64, [I32, I32, I32, I32, I32, I32]),
+        "pa_decode": (ctypes.c_int, [P, P, P, P, P, P, F32, I32, I32, I32, I32, I32, I64, I32, I32, I32, I32,
+                                     P, P, P, I64, I32, P]),
+        "pa_copy_blocks": (ctypes.c_int, [P, P, P, I32, I64, I32, I32, I32, I32, P]),
+        "pa_alloc_create": (ctypes.c_int, [I32, I32, P, ctypes.POINTER(P)]),
+        "pa_alloc_destroy": (None, [P]),
+        "pa_seq_add": (ctypes.c_int, [P, I64]),
+        "pa_seq_append": (ctypes.c_int, [P, I64, I32, P, P, P]),
+        "pa_batch_append": (ctypes.c_int, [P, P, P, I32, P, P, P]),
+        "pa_seq_fork": (ctypes.c_int, [P, I64, I64]),
+        "pa_seq_free": (ctypes.c_int, [P, I64]),
+        "pa_block_tables": (ctypes.c_int, [P, P, I32, I32, P, P]),
+        "pa_alloc_stats": (ctypes.c_int, [P, ctypes.POINTER(pa_alloc_stats_t)]),
+        "pa_alloc_dump": (ctypes.c_int, [P, P, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc == PA_OK:
+        return
+    msg = load().pa_last_error().decode()
+    cls = NoBlocksError if rc == PA_ERR_NO_BLOCKS else UnsupportedError if rc == PA_ERR_UNSUPPORTED else PagedKVError
+    raise cls(rc, msg)
+
+
+# --------------------------------------------------------------------------- device ops
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t, what):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PA_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return PA_DTYPE_BF16
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return PA_DTYPE_FP8_E4M3
+    raise TypeError(f"{what}: unsupported dtype {t.dtype}")
+
+
+def _dev(t, what):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def pa_kv_write(k, v, slot_mapping, k_cache, v_cache, *, k_scale=None, v_scale=None, stream=None,
+                validate=False):
+    """Write new tokens' K/V rows (k, v: [T, Hkv, d]) into caches [N, Hkv, bs, d] at the
+    int64 slots in slot_mapping (< 0 = skip)."""
+    torch = _torch()
+    T, H, d = k.shape
+    N, Hc, bs, dc = k_cache.shape
+    if v.shape != k.shape or v_cache.shape != k_cache.shape or (Hc, dc) != (H, d):
+        raise ValueError(f"shape mismatch: k {tuple(k.shape)} v {tuple(v.shape)} caches {tuple(k_cache.shape)}")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be int64 [num_tokens]")
+    if validate:
+        s = slot_mapping.cpu().numpy()
+        live = s[s >= 0]
+        if live.size and (live.max() >= N * bs or len(np.unique(live)) != live.size):
+            raise ValueError("slot_mapping holds out-of-range or duplicate slots")
+    rc = load().pa_kv_write(_dev(k, "k"), _dev(v, "v"), _dev(slot_mapping, "slot_mapping"), T,
+                            _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), N, H, d, bs,
+                            _dtype_code(k, "k"), _dtype_code(k_cache, "k_cache"),
+                            _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _stream(stream))
+    _check(rc)
+
+
+def pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len, partition_tokens=512,
+                              block_size=16) -> int:
+    n = load().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len, partition_tokens,
+                                         block_size)
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, block_size, *, max_seq_len=None,
+              k_scale=None, v_scale=None, workspace=None, partition_tokens=512, stream=None, validate=False):
+    """Decode attention: out[b, h] = softmax(scale * q[b, h] . K_b^T) . V_b through the block
+    table.  q, out: [B, Hq, d]; caches [N, Hkv, bs, d]; block_tables int32 [B, max_blocks];
+    seq_lens int32 [B].  max_seq_len defaults to the table capacity (no device sync).  A
+    workspace is taken from torch's caching allocator when not given; workspace=False runs
+    every request as a single partition."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    N, Hkv, bs, dc = k_cache.shape
+    if out.shape != q.shape or v_cache.shape != k_cache.shape or dc != d or bs != block_size:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} out {tuple(out.shape)} cache {tuple(k_cache.shape)} "
+                         f"block_size {block_size}")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [num_seqs, max_blocks]")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be int32 [num_seqs]")
+    max_blocks = block_tables.shape[1]
+    if max_seq_len is None:
+        max_seq_len = max_blocks * block_size
+    if validate:
+        lens = seq_lens.cpu().numpy()
+        tab = block_tables.cpu().numpy()
+        if lens.size and (lens.min() < 0 or lens.max() > max_seq_len):
+            raise ValueError("seq_lens outside [0, max_seq_len]")
+        for b, L in enumerate(lens):
+            live = tab[b, : -(-int(L) // block_size)]
+            if live.size and (live.min() < 0 or live.max() >= N):
+                raise ValueError(f"block table row {b} holds an id outside [0, {N})")
+    if workspace is None:
+        nbytes = pa_decode_workspace_bytes(B, Hq, d, max_seq_len, partition_tokens, block_size)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device) if nbytes > 0 else None
+    elif workspace is False:          # explicitly none: one partition per request
+        workspace = None
+    ws_ptr = _dev(workspace, "workspace")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = load().pa_decode(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                          _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), float(scale),
+                          block_size, B, Hq, Hkv, d, N, max_blocks, int(max_seq_len),
+                          _dtype_code(q, "q"), _dtype_code(k_cache, "k_cache"),
+                          _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), ws_ptr, ws_bytes,
+                          int(partition_tokens), _stream(stream))
+    _check(rc)
+
+
+def pa_copy_blocks(k_cache, v_cache, src_dst, *, stream=None):
+    """Copy whole blocks src -> dst (int64 [n, 2] device tensor) in both caches."""
+    torch = _torch()
+    N, Hkv, bs, d = k_cache.shape
+    if src_dst.dtype != torch.int64 or src_dst.dim() != 2 or src_dst.shape[1] != 2:
+        raise ValueError("src_dst must be int64 [n, 2]")
+    rc = load().pa_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(src_dst, "src_dst"),
+                               src_dst.shape[0], N, Hkv, d, bs, _dtype_code(k_cache, "k_cache"), _stream(stream))
+    _check(rc)
+
+
+# --------------------------------------------------------------------------- host allocator
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def pa_alloc_create(num_blocks, block_size, initial_free_order=None):
+    h = ctypes.c_void_p()
+    order = None
+    if initial_free_order is not None:
+        order = np.ascontiguousarray(initial_free_order, dtype=np.int32)
+    _check(load().pa_alloc_create(num_blocks, block_size, _p(order) if order is not None else None,
+                                  ctypes.byref(h)))
+    return h
+
+
+def pa_alloc_destroy(h):
+    load().pa_alloc_destroy(h)
+
+
+def pa_seq_add(h, seq_id):
+    _check(load().pa_seq_add(h, seq_id))
+
+
+def pa_seq_append(h, seq_id, n_tokens):
+    slots = np.empty(max(n_tokens, 1), dtype=np.int64)
+    cow = np.empty(2, dtype=np.int64)
+    ncow = np.zeros(1, dtype=np.int32)
+    _check(load().pa_seq_append(h, seq_id, n_tokens, _p(slots), _p(cow), _p(ncow)))
+    return slots[:n_tokens], [(int(cow[0]), int(cow[1]))] if ncow[0] else []
+
+
+def pa_batch_append(h, seq_ids, n_tokens):
+    ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+    nt = np.ascontiguousarray(n_tokens, dtype=np.int32)
+    slots = np.empty(max(int(nt.sum()), 1), dtype=np.int64)
+    cow = np.empty(max(2 * len(ids), 2), dtype=np.int64)
+    ncow = np.zeros(1, dtype=np.int32)
+    _check(load().pa_batch_append(h, _p(ids), _p(nt), len(ids), _p(slots), _p(cow), _p(ncow)))
+    return slots[: int(nt.sum())], [(int(cow[2 * i]), int(cow[2 * i + 1])) for i in range(int(ncow[0]))]
+
+
+def pa_seq_fork(h, parent, child):
+    _check(load().pa_seq_fork(h, parent, child))
+
+
+def pa_seq_free(h, seq_id):
+    _check(load().pa_seq_free(h, seq_id))
+
+
+def pa_block_tables(h, seq_ids, max_blocks, tables_out=None, seq_lens_out=None):
+    ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+    tab = tables_out if tables_out is not None else np.empty((len(ids), max_blocks), dtype=np.int32)
+    lens = seq_lens_out if seq_lens_out is not None else np.empty(len(ids), dtype=np.int32)
+    assert tab.dtype == np.int32 and tab.flags.c_contiguous and tab.shape == (len(ids), max_blocks)
+    assert lens.dtype == np.int32 and lens.shape == (len(ids),)
+    _check(load().pa_block_tables(h, _p(ids), len(ids), max_blocks, _p(tab), _p(lens)))
+    return tab, lens
+
+
+def pa_alloc_stats(h) -> dict:
+    st = pa_alloc_stats_t()
+    _check(load().pa_alloc_stats(h, ctypes.byref(st)))
+    return {n: int(getattr(st, n)) for n, _ in pa_alloc_stats_t._fields_}
+
+
+def pa_alloc_dump(h, num_blocks):
+    ref = np.empty(num_blocks, dtype=np.int32)
+    free = np.empty(num_blocks, dtype=np.int32)
+    nf = np.zeros(1, dtype=np.int32)
+    _check(load().pa_alloc_dump(h, _p(ref), _p(free), _p(nf)))
+    return ref, free[: int(nf[0])]
+
+
+class Allocator:
+    """Owning wrapper of a pa_allocator handle (host only)."""
+
+    def __init__(self, num_blocks, block_size, initial_free_order=None):
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        self._h = pa_alloc_create(self.num_blocks, self.block_size, initial_free_order)
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h is not None and _lib is not None:
+            pa_alloc_destroy(h)
+
+    def add(self, seq_id):
+        pa_seq_add(self._h, seq_id)
+
+    def append(self, seq_id, n_tokens):
+        return pa_seq_append(self._h, seq_id, n_tokens)
+
+    def batch_append(self, seq_ids, n_tokens):
+        return pa_batch_append(self._h, seq_ids, n_tokens)
+
+    def fork(self, parent, child):
+        pa_seq_fork(self._h, parent, child)
+
+    def free(self, seq_id):
+        pa_seq_free(self._h, seq_id)
+
+    def block_tables(self, seq_ids, max_blocks, tables_out=None, seq_lens_out=None):
+        return pa_block_tables(self._h, seq_ids, max_blocks, tables_out, seq_lens_out)
+
+    def stats(self):
+        return pa_alloc_stats(self._h)
+
+    def dump(self):
+        return pa_alloc_dump(self._h, self.num_blocks)
+
+
+def blocks_for(seq_lens, block_size) -> int:
+    return int(sum(math.ceil(int(L) / block_size) for L in seq_lens))

@@ -1,0 +1,176 @@
+"""Helpers of the GPU parity tests: run a workload's operation script through the library
+(allocator, KV write, decode on the device) and, separately, through the oracle, from the
+same seeded inputs.  The two sides share only the inputs from workloads.py."""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import paged_kv_cache_408_amd as pk
+from oracle import attention as OA
+from oracle.allocator import Allocator as OAlloc
+
+DEV = "cuda"
+SENTINEL = {"f32": np.float32(np.nan), "bf16": np.uint16(0x7FC0), "fp8": np.uint8(0x7F)}
+NP_DT = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+
+# bf16 attention tolerance (element-wise): |gpu - oracle| <= ATOL + RTOL * |oracle|
+BF16_ATOL, BF16_RTOL = 2e-3, 1e-2
+# f32 attention tolerance, from fp32 accumulation over <= a few thousand terms
+F32_ATOL, F32_RTOL = 2e-5, 2e-4
+
+
+def to_dev(a: np.ndarray, fmt: str) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if fmt == "bf16":
+        return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
+    if fmt == "fp8":
+        return torch.from_numpy(a).to(DEV)
+    return torch.from_numpy(a).to(DEV)
+
+
+def to_host(t: torch.Tensor, fmt: str) -> np.ndarray:
+    if fmt == "bf16":
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    if fmt == "fp8":
+        return t.view(torch.uint8).cpu().numpy()
+    return t.cpu().numpy()
+
+
+def bits(a: np.ndarray) -> np.ndarray:
+    """Raw bit patterns, so NaN sentinels compare equal to themselves."""
+    return a.view(np.uint32) if a.dtype == np.float32 else a
+
+
+def out_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def sentinel_cache(w, fmt=None):
+    fmt = fmt or w.fmt
+    return np.full((w.num_blocks, w.Hkv, w.bs, w.d), SENTINEL[fmt], dtype=NP_DT[fmt])
+
+
+def dev_sentinel_cache(w):
+    return to_dev(sentinel_cache(w), w.fmt)
+
+
+class GpuSide:
+    """The library path: C++ allocator, pa_kv_write, pa_decode."""
+
+    def __init__(self, w, vals, partition_tokens=512, workspace=True):
+        self.w = w
+        self.alloc = pk.Allocator(w.num_blocks, w.bs, w.free_order)
+        self.kc = dev_sentinel_cache(w)
+        self.vc = dev_sentinel_cache(w)
+        self.ks = self.vs = None
+        if w.fmt == "fp8":
+            self.ks = torch.from_numpy(vals["k_scale"]).to(DEV)
+            self.vs = torch.from_numpy(vals["v_scale"]).to(DEV)
+        slots = []
+        for op in w.ops:
+            if op[0] == "add":
+                self.alloc.add(op[1])
+            elif op[0] == "append":
+                s, cow = self.alloc.append(op[1], op[2])
+                assert not cow
+                slots.append(s)
+            elif op[0] == "fork":
+                self.alloc.fork(op[1], op[2])
+            elif op[0] == "free":
+                self.alloc.free(op[1])
+        self.prefill_slots = np.concatenate(slots) if slots else np.zeros(0, np.int64)
+        if len(self.prefill_slots):
+            self.write(vals["k_pre"], vals["v_pre"], self.prefill_slots)
+        step, cow = self.alloc.batch_append(list(range(w.B)), [1] * w.B)
+        assert not cow
+        self.step_slots = step
+        self.write(vals["k_new"], vals["v_new"], step)
+        tab, lens = self.alloc.block_tables(list(range(w.B)), max(w.max_blocks, 1))
+        self.tables_np, self.lens_np = tab, lens
+        self.tables = torch.from_numpy(tab).to(DEV)
+        self.lens = torch.from_numpy(lens).to(DEV)
+        self.q = to_dev(vals["q"], w.q_fmt)
+        self.scale = 1.0 / math.sqrt(w.d)
+        self.partition_tokens = partition_tokens
+        self.use_workspace = workspace
+
+    def write(self, k, v, slots):
+        pk.pa_kv_write(to_dev(k, self.w.in_fmt), to_dev(v, self.w.in_fmt),
+                       torch.from_numpy(np.asarray(slots, dtype=np.int64)).to(DEV), self.kc, self.vc,
+                       k_scale=self.ks, v_scale=self.vs)
+
+    def decode(self, tables=None, kc=None, vc=None, partition_tokens=None, max_seq_len=None):
+        out = torch.empty_like(self.q)
+        pk.pa_decode(out, self.q, self.kc if kc is None else kc, self.vc if vc is None else vc,
+                     self.tables if tables is None else tables, self.lens, self.scale, self.w.bs,
+                     max_seq_len=max_seq_len if max_seq_len is not None else int(self.lens_np.max()),
+                     k_scale=self.ks, v_scale=self.vs,
+                     partition_tokens=partition_tokens or self.partition_tokens,
+                     workspace=None if self.use_workspace else False)
+        torch.cuda.synchronize()
+        return out
+
+
+class OracleSide:
+    """The oracle path: Python allocator, numpy scatter, float64 attention."""
+
+    def __init__(self, w, vals):
+        self.w = w
+        self.alloc = OAlloc(w.num_blocks, w.bs, w.free_order)
+        self.kc = sentinel_cache(w)
+        self.vc = sentinel_cache(w)
+        self.ks = vals.get("k_scale")
+        self.vs = vals.get("v_scale")
+        slots = []
+        for op in w.ops:
+            if op[0] == "add":
+                self.alloc.add(op[1])
+            elif op[0] == "append":
+                slots += self.alloc.append(op[1], op[2])[0]
+            elif op[0] == "fork":
+                self.alloc.fork(op[1], op[2])
+            elif op[0] == "free":
+                self.alloc.release(op[1])
+        self.prefill_slots = np.array(slots, dtype=np.int64)
+        if slots:
+            OA.kv_write(vals["k_pre"], vals["v_pre"], self.prefill_slots, self.kc, self.vc, w.bs, w.fmt,
+                        self.ks, self.vs)
+        step, _ = self.alloc.append_batch(list(range(w.B)), [1] * w.B)
+        self.step_slots = np.array(step, dtype=np.int64)
+        OA.kv_write(vals["k_new"], vals["v_new"], self.step_slots, self.kc, self.vc, w.bs, w.fmt, self.ks, self.vs)
+        t, L = self.alloc.block_table(range(w.B), max(w.max_blocks, 1))
+        self.tables, self.lens = np.array(t, dtype=np.int64), np.array(L)
+        self.q = vals["q"]
+        self.scale = np.float32(1.0 / math.sqrt(w.d))
+
+    def decode(self, rows=None):
+        """Full output, or only the requests in `rows` (others left 0)."""
+        w = self.w
+        if rows is None:
+            return OA.decode(self.q, self.kc, self.vc, self.tables, self.lens, self.scale, w.bs, w.fmt, w.q_fmt,
+                             self.ks, self.vs)
+        out = np.zeros((w.B, w.Hq, w.d))
+        sub = OA.decode(self.q[rows], self.kc, self.vc, self.tables[rows], self.lens[rows], self.scale, w.bs,
+                        w.fmt, w.q_fmt, self.ks, self.vs)
+        out[rows] = sub
+        return out
+
+
+def check_close(got: np.ndarray, ref: np.ndarray, fmt: str, what: str = ""):
+    atol, rtol = (F32_ATOL, F32_RTOL) if fmt == "f32" else (BF16_ATOL, BF16_RTOL)
+    err = np.abs(got - ref)
+    bad = ~(err <= atol + rtol * np.abs(ref))
+    rms_ref = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    rel_rms = float(np.sqrt(np.mean(err ** 2))) / rms_ref if rms_ref > 0 else 0.0
+    msg = (f"{what}: {int(bad.sum())} of {bad.size} outside atol {atol} rtol {rtol}; max abs err "
+           f"{float(err.max()) if err.size else 0:.3e}; rms err / rms out {rel_rms:.3e}")
+    assert not bad.any(), msg
+    # sensitivity: the element-wise bound is loose where outputs are tiny; the normalised
+    # RMS error must stay at the level of the output rounding
+    assert rel_rms <= (1e-4 if fmt == "f32" else 1e-2), msg
+    return msg

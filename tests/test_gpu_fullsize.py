@@ -1,0 +1,95 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times
+(partitions of 512 tokens): the whole cache is compared bit for bit with the oracle's
+write, and sampled requests' outputs with the oracle's attention.  Inputs are drawn on the
+device from seeded generators (workloads.device_normal) and copied to the host for the
+oracle."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_408_amd as pk
+import workloads
+from oracle import attention as OA
+from oracle.allocator import Allocator as OAlloc
+from tests.gpu_common import DEV, check_close, out_f64, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu case] {request.node.name}", flush=True)
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+
+
+def _bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def full_case(w, sample_rows):
+    T = w.prefill_tokens
+    k_pre = workloads.device_normal(w, "k_pre", (T, w.Hkv, w.d))
+    v_pre = workloads.device_normal(w, "v_pre", (T, w.Hkv, w.d))
+    k_new = workloads.device_normal(w, "k_new", (w.B, w.Hkv, w.d))
+    v_new = workloads.device_normal(w, "v_new", (w.B, w.Hkv, w.d))
+    q = workloads.device_normal(w, "q", (w.B, w.Hq, w.d))
+    # library side
+    ga = pk.Allocator(w.num_blocks, w.bs, w.free_order)
+    slots = []
+    for op in w.ops:
+        if op[0] == "add":
+            ga.add(op[1])
+        elif op[0] == "append":
+            slots.append(ga.append(op[1], op[2])[0])
+    slots = np.concatenate(slots)
+    kc = torch.full((w.num_blocks, w.Hkv, w.bs, w.d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    vc = torch.full_like(kc, float("nan"))
+    pk.pa_kv_write(k_pre, v_pre, torch.from_numpy(slots).to(DEV), kc, vc)
+    step, _ = ga.batch_append(list(range(w.B)), [1] * w.B)
+    pk.pa_kv_write(k_new, v_new, torch.from_numpy(step).to(DEV), kc, vc)
+    tab, lens = ga.block_tables(list(range(w.B)), w.max_blocks)
+    out = torch.empty_like(q)
+    pk.pa_decode(out, q, kc, vc, torch.from_numpy(tab).to(DEV), torch.from_numpy(lens).to(DEV),
+                 1 / math.sqrt(w.d), w.bs, max_seq_len=int(lens.max()), partition_tokens=512)
+    torch.cuda.synchronize()
+    # oracle side, from the same stored inputs
+    oa = OAlloc(w.num_blocks, w.bs, w.free_order)
+    oslots = []
+    for op in w.ops:
+        if op[0] == "add":
+            oa.add(op[1])
+        elif op[0] == "append":
+            oslots += oa.append(op[1], op[2])[0]
+    ostep, _ = oa.append_batch(list(range(w.B)), [1] * w.B)
+    assert np.array_equal(slots, np.array(oslots)) and np.array_equal(step, np.array(ostep))
+    okc = np.full((w.num_blocks, w.Hkv, w.bs, w.d), 0x7FC0, np.uint16)
+    ovc = okc.copy()
+    OA.kv_write(_bits(k_pre), _bits(v_pre), np.array(oslots), okc, ovc, w.bs, "bf16")
+    OA.kv_write(_bits(k_new), _bits(v_new), np.array(ostep), okc, ovc, w.bs, "bf16")
+    assert np.array_equal(_bits(kc), okc), "K cache differs"
+    assert np.array_equal(_bits(vc), ovc), "V cache differs"
+    del okc  # keep host memory low; ovc still needed
+    otab, olens = oa.block_table(range(w.B), w.max_blocks)
+    assert np.array_equal(tab, np.array(otab)) and np.array_equal(lens, np.array(olens))
+    kc_h = _bits(kc)
+    rows = np.array(sample_rows)
+    ref = OA.decode(_bits(q)[rows], kc_h, ovc, np.array(otab)[rows], np.array(olens)[rows],
+                    np.float32(1 / math.sqrt(w.d)), w.bs, "bf16", "bf16")
+    got = out_f64(out)[rows]
+    print(check_close(got, ref, "bf16", w.name), flush=True)
+    assert np.isfinite(out_f64(out)).all()
+
+
+def test_llama_layer_full_sampled():
+    """One full Llama-3-8B-shaped layer: 16 requests x 4096 tokens, 32 q / 8 kv heads."""
+    full_case(workloads.gqa_uniform(B=16, L=4096, layers=1), sample_rows=[0, 7, 15])
+
+
+def test_long_context_full():
+    """The 70B-shaped layer at 131072 tokens x 2 requests: 256 partitions merged."""
+    full_case(workloads.long_context(), sample_rows=[0, 1])
