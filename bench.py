@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the paged KV cache on one MI355X.
+
+Workload (default): Llama-3-8B-shaped GQA decode -- 32 layers, batch 16, 32 q heads / 8 KV
+heads, head_dim 128, bf16 cache and q, block size 16, every request at 4096 tokens when the
+timed steps start, 32 per-layer caches (8.6 GB) sharing one seeded-permutation block table.
+
+One step is one pass of the whole hot path over the batch:
+  1. host allocator: append one token to each request (slots; copy-on-write pairs, if any,
+     are copied with pa_copy_blocks in every layer),
+  2. block-table export to pinned host memory and an async copy to the device,
+  3. for each of the 32 layers: pa_kv_write of the 16 new tokens' K/V, then pa_decode.
+Requests grow by one token per step, as in generation.
+
+Reported (one JSON line): `value` = algorithmic bytes of the whole step (every request's
+cached K/V once per KV head, q, out, table entries, lengths; plus the write's rows and
+slots) / wall time per step.  `roofline` = pa_decode (a single kernel launch) measured with
+HIP events around every launch in the timed region on the launch stream.  `cpu_baseline` =
+the float64 oracle timed on a bounded sample of the same per-request work on the host.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode attention KV GB/s and % of HBM peak (GQA 32q/8kv d128, bf16)"
+HBM_PEAK_GBPS = 8000.0
+DECODE_KERNEL = "decode_partial_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama3_8b_bf16_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_408_amd", "csrc", "pagedkv.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- byte model
+
+def decode_bytes(seq_lens, Hq, Hkv, d, bs, kv_bytes, q_bytes):
+    """Algorithmic bytes of one decode launch: K and V of every cached token once per KV
+    head, q in, out, the table entries in use and the lengths."""
+    kv = sum(2 * Hkv * int(L) * d * kv_bytes for L in seq_lens)
+    qo = len(seq_lens) * Hq * d * 2 * q_bytes
+    tab = sum(4 * -(-int(L) // bs) for L in seq_lens)
+    return kv + qo + tab + 4 * len(seq_lens)
+
+
+def kv_write_bytes(T, Hkv, d, e_in, e_cache):
+    return 2 * T * Hkv * d * (e_in + e_cache) + 8 * T
+
+
+def kernel_source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it was
+    taken with the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    h = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not h or not t or h.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(seconds: float):
+    """The float64 oracle (as it stands) on a bounded sample of the benchmark's work: one
+    request of one layer at 4096 tokens, all 32 q heads, decoded repeatedly."""
+    import numpy as np
+    import workloads
+    from oracle import attention as OA
+    from oracle.allocator import Allocator as OAlloc
+
+    w = workloads.gqa_uniform(B=1, L=4096, layers=1, seed_index=2, name="cpu_sample")
+    vals = workloads.host_values(w)
+    al = OAlloc(w.num_blocks, w.bs, w.free_order)
+    slots = []
+    for op in w.ops:
+        if op[0] == "add":
+            al.add(op[1])
+        else:
+            slots += al.append(op[1], op[2])[0]
+    kc = np.zeros((w.num_blocks, w.Hkv, w.bs, w.d), np.uint16)
+    vc = np.zeros_like(kc)
+    OA.kv_write(vals["k_pre"], vals["v_pre"], np.array(slots), kc, vc, w.bs, "bf16")
+    step = al.append_batch([0], [1])[0]
+    OA.kv_write(vals["k_new"], vals["v_new"], np.array(step), kc, vc, w.bs, "bf16")
+    t, L = al.block_table([0], w.max_blocks)
+    scale = np.float32(1 / math.sqrt(w.d))
+    per_call = decode_bytes(L, w.Hq, w.Hkv, w.d, w.bs, 2, 2)
+    calls = 0
+    c0, t0 = time.process_time(), time.perf_counter()
+    while True:
+        OA.decode(vals["q"], kc, vc, np.array(t), np.array(L), scale, w.bs, "bf16", "bf16")
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    cpu = time.process_time() - c0
+    return {
+        "value": round(per_call * calls / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": max(1, round(cpu / el)),
+        "kind": "oracle",
+        "sample": f"{calls} float64 decodes of 1 request x 32 q heads x {int(L[0])} tokens (one layer of the "
+                  f"benchmark batch's per-request work), {el:.1f} s wall, {cpu:.1f} s CPU, "
+                  f"{len(os.sched_getaffinity(0))} host cores visible",
+    }
+
+
+# ----------------------------------------------------------------------------- GPU step
+
+def run(args):
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_408_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    import paged_kv_cache_408_amd as pk
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    steps, warm = args.steps, args.warmup
+    L0 = 4096
+    grow = steps + warm
+    w = workloads.gqa_uniform(B=16, L=L0, layers=32, spare_blocks=16 * (grow // 16 + 2))
+    B, Hq, Hkv, d, bs, layers = w.B, w.Hq, w.Hkv, w.d, w.bs, w.layers
+    max_blocks = -(-(L0 + grow) // bs)
+    max_seq = max_blocks * bs
+    scale = 1.0 / math.sqrt(d)
+    log(f"workload {w.name}: {layers} layers x batch {B}, {Hq}q/{Hkv}kv, d {d}, block {bs}, "
+        f"{w.num_blocks} blocks per layer")
+
+    # allocator and prefill (L0 - 1 tokens per request; the first step appends token L0)
+    alloc = pk.Allocator(w.num_blocks, bs, w.free_order)
+    slots = []
+    for op in w.ops:
+        if op[0] == "add":
+            alloc.add(op[1])
+        else:
+            slots.append(alloc.append(op[1], op[2])[0])
+    slots = torch.from_numpy(np.concatenate(slots)).to(dev)
+    T = slots.numel()
+    kc, vc, q, kn, vn, outs = [], [], [], [], [], []
+    for l in range(layers):
+        k_cache = torch.empty((w.num_blocks, Hkv, bs, d), dtype=torch.bfloat16, device=dev)
+        v_cache = torch.empty_like(k_cache)
+        kp = workloads.device_normal(w, "k_pre", (T, Hkv, d), layer=l)
+        vp = workloads.device_normal(w, "v_pre", (T, Hkv, d), layer=l)
+        pk.pa_kv_write(kp, vp, slots, k_cache, v_cache)
+        del kp, vp
+        kc.append(k_cache)
+        vc.append(v_cache)
+        q.append(workloads.device_normal(w, "q", (B, Hq, d), layer=l))
+        kn.append(workloads.device_normal(w, "k_new", (B, Hkv, d), layer=l))
+        vn.append(workloads.device_normal(w, "v_new", (B, Hkv, d), layer=l))
+        outs.append(torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev))
+    torch.cuda.synchronize()
+    log(f"caches ready: {2 * layers * kc[0].numel() * 2 / 1e9:.2f} GB")
+
+    # per-step device inputs, refreshed from pinned host buffers (one buffer per step, so no
+    # host write can race an async copy still in flight)
+    tables_d = torch.empty((B, max_blocks), dtype=torch.int32, device=dev)
+    lens_d = torch.empty((B,), dtype=torch.int32, device=dev)
+    slot_d = torch.empty((B,), dtype=torch.int64, device=dev)
+    pin_tab = [torch.empty((B, max_blocks), dtype=torch.int32).pin_memory() for _ in range(grow)]
+    pin_len = [torch.empty((B,), dtype=torch.int32).pin_memory() for _ in range(grow)]
+    pin_slot = [torch.empty((B,), dtype=torch.int64).pin_memory() for _ in range(grow)]
+    nbytes = pk.pa_decode_workspace_bytes(B, Hq, d, max_seq, args.partition_tokens, bs)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    pk.pa_decode_workspace_init(ws)
+    dec = [pk.PreparedDecode(outs[l], q[l], kc[l], vc[l], tables_d, lens_d, scale, bs, max_seq_len=max_seq,
+                             workspace=ws, partition_tokens=args.partition_tokens) for l in range(layers)]
+    wr = [pk.PreparedKVWrite(kn[l], vn[l], slot_d, kc[l], vc[l]) for l in range(layers)]
+    seq_ids = list(range(B))
+    ones = [1] * B
+
+    def step(i, events=None):
+        s, cow = alloc.batch_append(seq_ids, ones)
+        alloc.block_tables(seq_ids, max_blocks, pin_tab[i].numpy(), pin_len[i].numpy())
+        pin_slot[i].numpy()[:] = s
+        tables_d.copy_(pin_tab[i], non_blocking=True)
+        lens_d.copy_(pin_len[i], non_blocking=True)
+        slot_d.copy_(pin_slot[i], non_blocking=True)
+        if cow:
+            pairs = torch.tensor(cow, dtype=torch.int64).to(dev, non_blocking=False)
+            for l in range(layers):
+                pk.pa_copy_blocks(kc[l], vc[l], pairs)
+        for l in range(layers):
+            wr[l]()
+            if events is not None:
+                e0, e1 = events[l]
+                e0.record()
+                dec[l]()
+                e1.record()
+            else:
+                dec[l]()
+        return pin_len[i].numpy().copy()
+
+    for i in range(warm):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup done ({warm} steps); timing {steps} steps")
+
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(layers)]
+           for _ in range(steps)]
+    lens_per_step = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        lens_per_step.append(step(warm + i, evs[i]))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    log(f"timed {steps} steps in {wall * 1e3:.2f} ms")
+
+    dec_ms = [e0.elapsed_time(e1) for st in evs for (e0, e1) in st]
+    dec_bytes = [decode_bytes(L, Hq, Hkv, d, bs, 2, 2) for L in lens_per_step for _ in range(layers)]
+    step_bytes = sum(dec_bytes) + steps * layers * kv_write_bytes(B, Hkv, d, 2, 2)
+    value = step_bytes / wall / 1e9
+    avg_launch_s = sum(dec_ms) / len(dec_ms) / 1e3
+    avg_bytes = sum(dec_bytes) / len(dec_bytes)
+    achieved = avg_bytes / avg_launch_s / 1e9
+    traffic = measured_traffic()
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(wall / steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)*0.5 K/V/q drawn on the device; seeded block permutation)",
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "config": {
+            "workload": "llama3_8b_gqa_decode: 32 layers x batch 16, 32 q / 8 kv heads, head_dim 128, bf16, "
+                        "block 16, 4096 tokens per request at the first timed step (+1 per step), "
+                        "split-K partitions of %d tokens" % args.partition_tokens,
+            "layers": layers, "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": d,
+            "block_size": bs, "seq_len_start": int(lens_per_step[0][0]), "partition_tokens": args.partition_tokens,
+            "kv_cache_gb": round(2 * layers * kc[0].numel() * 2 / 1e9, 3),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": DECODE_KERNEL,
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(round(avg_bytes)),
+            "avg_launch_us": round(avg_launch_s * 1e6, 3),
+            "launches": len(dec_ms),
+        },
+    }
+    return result
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--partition-tokens", type=int, default=512)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run pa_copy_blocks over 1 GiB of blocks (for HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    result = run(args)
+    if not args.no_cpu_baseline:
+        log(f"timing the oracle on the host for ~{args.cpu_seconds:.0f} s")
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+def calibrate_copy():
+    """A plain copy of known size for scaling the HBM byte counters: pa_copy_blocks over
+    8192 block pairs of 64 KiB in each of K and V (512 MiB read, 512 MiB written per launch),
+    5 launches."""
+    import torch
+    import paged_kv_cache_408_amd as pk
+    dev = torch.device("cuda:0")
+    N, Hkv, bs, d = 16384, 8, 16, 128
+    kc = torch.zeros((N, Hkv, bs, d), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    src = torch.arange(0, N // 2, dtype=torch.int64)
+    pairs = torch.stack([src, src + N // 2], 1).to(dev)
+    for _ in range(5):
+        pk.pa_copy_blocks(kc, vc, pairs)
+    torch.cuda.synchronize()
+    block = Hkv * bs * d * 2
+    print(json.dumps({"copy_read_bytes_per_launch": 2 * (N // 2) * block,
+                      "copy_write_bytes_per_launch": 2 * (N // 2) * block, "launches": 5}), flush=True)
+
+
+if __name__ == "__main__":
+    main()

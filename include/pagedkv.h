@@ -119,7 +119,15 @@ int pa_kv_write(const void* k, const void* v, const int64_t* slot_mapping, int64
  *  max_seq_len   host upper bound of seq_lens (sizes the grid and the workspace)
  *  workspace     device scratch of at least pa_decode_workspace_bytes(...) bytes, or NULL
  *                (then each request is reduced in a single partition, which is correct but
- *                slow for long contexts)
+ *                slow for long contexts).  It holds the partitions' partial results and merge
+ *                ticket counters: the last work-group of each group of 16 partitions of a
+ *                request and KV head merges that group, and with more than one group the last
+ *                group-merger merges the groups, all in the same launch.  Zero the workspace
+ *                (pa_decode_workspace_init) before its first use and whenever it is reused
+ *                with different (num_seqs, num_q_heads, head_dim, max_seq_len,
+ *                partition_tokens, block_size); consecutive calls with the same sizes leave
+ *                the counters at zero and need no re-zeroing.  Calls that share a workspace
+ *                must not run concurrently (order them on one stream).
  *
  * Device-side faults are turned into loud results instead of out-of-bounds accesses: a
  * request whose L exceeds max_seq_len or max_blocks_per_seq * block_size, or whose table
@@ -129,6 +137,10 @@ int pa_kv_write(const void* k, const void* v, const int64_t* slot_mapping, int64
 int64_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_seq_len, int32_t partition_tokens,
                                   int32_t block_size);
+
+/* Zero a decode workspace (a store kernel on `stream`; no memset node is recorded, so this
+ * may be captured in a graph).  workspace_bytes must be a multiple of 4. */
+int pa_decode_workspace_init(void* workspace, int64_t workspace_bytes, void* stream);
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, const int32_t* seq_lens, float scale,

@@ -20,7 +20,8 @@ PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_NO_BLOCKS, PA_ERR_DEVICE = 0, 
 PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_FP8_E4M3 = 0, 1, 2
 
 EXPORTED = [
-    "pa_last_error", "pa_abi_version", "pa_kv_write", "pa_decode_workspace_bytes", "pa_decode",
+    "pa_last_error", "pa_abi_version", "pa_kv_write", "pa_decode_workspace_bytes",
+    "pa_decode_workspace_init", "pa_decode",
     "pa_copy_blocks", "pa_alloc_create", "pa_alloc_destroy", "pa_seq_add", "pa_seq_append",
     "pa_batch_append", "pa_seq_fork", "pa_seq_free", "pa_block_tables", "pa_alloc_stats",
     "pa_alloc_dump",
@@ -64,6 +65,7 @@ def load(path: str = LIB_PATH):
         "pa_abi_version": (I32, []),
         "pa_kv_write": (ctypes.c_int, [P, P, P, I64, P, P, I64, I32, I32, I32, I32, I32, P, P, P]),
         "pa_decode_workspace_bytes": (I64, [I32, I32, I32, I32, I32, I32]),
+        "pa_decode_workspace_init": (ctypes.c_int, [P, I64, P]),
         "pa_decode": (ctypes.c_int, [P, P, P, P, P, P, F32, I32, I32, I32, I32, I32, I64, I32, I32, I32, I32,
                                      P, P, P, I64, I32, P]),
         "pa_copy_blocks": (ctypes.c_int, [P, P, P, I32, I64, I32, I32, I32, I32, P]),
@@ -160,13 +162,41 @@ def pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len, part
     return int(n)
 
 
+def pa_decode_workspace_init(workspace, *, stream=None):
+    """Zero a decode workspace (uint8 device tensor) on the stream."""
+    rc = load().pa_decode_workspace_init(_dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                         _stream(stream))
+    _check(rc)
+
+
+def decode_workspace(nbytes, device, layout_key, *, stream=None):
+    """A workspace of at least nbytes kept per device and grown on demand.  It is zeroed
+    whenever the call's sizes (layout_key) differ from the previous call's, as the ticket
+    counters require; callers using it on several streams at once must bring their own."""
+    torch = _torch()
+    dev = torch.device(device)
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    ws, last = _WORKSPACES.get(key, (None, None))
+    if ws is None or ws.numel() < nbytes:
+        n = (max(int(nbytes), 16) + 255) // 256 * 256
+        ws, last = torch.empty(n, dtype=torch.uint8, device=device), None
+    if last != layout_key:
+        pa_decode_workspace_init(ws, stream=stream)
+    _WORKSPACES[key] = (ws, layout_key)
+    return ws
+
+
+_WORKSPACES = {}
+
+
 def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, block_size, *, max_seq_len=None,
               k_scale=None, v_scale=None, workspace=None, partition_tokens=512, stream=None, validate=False):
     """Decode attention: out[b, h] = softmax(scale * q[b, h] . K_b^T) . V_b through the block
     table.  q, out: [B, Hq, d]; caches [N, Hkv, bs, d]; block_tables int32 [B, max_blocks];
     seq_lens int32 [B].  max_seq_len defaults to the table capacity (no device sync).  A
-    workspace is taken from torch's caching allocator when not given; workspace=False runs
-    every request as a single partition."""
+    zeroed workspace kept per device is used when none is given (it must not be shared by
+    calls in flight on different streams); workspace=False runs every request as a single
+    partition."""
     torch = _torch()
     B, Hq, d = q.shape
     N, Hkv, bs, dc = k_cache.shape
@@ -191,7 +221,8 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, block_siz
                 raise ValueError(f"block table row {b} holds an id outside [0, {N})")
     if workspace is None:
         nbytes = pa_decode_workspace_bytes(B, Hq, d, max_seq_len, partition_tokens, block_size)
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device) if nbytes > 0 else None
+        key = (B, Hq, d, int(max_seq_len), int(partition_tokens), block_size)
+        workspace = decode_workspace(nbytes, q.device, key, stream=stream) if nbytes > 0 else None
     elif workspace is False:          # explicitly none: one partition per request
         workspace = None
     ws_ptr = _dev(workspace, "workspace")
@@ -329,3 +360,52 @@ class Allocator:
 
 def blocks_for(seq_lens, block_size) -> int:
     return int(sum(math.ceil(int(L) / block_size) for L in seq_lens))
+
+
+# --------------------------------------------------------------------------- prepared calls
+
+class PreparedDecode:
+    """pa_decode with its arguments checked and marshalled once; calling it enqueues the
+    kernel with the same buffers (their contents may change between calls).  For loops
+    where per-call Python overhead would otherwise show next to a ~50 us kernel."""
+
+    def __init__(self, out, q, k_cache, v_cache, block_tables, seq_lens, scale, block_size, *, max_seq_len,
+                 workspace, k_scale=None, v_scale=None, partition_tokens=512, stream=None):
+        B, Hq, d = q.shape
+        N, Hkv, bs, dc = k_cache.shape
+        if out.shape != q.shape or v_cache.shape != k_cache.shape or dc != d or bs != block_size:
+            raise ValueError("shape mismatch")
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        self._keep = (out, q, k_cache, v_cache, block_tables, seq_lens, workspace, k_scale, v_scale)
+        self._args = (_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                      _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), ctypes.c_float(scale),
+                      block_size, B, Hq, Hkv, d, N, block_tables.shape[1], int(max_seq_len),
+                      _dtype_code(q, "q"), _dtype_code(k_cache, "k_cache"), _dev(k_scale, "k_scale"),
+                      _dev(v_scale, "v_scale"), _dev(workspace, "workspace"), ws_bytes, int(partition_tokens),
+                      _stream(stream))
+        self._fn = load().pa_decode
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc:
+            _check(rc)
+
+
+class PreparedKVWrite:
+    """pa_kv_write with its arguments marshalled once (see PreparedDecode)."""
+
+    def __init__(self, k, v, slot_mapping, k_cache, v_cache, *, k_scale=None, v_scale=None, stream=None):
+        T, H, d = k.shape
+        N, Hc, bs, dc = k_cache.shape
+        if v.shape != k.shape or v_cache.shape != k_cache.shape or (Hc, dc) != (H, d) or slot_mapping.shape != (T,):
+            raise ValueError("shape mismatch")
+        self._keep = (k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale)
+        self._args = (_dev(k, "k"), _dev(v, "v"), _dev(slot_mapping, "slot_mapping"), T, _dev(k_cache, "k_cache"),
+                      _dev(v_cache, "v_cache"), N, H, d, bs, _dtype_code(k, "k"), _dtype_code(k_cache, "k_cache"),
+                      _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _stream(stream))
+        self._fn = load().pa_kv_write
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc:
+            _check(rc)

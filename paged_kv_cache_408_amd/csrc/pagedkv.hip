@@ -14,19 +14,26 @@
 //                        quantisation; slots < 0 or beyond the pool are skipped.
 //  decode_partial_kernel one work-group (4 wave64) per (partition, KV head, request).  The
 //                        G = Hq/Hkv query heads of a KV head share every K/V load, so each
-//                        cached byte is read once.  Per pass of TPP tokens a wave:
+//                        cached byte is read once.  A wave takes every 4th pass of TPP
+//                        tokens; its block ids sit one per lane in a register (v_readlane
+//                        per pass), and the loads of the next pass are in flight while the
+//                        current one is computed.  Per pass:
 //                          K phase: KL lanes per token row, each lane a few 16-byte loads of
 //                            that row (every group of 4 lanes reads 64 contiguous bytes);
 //                            partial dot products with the lane's slice of q (v_dot2 on
-//                            bf16 pairs), reduced across the KL lanes;
-//                          online softmax: wave max of the pass, rescale of the running
-//                            state, p = exp2(s - m) (scores carry scale * log2(e));
+//                            bf16 pairs), summed across the KL lanes with DPP;
+//                          online softmax against a reference maximum that is only raised
+//                            (with a rescale) when a score passes it by 2^8 -- one ballot
+//                            per pass; p = exp2(s - m) (scores carry scale * log2(e));
 //                          V phase: one 16-byte vector of a row per lane, consecutive lanes
 //                            covering consecutive bytes (1 KiB per wave load); p is handed
 //                            from the K-phase lanes through LDS; acc[h][dims] += p * v.
 //                        The 4 waves' states are merged in LDS; a single-partition request
 //                        writes `out`, otherwise (m, l, acc) goes to the workspace.
-//  decode_merge_kernel   log-sum-exp merge of the partitions of each (request, q head).
+//                        With several partitions, the last work-group of a (request, KV
+//                        head) to finish merges them by log-sum-exp (ticket counter in the
+//                        workspace, agent-scope release/acquire), so one launch does both.
+//  zero_kernel           clears a workspace (a plain store kernel, no memset node).
 //  copy_blocks_kernel    whole-block copies for copy-on-write.
 //
 // Reduction order depends only on logical token positions (never on physical block ids),
@@ -47,6 +54,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMergeGroup = 16;   // partitions merged together at the first merge level
 
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
@@ -93,9 +101,67 @@ __device__ __forceinline__ float2v e4m3x2_to_f32(uint32_t w) {
 }
 
 // ------------------------------------------------------------------ cross-lane helpers
+//
+// Reductions use DPP lane permutations (quad_perm, row_ror, row_half_mirror) inside a
+// 16-lane row and the gfx950 permlane swaps across rows: v_permlane16_swap exchanges the
+// odd rows of one register with the even rows of the other, v_permlane32_swap the upper
+// half of one with the lower half of the other.  Given the same value in both operands,
+// the two results of a swap hold the value of the lane and of its partner 16 (or 32) lanes
+// away, in some order, so any symmetric combination of them is the pair reduction.
 
-__device__ __forceinline__ float xor_shfl(float v, int mask) {
-    return __shfl_xor(v, mask, 64);
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppRowRor4 = 0x124;    // row_ror:4
+constexpr int kDppRowRor8 = 0x128;    // row_ror:8
+constexpr int kDppRowHalfMirror = 0x141;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float pair16_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair16_max(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Sum over the KL (4 or 8) consecutive lanes that share a token row.
+template <int KL>
+__device__ __forceinline__ float group_sum(float x) {
+    x += dpp<kDppQuadXor1>(x);
+    x += dpp<kDppQuadXor2>(x);
+    if constexpr (KL == 8) x += dpp<kDppRowHalfMirror>(x);
+    return x;
+}
+
+// Max over the wave of a value that is already uniform within groups of KL lanes.
+template <int KL>
+__device__ __forceinline__ float wave_max_of_groups(float x) {
+    if constexpr (KL == 4) x = fmaxf(x, dpp<kDppRowRor4>(x));
+    x = fmaxf(x, dpp<kDppRowRor8>(x));
+    x = pair16_max(x);
+    return pair32_max(x);
+}
+
+// Sum over the 64 / VL lanes that share lane % VL (VL in {4, 8, 16, 32}).
+template <int VL>
+__device__ __forceinline__ float sum_over_row_groups(float x) {
+    if constexpr (VL == 4) x += dpp<kDppRowRor4>(x);
+    if constexpr (VL <= 8) x += dpp<kDppRowRor8>(x);
+    if constexpr (VL <= 16) x = pair16_sum(x);
+    return pair32_sum(x);
 }
 
 __device__ __forceinline__ void wave_sync_lds() {
@@ -222,9 +288,13 @@ struct DecodeArgs {
     const int32_t* seq_lens;
     const float* k_scale;
     const float* v_scale;
-    float* ws_m;
+    int* ws_ctr;           // merge tickets (level 1: per group of partitions; level 2), zero between calls
+    float* ws_m;           // level-1 partials: one row per (request, q head, partition)
     float* ws_l;
     float* ws_acc;
+    float* ws_m2;          // level-2 partials: one row per (request, q head, group of partitions)
+    float* ws_l2;
+    float* ws_acc2;
     float score_scale;     // scale * log2(e)
     int hkv;
     int64_t num_blocks;
@@ -232,9 +302,118 @@ struct DecodeArgs {
     int max_seq_len;
     int part_tokens;
     int max_parts;
+    int max_groups;        // ceil(max_parts / kMergeGroup)
 };
 
-// ------------------------------------------------------------------ decode: pass 1
+// ------------------------------------------------------------------ decode: partitions and merge
+
+// Rescale threshold of the online softmax, in log2 units: a wave keeps a reference maximum
+// and only rescales its state when a score exceeds it by more than this, so exponentials
+// stay <= 2^8 and most passes need no cross-lane maximum at all.
+constexpr float kRescaleThreshold = 8.0f;
+
+__device__ __forceinline__ void store_agent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Raw buffer view of a float array for agent-scope (sc1) vector loads; out-of-range reads
+// return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_view(const float* base, int64_t n_floats) {
+    const int64_t bytes = n_floats * 4;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0,
+                                             static_cast<int>(bytes > 0x7fffffff ? 0x7fffffff : bytes), 0x00020000);
+}
+
+// Log-sum-exp merge of `count` consecutive partial rows (m, l, acc[D]) of each of the G heads
+// of one (request, KV head): head h's rows are row0 + h * head_stride + [0, count).  The block's threads take float4
+// columns of the G x D outputs and split the rows among themselves; each keeps an online
+// (max, sum, accumulator) state, and the slices are combined in LDS.  A NaN max in any row
+// (a bad block id) makes the result NaN.  Writes `out` (rounded) or, when out == nullptr, one
+// partial row per head to (m_dst, l_dst, acc_dst) with the given head stride, by
+// agent-scope stores.
+template <int QDT, int D, int G>
+__device__ void merge_rows(const float* m_src, const float* l_src, const float* acc_src, int64_t row0,
+                           int64_t head_stride, int count, typename Elem<QDT>::T* out, float* m_dst, float* l_dst,
+                           float* acc_dst, int64_t dst_head_stride) {
+    constexpr int NC = G * D / 4;               // float4 columns
+    constexpr int NS = kThreads / NC > 0 ? kThreads / NC : 1;   // row slices
+    static_assert(NC <= kThreads, "one column per thread");
+    __shared__ float s_mm[NS][NC], s_ll[NS][NC];
+    __shared__ float4 s_num[NS][NC];
+    const int t = threadIdx.x;
+    const int col = t % NC, slice = t / NC;
+    const int h = col / (D / 4), c4 = col % (D / 4);
+    const bool active = slice < NS;
+    float M = -INFINITY, den = 0.0f;
+    float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    bool nan_seen = false;
+    if (active) {
+        const int64_t rh = row0 + int64_t(h) * head_stride;     // rows rh .. rh + count - 1
+        const auto racc = coherent_view(acc_src + rh * D, int64_t(count) * D);
+        for (int r = slice; r < count; r += NS) {
+            const float mr = load_agent(m_src + rh + r);
+            const float lr = load_agent(l_src + rh + r);
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(racc, (r * D + c4 * 4) * 4, 0, 16);
+            nan_seen |= __builtin_isnan(mr);
+            if (mr > M) {   // new maximum: rescale the state (exp2(-inf) = 0 on the first row)
+                const float f = __builtin_amdgcn_exp2f(M - mr);
+                den *= f;
+                num.x *= f; num.y *= f; num.z *= f; num.w *= f;
+                M = mr;
+            }
+            const float wgt = __builtin_amdgcn_exp2f(mr - M);
+            den = fmaf(wgt, lr, den);
+            num.x = fmaf(wgt, __int_as_float(v[0]), num.x);
+            num.y = fmaf(wgt, __int_as_float(v[1]), num.y);
+            num.z = fmaf(wgt, __int_as_float(v[2]), num.z);
+            num.w = fmaf(wgt, __int_as_float(v[3]), num.w);
+        }
+        if (nan_seen) M = __builtin_nanf("");
+        s_mm[slice][col] = M;
+        s_ll[slice][col] = den;
+        s_num[slice][col] = num;
+    }
+    __syncthreads();
+    if (slice != 0) return;
+    float Mt = s_mm[0][col];
+    bool nan_any = __builtin_isnan(Mt);
+#pragma unroll
+    for (int sl = 1; sl < NS; ++sl) {
+        nan_any |= __builtin_isnan(s_mm[sl][col]);
+        Mt = fmaxf(Mt, s_mm[sl][col]);
+    }
+    float dt = 0.0f;
+    float4 nt = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
+        const float f = __builtin_amdgcn_exp2f(s_mm[sl][col] - Mt);   // 0 for an empty slice
+        dt = fmaf(f, s_ll[sl][col], dt);
+        const float4 v = s_num[sl][col];
+        nt.x = fmaf(f, v.x, nt.x); nt.y = fmaf(f, v.y, nt.y); nt.z = fmaf(f, v.z, nt.z); nt.w = fmaf(f, v.w, nt.w);
+    }
+    if (nan_any) { Mt = dt = __builtin_nanf(""); }
+    if (out != nullptr) {
+        const float o[4] = {nt.x / dt, nt.y / dt, nt.z / dt, nt.w / dt};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (QDT == PA_DTYPE_BF16) out[h * D + c4 * 4 + e] = f32_to_bf16(o[e]);
+            else out[h * D + c4 * 4 + e] = o[e];
+        }
+    } else {
+        float* ad = acc_dst + int64_t(h) * dst_head_stride * D + c4 * 4;
+        store_agent(ad + 0, nt.x);
+        store_agent(ad + 1, nt.y);
+        store_agent(ad + 2, nt.z);
+        store_agent(ad + 3, nt.w);
+        if (c4 == 0) {
+            store_agent(m_dst + int64_t(h) * dst_head_stride, Mt);
+            store_agent(l_dst + int64_t(h) * dst_head_stride, dt);
+        }
+    }
+}
 
 template <int CDT, int QDT, int D, int BS, int G>
 __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeArgs a) {
@@ -242,11 +421,14 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeAr
     using CT = typename Elem<CDT>::T;
     using QT = typename Elem<QDT>::T;
     constexpr bool kDot2 = CDT == PA_DTYPE_BF16;   // bf16 cache: v_dot2 on packed pairs
+    constexpr int KL = C::KL, TPP = C::TPP, EPV = C::EPV, KVPL = C::KVPL, VL = C::VL, VRG = C::VRG,
+                  VR = C::VR, BPP = C::BPP;
 
-    __shared__ float s_p[kWaves][C::TPP][G];
+    __shared__ float s_p[kWaves][TPP][G];
     __shared__ float s_m[kWaves][G];
     __shared__ float s_l[kWaves][G];
     __shared__ float s_acc[kWaves][G][D];
+    __shared__ int s_last;
 
     const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -269,11 +451,14 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeAr
 
     const int t0 = part * a.part_tokens;
     const int t1 = min(L, t0 + a.part_tokens);
-    const int npass = (t1 - t0 + C::TPP - 1) / C::TPP;
+    const int npass = (t1 - t0 + TPP - 1) / TPP;
+    const int nk = npass > w ? (npass - w + kWaves - 1) / kWaves : 0;   // passes w, w+4, ...
     const int nblk = (L + BS - 1) / BS;
     const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
     const CT* kbase = reinterpret_cast<const CT*>(a.k_cache);
     const CT* vbase = reinterpret_cast<const CT*>(a.v_cache);
+    const int64_t head_tile = int64_t(g) * (BS * D);
+    const int64_t block_stride = int64_t(a.hkv) * (BS * D);
 
     float sc = a.score_scale;
     float vsc = 1.0f;
@@ -282,102 +467,115 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeAr
         vsc = a.v_scale[g];
     }
 
-    // ---- q slice of this lane (K-phase layout): vectors j*KL + c of the row
-    const int krow = lane / C::KL, kc = lane % C::KL;
+    // ---- q slice of this lane (K-phase layout): vectors j*KL + kc of the row
+    const int krow = lane / KL, kc = lane % KL;
     const QT* qrow = reinterpret_cast<const QT*>(a.q) + (int64_t(b) * hq + int64_t(g) * G) * D;
     uint32_t qpk[kDot2 ? G : 1][kDot2 ? C::EPL / 2 : 1];
     float qf[kDot2 ? 1 : G][kDot2 ? 1 : C::EPL];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
-        for (int j = 0; j < C::KVPL; ++j) {
-            const int d0 = (j * C::KL + kc) * C::EPV;
+        for (int j = 0; j < KVPL; ++j) {
+            const int d0 = (j * KL + kc) * EPV;
             if constexpr (kDot2) {
                 const uint32_t* src = reinterpret_cast<const uint32_t*>(qrow + h * D + d0);
 #pragma unroll
-                for (int e = 0; e < C::EPV / 2; ++e) qpk[h][j * (C::EPV / 2) + e] = src[e];
+                for (int e = 0; e < EPV / 2; ++e) qpk[h][j * (EPV / 2) + e] = src[e];
             } else {
 #pragma unroll
-                for (int e = 0; e < C::EPV; ++e) {
+                for (int e = 0; e < EPV; ++e) {
                     const QT x = qrow[h * D + d0 + e];
-                    if constexpr (QDT == PA_DTYPE_BF16) qf[h][j * C::EPV + e] = bf16_to_f32(x);
-                    else qf[h][j * C::EPV + e] = x;
+                    if constexpr (QDT == PA_DTYPE_BF16) qf[h][j * EPV + e] = bf16_to_f32(x);
+                    else qf[h][j * EPV + e] = x;
                 }
             }
         }
     }
 
-    float m_run[G], l_run[G], acc[G][C::EPV];
+    float m_ref[G], l_run[G], acc[G][EPV];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        m_run[h] = -INFINITY;
+        m_ref[h] = -INFINITY;
         l_run[h] = 0.0f;
 #pragma unroll
-        for (int e = 0; e < C::EPV; ++e) acc[h][e] = 0.0f;
+        for (int e = 0; e < EPV; ++e) acc[h][e] = 0.0f;
     }
     bool bad = false;
-    const int vrg = lane / C::VL, vcol = lane % C::VL;
+    const int vrg = lane / VL, vcol = lane % VL;
 
-    for (int i = w; i < npass; i += kWaves) {
-        const int tbase = t0 + i * C::TPP;
-        // ---- block ids of this pass (uniform scalar loads; clamped to the live entries)
-        const int e0 = tbase / BS;
-        int blk[C::BPP];
-#pragma unroll
-        for (int q2 = 0; q2 < C::BPP; ++q2) {
-            const int e = min(e0 + q2, nblk - 1);
-            int id = table[e];
-            if (id < 0 || id >= a.num_blocks) {
-                // only an error if a live token of this pass lies in that block
-                if ((e0 + q2) * BS < t1) bad = true;
-                id = 0;
-            }
-            blk[q2] = id;
+    // ---- block ids of this wave's passes, 64 at a time: lane j holds the first (and for
+    // BPP == 2 the second) block of pass w + kWaves * (k0 + j); ids outside the pool are
+    // recorded as an error and replaced by 0 so every address stays inside the cache
+    int ent_a = 0, ent_b = 0;
+    auto load_entries = [&](int k0) {
+        const int kk = k0 + lane;
+        const int tb = t0 + (w + kWaves * kk) * TPP;
+        const bool live = kk < nk;
+        const int e = tb / BS;
+        int id = table[min(e, nblk - 1)];
+        if (id < 0 || id >= a.num_blocks) {
+            if (live) bad = true;
+            id = 0;
         }
-        // ---- issue K and V loads
-        const int tk = tbase + krow;
-        const bool kvalid = tk < t1;
-        U4 kv[C::KVPL];
+        ent_a = id;
+        if constexpr (BPP == 2) {
+            int id2 = table[min(e + 1, nblk - 1)];
+            if (id2 < 0 || id2 >= a.num_blocks) {
+                if (live && (e + 1) * BS < t1) bad = true;
+                id2 = 0;
+            }
+            ent_b = id2;
+        }
+    };
+    load_entries(0);
+
+    // ---- issue the K and V loads of pass k (no masking: rows past the end still lie in a
+    // valid block; their contributions are masked in compute)
+    auto issue = [&](int k, U4 (&kb)[KVPL], U4 (&vb)[VR]) {
+        if ((k & 63) == 0 && k > 0) load_entries(k);
+        const int tb = t0 + (w + kWaves * k) * TPP;
+        const int b0 = __builtin_amdgcn_readlane(ent_a, k & 63);
+        const int b1 = BPP == 2 ? __builtin_amdgcn_readlane(ent_b, k & 63) : b0;
+        const int row0 = BPP == 2 ? 0 : tb % BS;
         {
-            const int bi = C::BPP == 1 ? 0 : (krow / BS);
-            const CT* rowp = kbase + ((int64_t(blk[bi]) * a.hkv + g) * BS + (tk % BS)) * D;
+            const int blk = (BPP == 2 && krow >= BS) ? b1 : b0;
+            const int row = BPP == 2 ? krow % BS : row0 + krow;
+            const CT* p = kbase + (int64_t(blk) * block_stride + head_tile) + (row * D + kc * EPV);
 #pragma unroll
-            for (int j = 0; j < C::KVPL; ++j) {
-                kv[j] = kvalid ? ld16(rowp + (j * C::KL + kc) * C::EPV) : U4{0, 0, 0, 0};
-            }
+            for (int j = 0; j < KVPL; ++j) kb[j] = ld16(p + j * KL * EPV);
         }
-        U4 vv[C::VR];
 #pragma unroll
-        for (int r = 0; r < C::VR; ++r) {
-            const int row = vrg + r * C::VRG;
-            const int tv = tbase + row;
-            const int bi = C::BPP == 1 ? 0 : (row / BS);
-            const CT* rowp = vbase + ((int64_t(blk[bi]) * a.hkv + g) * BS + (tv % BS)) * D;
-            vv[r] = tv < t1 ? ld16(rowp + vcol * C::EPV) : U4{0, 0, 0, 0};
+        for (int r = 0; r < VR; ++r) {
+            const int rt = vrg + r * VRG;
+            const int blk = (BPP == 2 && rt >= BS) ? b1 : b0;
+            const int row = BPP == 2 ? rt % BS : row0 + rt;
+            vb[r] = ld16(vbase + (int64_t(blk) * block_stride + head_tile) + (row * D + vcol * EPV));
         }
+    };
 
-        // ---- scores of this lane's token for the G heads
+    auto compute = [&](int k, U4 (&kb)[KVPL], U4 (&vb)[VR]) {
+        const int tb = t0 + (w + kWaves * k) * TPP;
+        const bool partial = tb + TPP > t1;     // uniform: the pass runs past the partition end
+        // scores of this lane's token row for the G heads
         float s[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             float accs = 0.0f;
 #pragma unroll
-            for (int j = 0; j < C::KVPL; ++j) {
+            for (int j = 0; j < KVPL; ++j) {
                 if constexpr (kDot2) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        accs = __builtin_amdgcn_fdot2_f32_bf16(
-                            __builtin_bit_cast(bf16x2v, qpk[h][j * 4 + e]),
-                            __builtin_bit_cast(bf16x2v, u4_get(kv[j], e)), accs, false);
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        accs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, qpk[h][j * 4 + e]),
+                                                               __builtin_bit_cast(bf16x2v, u4_get(kb[j], e)),
+                                                               accs, false);
                 } else if constexpr (CDT == PA_DTYPE_F32) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        accs = fmaf(qf[h][j * 4 + e], __uint_as_float(u4_get(kv[j], e)), accs);
+                    for (int e = 0; e < 4; ++e) accs = fmaf(qf[h][j * 4 + e], __uint_as_float(u4_get(kb[j], e)), accs);
                 } else {  // fp8
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const uint32_t wv = u4_get(kv[j], e);
+                        const uint32_t wv = u4_get(kb[j], e);
                         const float2v lo = e4m3x2_to_f32<false>(wv);
                         const float2v hi = e4m3x2_to_f32<true>(wv);
                         accs = fmaf(qf[h][j * 16 + 4 * e + 0], lo.x, accs);
@@ -387,57 +585,59 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeAr
                     }
                 }
             }
-#pragma unroll
-            for (int m = 1; m < C::KL; m <<= 1) accs += xor_shfl(accs, m);
-            s[h] = kvalid ? accs * sc : -INFINITY;
+            s[h] = group_sum<KL>(accs) * sc;
         }
-
-        // ---- online softmax over the pass
-        float p[G], alpha[G];
+        if (partial) {
+            const bool kvalid = tb + krow < t1;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float mx = s[h];
+            for (int h = 0; h < G; ++h) s[h] = kvalid ? s[h] : -INFINITY;
+        }
+        // online softmax: rescale only when a score passes the reference by the threshold
+        bool over = false;
 #pragma unroll
-            for (int m = C::KL; m < 64; m <<= 1) mx = fmaxf(mx, xor_shfl(mx, m));
-            const float m_new = fmaxf(m_run[h], mx);
-            alpha[h] = __builtin_amdgcn_exp2f(m_run[h] - m_new);
-            p[h] = __builtin_amdgcn_exp2f(s[h] - m_new);
-            m_run[h] = m_new;
+        for (int h = 0; h < G; ++h) over |= s[h] > m_ref[h] + kRescaleThreshold;
+        if (__builtin_amdgcn_ballot_w64(over) != 0) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float m_new = fmaxf(m_ref[h], wave_max_of_groups<KL>(s[h]));
+                const float alpha = __builtin_amdgcn_exp2f(m_ref[h] - m_new);   // 0 on the first pass
+                m_ref[h] = m_new;
+                l_run[h] *= alpha;
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) acc[h][e] *= alpha;
+            }
         }
         if (kc == 0) {
 #pragma unroll
-            for (int h = 0; h < G; ++h) s_p[w][krow][h] = p[h];
+            for (int h = 0; h < G; ++h) s_p[w][krow][h] = __builtin_amdgcn_exp2f(s[h] - m_ref[h]);
         }
         wave_sync_lds();
-
-        // ---- V phase
+        if (partial) {   // rows past the end may hold anything: never multiply them in
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            l_run[h] *= alpha[h];
-#pragma unroll
-            for (int e = 0; e < C::EPV; ++e) acc[h][e] *= alpha[h];
+            for (int r = 0; r < VR; ++r)
+                if (tb + vrg + r * VRG >= t1) vb[r] = U4{0, 0, 0, 0};
         }
 #pragma unroll
-        for (int r = 0; r < C::VR; ++r) {
-            const int row = vrg + r * C::VRG;
+        for (int r = 0; r < VR; ++r) {
+            const int rt = vrg + r * VRG;
             float pv[G];
 #pragma unroll
-            for (int h = 0; h < G; ++h) pv[h] = s_p[w][row][h];
-            float vf[C::EPV];
+            for (int h = 0; h < G; ++h) pv[h] = s_p[w][rt][h];
+            float vf[EPV];
             if constexpr (CDT == PA_DTYPE_F32) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) vf[e] = __uint_as_float(u4_get(vv[r], e));
+                for (int e = 0; e < 4; ++e) vf[e] = __uint_as_float(u4_get(vb[r], e));
             } else if constexpr (CDT == PA_DTYPE_BF16) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const uint32_t x = u4_get(vv[r], e);
+                    const uint32_t x = u4_get(vb[r], e);
                     vf[2 * e] = __uint_as_float(x << 16);
                     vf[2 * e + 1] = __uint_as_float(x & 0xffff0000u);
                 }
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const uint32_t x = u4_get(vv[r], e);
+                    const uint32_t x = u4_get(vb[r], e);
                     const float2v lo = e4m3x2_to_f32<false>(x);
                     const float2v hi = e4m3x2_to_f32<true>(x);
                     vf[4 * e + 0] = lo.x;
@@ -450,33 +650,44 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeAr
             for (int h = 0; h < G; ++h) {
                 l_run[h] += pv[h];
 #pragma unroll
-                for (int e = 0; e < C::EPV; ++e) acc[h][e] = fmaf(pv[h], vf[e], acc[h][e]);
+                for (int e = 0; e < EPV; ++e) acc[h][e] = fmaf(pv[h], vf[e], acc[h][e]);
             }
         }
         wave_sync_lds();   // s_p is rewritten by the next pass
+    };
+
+    // ---- software-pipelined pass loop: the loads of pass k+1 are in flight while pass k
+    // is computed (two register sets, alternating)
+    {
+        U4 ka[KVPL], va[VR], kb2[KVPL], vb2[VR];
+        if (nk > 0) issue(0, ka, va);
+        for (int k = 0; k < nk; k += 2) {
+            if (k + 1 < nk) issue(k + 1, kb2, vb2);
+            compute(k, ka, va);
+            if (k + 1 >= nk) break;
+            if (k + 2 < nk) issue(k + 2, ka, va);
+            compute(k + 1, kb2, vb2);
+        }
     }
 
     // ---- reduce the V-phase row groups of this wave
 #pragma unroll
-    for (int m = C::VL; m < 64; m <<= 1) {
+    for (int h = 0; h < G; ++h) {
+        l_run[h] = sum_over_row_groups<VL>(l_run[h]);
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            l_run[h] += xor_shfl(l_run[h], m);
-#pragma unroll
-            for (int e = 0; e < C::EPV; ++e) acc[h][e] += xor_shfl(acc[h][e], m);
-        }
+        for (int e = 0; e < EPV; ++e) acc[h][e] = sum_over_row_groups<VL>(acc[h][e]);
     }
-    if (lane < C::VL) {
+    if (lane < VL) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
 #pragma unroll
-            for (int e = 0; e < C::EPV; ++e) s_acc[w][h][lane * C::EPV + e] = acc[h][e];
+            for (int e = 0; e < EPV; ++e) s_acc[w][h][lane * EPV + e] = acc[h][e];
         }
     }
     if (lane == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            s_m[w][h] = m_run[h];
+            s_m[w][h] = m_ref[h];
             s_l[w][h] = l_run[h];
         }
     }
@@ -505,45 +716,66 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeAr
             const float o = num / den * vsc;
             if constexpr (QDT == PA_DTYPE_BF16) out[idx] = f32_to_bf16(o); else out[idx] = o;
         } else {
+            // partials go out as agent-scope (coherent) stores, see below
             const int64_t row = (int64_t(b) * hq + int64_t(g) * G + h) * a.max_parts + part;
-            a.ws_acc[row * D + dim] = num * vsc;
+            store_agent(a.ws_acc + row * D + dim, num * vsc);
             if (dim == 0) {
-                a.ws_m[row] = M;
-                a.ws_l[row] = den;
+                store_agent(a.ws_m + row, M);
+                store_agent(a.ws_l + row, den);
             }
         }
     }
+    if (single) return;
+
+    // ---- log-sum-exp merge of the partitions, in up to two levels: the last work-group
+    // of each group of kMergeGroup partitions to finish merges that group; with more than
+    // one group, the last group-merger then merges the groups.  Partials are written with
+    // agent-scope stores (coherent across the XCDs' L2s); draining the store counter makes
+    // them visible at agent scope before a ticket is taken, and mergers read them with
+    // agent-scope loads.  This avoids agent-scope fences, whose L2 write-back/invalidate
+    // would serialise the work-groups of an XCD.  Counters are left at zero.
+    const int ngroups = (nparts + kMergeGroup - 1) / kMergeGroup;
+    const int grp = part / kMergeGroup;
+    const int64_t bg = int64_t(b) * a.hkv + g;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int* ctr = a.ws_ctr + bg * a.max_groups + grp;
+        const int members = min(kMergeGroup, nparts - grp * kMergeGroup);
+        const int ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = ticket == members - 1;
+        if (s_last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    const int64_t rows1 = (int64_t(b) * hq + int64_t(g) * G) * a.max_parts;    // head h: + h * max_parts
+    const int first = grp * kMergeGroup, count = min(kMergeGroup, nparts - first);
+    if (ngroups == 1) {
+        merge_rows<QDT, D, G>(a.ws_m, a.ws_l, a.ws_acc, rows1 + first, a.max_parts, count, out, nullptr, nullptr,
+                              nullptr, 0);
+        return;
+    }
+    const int64_t rows2 = (int64_t(b) * hq + int64_t(g) * G) * a.max_groups;
+    merge_rows<QDT, D, G>(a.ws_m, a.ws_l, a.ws_acc, rows1 + first, a.max_parts, count, nullptr, a.ws_m2 + rows2 + grp,
+                          a.ws_l2 + rows2 + grp, a.ws_acc2 + (rows2 + grp) * D, a.max_groups);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int* ctr = a.ws_ctr + int64_t(a.max_groups) * gridDim.y * gridDim.z + bg;
+        const int ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = ticket == ngroups - 1;
+        if (s_last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    merge_rows<QDT, D, G>(a.ws_m2, a.ws_l2, a.ws_acc2, rows2, a.max_groups, ngroups, out, nullptr, nullptr, nullptr, 0);
 }
 
-// ------------------------------------------------------------------ decode: merge
+// ------------------------------------------------------------------ workspace clear
 
-template <int QDT, int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(const DecodeArgs a, int block_size) {
-    using QT = typename Elem<QDT>::T;
-    const int h = blockIdx.x, b = blockIdx.y;
-    const int hq = gridDim.x;
-    const int L_raw = a.seq_lens[b];
-    const bool len_bad = L_raw < 0 || L_raw > a.max_seq_len || L_raw > a.max_blocks * block_size;
-    const int L = len_bad ? 0 : L_raw;
-    const int nparts = L > 0 ? (L + a.part_tokens - 1) / a.part_tokens : 1;
-    if (nparts <= 1) return;   // written by the partition kernel
-    const int64_t row0 = (int64_t(b) * hq + h) * a.max_parts;
-    const int dim = threadIdx.x;
-    float M = -INFINITY;
-    for (int p = 0; p < nparts; ++p) M = fmaxf(M, a.ws_m[row0 + p]);
-    float num = 0.0f, den = 0.0f;
-    for (int p = 0; p < nparts; ++p) {
-        const float f = __builtin_amdgcn_exp2f(a.ws_m[row0 + p] - M);
-        num = fmaf(f, a.ws_acc[(row0 + p) * D + dim], num);
-        den = fmaf(f, a.ws_l[row0 + p], den);
-    }
-    // a NaN partial (bad block id) must win over fmaxf's NaN-dropping
-    for (int p = 0; p < nparts; ++p) {
-        if (__builtin_isnan(a.ws_m[row0 + p])) den = __builtin_nanf("");
-    }
-    const float o = num / den;
-    QT* out = reinterpret_cast<QT*>(a.out) + (int64_t(b) * hq + h) * D;
-    if constexpr (QDT == PA_DTYPE_BF16) out[dim] = f32_to_bf16(o); else out[dim] = o;
+__global__ __launch_bounds__(256) void zero_kernel(uint32_t* __restrict__ p, int64_t n_words) {
+    for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n_words; i += int64_t(gridDim.x) * blockDim.x)
+        p[i] = 0u;
 }
 
 // ------------------------------------------------------------------ host helpers
@@ -564,17 +796,29 @@ int grid_for(int64_t work, int per_block) {
     return static_cast<int>(blocks < 1 ? 1 : blocks);
 }
 
+// Workspace (each region 256-byte aligned):
+//   [tickets: requests x q heads x groups int32 (level 1)][tickets: requests x q heads (level 2)]
+//   [m1, l1: rows1][acc1: rows1 x d]   rows1 = requests x q heads x partitions
+//   [m2, l2: rows2][acc2: rows2 x d]   rows2 = requests x q heads x groups (only with > 1 group)
+// (q heads bound the KV heads the tickets are indexed by.)
 struct WsLayout {
-    int64_t m_off, l_off, acc_off, bytes;
+    int64_t ctr_off, m_off, l_off, acc_off, m2_off, l2_off, acc2_off, bytes;
+    int groups;
 };
 
-WsLayout ws_layout(int64_t rows, int d) {
+WsLayout ws_layout(int64_t seqs_x_heads, int64_t parts, int d) {
     auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
     WsLayout w;
-    w.m_off = 0;
-    w.l_off = up(rows * 4);
-    w.acc_off = w.l_off + up(rows * 4);
-    w.bytes = w.acc_off + up(rows * int64_t(d) * 4);
+    w.groups = static_cast<int>((parts + kMergeGroup - 1) / kMergeGroup);
+    const int64_t rows1 = seqs_x_heads * parts, rows2 = w.groups > 1 ? seqs_x_heads * w.groups : 0;
+    w.ctr_off = 0;
+    w.m_off = up(seqs_x_heads * (w.groups + 1) * 4);
+    w.l_off = w.m_off + up(rows1 * 4);
+    w.acc_off = w.l_off + up(rows1 * 4);
+    w.m2_off = w.acc_off + up(rows1 * int64_t(d) * 4);
+    w.l2_off = w.m2_off + up(rows2 * 4);
+    w.acc2_off = w.l2_off + up(rows2 * 4);
+    w.bytes = w.acc2_off + up(rows2 * int64_t(d) * 4);
     return w;
 }
 
@@ -582,13 +826,7 @@ template <int CDT, int QDT, int D, int BS, int G>
 int launch_decode(const DecodeArgs& a, int B, hipStream_t st) {
     dim3 grid(a.max_parts, a.hkv, B);
     hipLaunchKernelGGL((decode_partial_kernel<CDT, QDT, D, BS, G>), grid, dim3(kThreads), 0, st, a);
-    int rc = check_launch("pa_decode (partition pass)");
-    if (rc != PA_OK) return rc;
-    if (a.max_parts > 1) {
-        hipLaunchKernelGGL((decode_merge_kernel<QDT, D>), dim3(a.hkv * G, B), dim3(D), 0, st, a, BS);
-        rc = check_launch("pa_decode (merge)");
-    }
-    return rc;
+    return check_launch("pa_decode");
 }
 
 template <int CDT, int QDT, int D, int BS>
@@ -684,7 +922,7 @@ int64_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
     const int pt = effective_partition(partition_tokens, unit);
     const int64_t parts = max_seq_len > 0 ? (int64_t(max_seq_len) + pt - 1) / pt : 1;
     if (parts <= 1) return 0;
-    return ws_layout(int64_t(num_seqs) * num_q_heads * parts, head_dim).bytes;
+    return ws_layout(int64_t(num_seqs) * num_q_heads, parts, head_dim).bytes;
 }
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -736,7 +974,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     int pt = effective_partition(partition_tokens, unit);
     int64_t parts = max_seq_len > 0 ? (int64_t(max_seq_len) + pt - 1) / pt : 1;
     if (parts > 1) {
-        const WsLayout lay = ws_layout(int64_t(num_seqs) * num_q_heads * parts, head_dim);
+        const WsLayout lay = ws_layout(int64_t(num_seqs) * num_q_heads, parts, head_dim);
         if (!workspace) {
             // no workspace: one partition per request
             pt = (max_seq_len + unit - 1) / unit * unit;
@@ -746,6 +984,11 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
                         (long long)workspace_bytes, (long long)lay.bytes);
         } else {
             char* base = static_cast<char*>(workspace);
+            a.ws_ctr = reinterpret_cast<int*>(base + lay.ctr_off);
+            a.max_groups = lay.groups;
+            a.ws_m2 = reinterpret_cast<float*>(base + lay.m2_off);
+            a.ws_l2 = reinterpret_cast<float*>(base + lay.l2_off);
+            a.ws_acc2 = reinterpret_cast<float*>(base + lay.acc2_off);
             a.ws_m = reinterpret_cast<float*>(base + lay.m_off);
             a.ws_l = reinterpret_cast<float*>(base + lay.l_off);
             a.ws_acc = reinterpret_cast<float*>(base + lay.acc_off);
@@ -763,6 +1006,19 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     if (cache_dtype == PA_DTYPE_BF16)
         return dispatch_d<PA_DTYPE_BF16, PA_DTYPE_BF16>(head_dim, block_size, G, a, num_seqs, st);
     return dispatch_d<PA_DTYPE_FP8_E4M3, PA_DTYPE_BF16>(head_dim, block_size, G, a, num_seqs, st);
+}
+
+int pa_decode_workspace_init(void* workspace, int64_t workspace_bytes, void* stream) {
+    pagedkv::clear_error();
+    if (workspace_bytes < 0 || workspace_bytes % 4 != 0)
+        return fail(PA_ERR_INVALID, "pa_decode_workspace_init: %lld bytes is not a multiple of 4", (long long)workspace_bytes);
+    if (workspace_bytes == 0) return PA_OK;
+    if (!workspace || !aligned16(workspace))
+        return fail(PA_ERR_INVALID, "pa_decode_workspace_init: NULL or misaligned workspace");
+    const int64_t words = workspace_bytes / 4;
+    hipLaunchKernelGGL(zero_kernel, dim3(grid_for(words, 256)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<uint32_t*>(workspace), words);
+    return check_launch("pa_decode_workspace_init");
 }
 
 int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst, int32_t num_pairs,

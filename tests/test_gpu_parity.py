@@ -398,3 +398,21 @@ def test_fork_append_cow_decode():
                  1 / math.sqrt(d), bs)
     ref = OA.decode(q, okc, ovc, np.array(otab), np.array(oL), np.float32(1 / math.sqrt(d)), bs, "bf16", "bf16")
     check_close(out_f64(out), ref, "bf16", "cow")
+
+
+def test_workspace_reuse_across_shapes():
+    """The binding's shared workspace is reused by calls of different sizes, alternating;
+    every call matches the oracle (the merge tickets are re-zeroed when the sizes change
+    and left at zero by every call of the same sizes)."""
+    shapes = [workloads.gqa_uniform(B=6, L=2000, layers=1, seed_index=90, name="ws_a"),
+              workloads.gqa_uniform(B=40, L=700, layers=1, seed_index=91, name="ws_b"),
+              workloads.long_context(B=2, L=9000, seed_index=92, name="ws_c")]
+    sides = []
+    for w in shapes:
+        vals = workloads.host_values(w)
+        sides.append((GpuSide(w, vals, partition_tokens=128), OracleSide(w, vals)))
+    refs = [o.decode() for _, o in sides]
+    for order in ([0, 1, 2, 0, 0, 2, 1, 1], [2, 2, 0, 1]):
+        for i in order:
+            g, _ = sides[i]
+            check_close(out_f64(g.decode()), refs[i], "bf16", g.w.name)

@@ -79,12 +79,18 @@ def test_errors_are_reported():
 
 
 def test_workspace_bytes():
-    # 16 requests x 32 heads, 4096 tokens in partitions of 512 -> 8 partitions
+    """[tickets: seqs x q heads x (groups + 1) int32][m1][l1][acc1][m2][l2][acc2], each region
+    256-byte aligned; groups = ceil(partitions / 16), the level-2 rows exist only with > 1
+    group."""
+    # 16 requests x 32 heads, 4096 tokens in partitions of 512 -> 8 partitions, 1 group
     rows = 16 * 32 * 8
-    want = rows * 4 + rows * 4 + rows * 128 * 4
+    want = 16 * 32 * 2 * 4 + rows * 4 + rows * 4 + rows * 128 * 4
     assert pk.pa_decode_workspace_bytes(16, 32, 128, 4096, 512, 16) == want
     assert pk.pa_decode_workspace_bytes(4, 8, 64, 200, 512, 16) == 0          # one partition
-    assert pk.pa_decode_workspace_bytes(2, 64, 128, 131072, 512, 16) == 2 * 64 * 256 * (8 + 512)
+    # 2 requests x 64 heads at 131072 tokens: 256 partitions in 16 groups
+    r1, r2 = 2 * 64 * 256, 2 * 64 * 16
+    want = 2 * 64 * 17 * 4 + 2 * r1 * 4 + r1 * 128 * 4 + 2 * r2 * 4 + r2 * 128 * 4
+    assert pk.pa_decode_workspace_bytes(2, 64, 128, 131072, 512, 16) == want
 
 
 # --------------------------------------------------------------------------- allocator parity
