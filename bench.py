@@ -2,8 +2,10 @@
 """Decode-step benchmark of the paged KV cache on one MI355X.
 
 Workload (default): Llama-3-8B-shaped GQA decode -- 32 layers, batch 16, 32 q heads / 8 KV
-heads, head_dim 128, bf16 cache and q, block size 16, every request at 4096 tokens when the
-timed steps start, 32 per-layer caches (8.6 GB) sharing one seeded-permutation block table.
+heads, head_dim 128, bf16 cache and q, block size 16, every request at 4096 tokens in the
+first timed step, 32 per-layer caches (8.6 GB) sharing one seeded-permutation block table;
+split-K partitions chosen by the library (partition_tokens 0: one work-group per compute
+unit).
 
 One step is one pass of the whole hot path over the batch:
   1. host allocator: append one token to each request (slots; copy-on-write pairs, if any,
@@ -141,9 +143,9 @@ def run(args):
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     steps, warm = args.steps, args.warmup
-    L0 = 4096
+    L0 = 4096                      # decode length of every request in the first timed step
     grow = steps + warm
-    w = workloads.gqa_uniform(B=16, L=L0, layers=32, spare_blocks=16 * (grow // 16 + 2))
+    w = workloads.gqa_uniform(B=16, L=L0 - warm, layers=32, spare_blocks=16 * (grow // 16 + 2))
     B, Hq, Hkv, d, bs, layers = w.B, w.Hq, w.Hkv, w.d, w.bs, w.layers
     max_blocks = -(-(L0 + grow) // bs)
     max_seq = max_blocks * bs
@@ -151,7 +153,8 @@ def run(args):
     log(f"workload {w.name}: {layers} layers x batch {B}, {Hq}q/{Hkv}kv, d {d}, block {bs}, "
         f"{w.num_blocks} blocks per layer")
 
-    # allocator and prefill (L0 - 1 tokens per request; the first step appends token L0)
+    # allocator and prefill (L0 - warm - 1 tokens per request: the warmup steps append the next
+    # warm tokens, and the first timed step appends token L0)
     alloc = pk.Allocator(w.num_blocks, bs, w.free_order)
     slots = []
     for op in w.ops:
@@ -186,7 +189,9 @@ def run(args):
     pin_tab = [torch.empty((B, max_blocks), dtype=torch.int32).pin_memory() for _ in range(grow)]
     pin_len = [torch.empty((B,), dtype=torch.int32).pin_memory() for _ in range(grow)]
     pin_slot = [torch.empty((B,), dtype=torch.int64).pin_memory() for _ in range(grow)]
-    nbytes = pk.pa_decode_workspace_bytes(B, Hq, d, max_seq, args.partition_tokens, bs)
+    nbytes = pk.pa_decode_workspace_bytes(B, Hq, Hkv, d, max_seq, args.partition_tokens, bs)
+    part_used = pk.pa_decode_partition_tokens(B, Hkv, max_seq, args.partition_tokens, bs)
+    log(f"split-K partitions of {part_used} tokens (requested {args.partition_tokens}; 0 = automatic)")
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     pk.pa_decode_workspace_init(ws)
     dec = [pk.PreparedDecode(outs[l], q[l], kc[l], vc[l], tables_d, lens_d, scale, bs, max_seq_len=max_seq,
@@ -259,9 +264,10 @@ def run(args):
         "config": {
             "workload": "llama3_8b_gqa_decode: 32 layers x batch 16, 32 q / 8 kv heads, head_dim 128, bf16, "
                         "block 16, 4096 tokens per request at the first timed step (+1 per step), "
-                        "split-K partitions of %d tokens" % args.partition_tokens,
+                        "split-K partitions of %d tokens" % part_used,
             "layers": layers, "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": d,
-            "block_size": bs, "seq_len_start": int(lens_per_step[0][0]), "partition_tokens": args.partition_tokens,
+            "block_size": bs, "seq_len_start": int(lens_per_step[0][0]), "seq_len_end": int(lens_per_step[-1][0]),
+            "partition_tokens": part_used,
             "kv_cache_gb": round(2 * layers * kc[0].numel() * 2 / 1e9, 3),
         },
         "roofline": {
@@ -285,7 +291,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--partition-tokens", type=int, default=512)
+    ap.add_argument("--partition-tokens", type=int, default=0, help="split-K partition size; 0 = automatic")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",

@@ -104,11 +104,15 @@ int pa_kv_write(const void* k, const void* v, const int64_t* slot_mapping, int64
  * weighted sum are accumulated in float32; out is rounded to nearest even in q's dtype.
  * L = 0 gives out = 0.  Slots at positions >= L are never read (they may hold anything).
  *
- * Long contexts are split into partitions of `partition_tokens` logical tokens (rounded up
- * to a multiple of max(64, block_size); 0 means 512); each partition is reduced to
- * (max score, sum of exponentials, unnormalised weighted sum) and the partitions are
- * merged by rescaling to the largest maximum (log-sum-exp).  The result depends only on
- * logical positions, so it is bit-identical under any physical placement of the blocks.
+ * Long contexts are split into partitions of `partition_tokens` logical tokens; each partition
+ * is reduced to (max score, sum of exponentials, unnormalised weighted sum) and the
+ * partitions are merged by rescaling to the largest maximum (log-sum-exp).  An explicit
+ * partition_tokens > 0 is rounded up to a multiple of max(64, block_size).  0 chooses it
+ * automatically (pa_decode_partition_tokens gives the value): with fewer (request, KV head)
+ * pairs than the device has compute units, each request is cut into ceil(CUs / pairs) equal
+ * partitions of ceil(max_seq_len / parts) tokens (one work-group per compute unit); otherwise
+ * partitions are 2048 tokens.  For a given partition size the result depends only on logical
+ * positions, so it is bit-identical under any physical placement of the blocks.
  *
  *  out           device, [num_seqs][num_q_heads][head_dim] of q_dtype
  *  q             device, [num_seqs][num_q_heads][head_dim] of q_dtype
@@ -124,7 +128,7 @@ int pa_kv_write(const void* k, const void* v, const int64_t* slot_mapping, int64
  *                request and KV head merges that group, and with more than one group the last
  *                group-merger merges the groups, all in the same launch.  Zero the workspace
  *                (pa_decode_workspace_init) before its first use and whenever it is reused
- *                with different (num_seqs, num_q_heads, head_dim, max_seq_len,
+ *                with different (num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
  *                partition_tokens, block_size); consecutive calls with the same sizes leave
  *                the counters at zero and need no re-zeroing.  Calls that share a workspace
  *                must not run concurrently (order them on one stream).
@@ -134,9 +138,14 @@ int pa_kv_write(const void* k, const void* v, const int64_t* slot_mapping, int64
  * holds a block id outside [0, num_blocks) within its first ceil(L / block_size) entries,
  * gets out = NaN for all its heads.
  */
-int64_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                  int32_t max_seq_len, int32_t partition_tokens,
+int64_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_seq_len, int32_t partition_tokens,
                                   int32_t block_size);
+
+/* The partition size in tokens that pa_decode uses for these sizes on the current device
+ * (partition_tokens as passed to pa_decode; 0 = automatic), or a negative status. */
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
+                                   int32_t partition_tokens, int32_t block_size);
 
 /* Zero a decode workspace (a store kernel on `stream`; no memset node is recorded, so this
  * may be captured in a graph).  workspace_bytes must be a multiple of 4. */

@@ -9,5 +9,5 @@ from ._lib import (  # noqa: F401
     EXPORTED, LIB_PATH, PreparedDecode, PreparedKVWrite, PA_DTYPE_BF16, PA_DTYPE_F32, PA_DTYPE_FP8_E4M3, Allocator, NoBlocksError,
     PagedKVError, UnsupportedError, load, pa_alloc_create, pa_alloc_destroy, pa_alloc_dump,
     pa_alloc_stats, pa_batch_append, pa_block_tables, pa_copy_blocks, pa_decode,
-    pa_decode_workspace_bytes, pa_decode_workspace_init, decode_workspace, pa_kv_write, pa_seq_add, pa_seq_append, pa_seq_fork, pa_seq_free,
+    pa_decode_workspace_bytes, pa_decode_partition_tokens, pa_decode_workspace_init, decode_workspace, pa_kv_write, pa_seq_add, pa_seq_append, pa_seq_fork, pa_seq_free,
 )

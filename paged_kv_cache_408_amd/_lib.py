@@ -21,7 +21,7 @@ PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_FP8_E4M3 = 0, 1, 2
 
 EXPORTED = [
     "pa_last_error", "pa_abi_version", "pa_kv_write", "pa_decode_workspace_bytes",
-    "pa_decode_workspace_init", "pa_decode",
+    "pa_decode_partition_tokens", "pa_decode_workspace_init", "pa_decode",
     "pa_copy_blocks", "pa_alloc_create", "pa_alloc_destroy", "pa_seq_add", "pa_seq_append",
     "pa_batch_append", "pa_seq_fork", "pa_seq_free", "pa_block_tables", "pa_alloc_stats",
     "pa_alloc_dump",
@@ -64,7 +64,8 @@ def load(path: str = LIB_PATH):
         "pa_last_error": (ctypes.c_char_p, []),
         "pa_abi_version": (I32, []),
         "pa_kv_write": (ctypes.c_int, [P, P, P, I64, P, P, I64, I32, I32, I32, I32, I32, P, P, P]),
-        "pa_decode_workspace_bytes": (I64, [I32, I32, I32, I32, I32, I32]),
+        "pa_decode_workspace_bytes": (I64, [I32, I32, I32, I32, I32, I32, I32]),
+        "pa_decode_partition_tokens": (I32, [I32, I32, I32, I32, I32]),
         "pa_decode_workspace_init": (ctypes.c_int, [P, I64, P]),
         "pa_decode": (ctypes.c_int, [P, P, P, P, P, P, F32, I32, I32, I32, I32, I32, I64, I32, I32, I32, I32,
                                      P, P, P, I64, I32, P]),
@@ -153,10 +154,18 @@ def pa_kv_write(k, v, slot_mapping, k_cache, v_cache, *, k_scale=None, v_scale=N
     _check(rc)
 
 
-def pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len, partition_tokens=512,
+def pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_tokens=0,
                               block_size=16) -> int:
-    n = load().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len, partition_tokens,
-                                         block_size)
+    n = load().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                         partition_tokens, block_size)
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def pa_decode_partition_tokens(num_seqs, num_kv_heads, max_seq_len, partition_tokens=0, block_size=16) -> int:
+    """Partition size (tokens) pa_decode uses for these sizes on the current device."""
+    n = load().pa_decode_partition_tokens(num_seqs, num_kv_heads, max_seq_len, partition_tokens, block_size)
     if n < 0:
         _check(int(n))
     return int(n)
@@ -190,12 +199,13 @@ _WORKSPACES = {}
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, block_size, *, max_seq_len=None,
-              k_scale=None, v_scale=None, workspace=None, partition_tokens=512, stream=None, validate=False):
+              k_scale=None, v_scale=None, workspace=None, partition_tokens=0, stream=None, validate=False):
     """Decode attention: out[b, h] = softmax(scale * q[b, h] . K_b^T) . V_b through the block
     table.  q, out: [B, Hq, d]; caches [N, Hkv, bs, d]; block_tables int32 [B, max_blocks];
-    seq_lens int32 [B].  max_seq_len defaults to the table capacity (no device sync).  A
-    zeroed workspace kept per device is used when none is given (it must not be shared by
-    calls in flight on different streams); workspace=False runs every request as a single
+    seq_lens int32 [B].  max_seq_len defaults to the table capacity (no device sync).
+    partition_tokens 0 lets the library choose the split-K partition size.  A zeroed
+    workspace kept per device is used when none is given (it must not be shared by calls in
+    flight on different streams); workspace=False runs every request as a single
     partition."""
     torch = _torch()
     B, Hq, d = q.shape
@@ -220,8 +230,8 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, block_siz
             if live.size and (live.min() < 0 or live.max() >= N):
                 raise ValueError(f"block table row {b} holds an id outside [0, {N})")
     if workspace is None:
-        nbytes = pa_decode_workspace_bytes(B, Hq, d, max_seq_len, partition_tokens, block_size)
-        key = (B, Hq, d, int(max_seq_len), int(partition_tokens), block_size)
+        nbytes = pa_decode_workspace_bytes(B, Hq, Hkv, d, max_seq_len, partition_tokens, block_size)
+        key = (B, Hq, Hkv, d, int(max_seq_len), int(partition_tokens), block_size)
         workspace = decode_workspace(nbytes, q.device, key, stream=stream) if nbytes > 0 else None
     elif workspace is False:          # explicitly none: one partition per request
         workspace = None
@@ -370,7 +380,7 @@ class PreparedDecode:
     where per-call Python overhead would otherwise show next to a ~50 us kernel."""
 
     def __init__(self, out, q, k_cache, v_cache, block_tables, seq_lens, scale, block_size, *, max_seq_len,
-                 workspace, k_scale=None, v_scale=None, partition_tokens=512, stream=None):
+                 workspace, k_scale=None, v_scale=None, partition_tokens=0, stream=None):
         B, Hq, d = q.shape
         N, Hkv, bs, dc = k_cache.shape
         if out.shape != q.shape or v_cache.shape != k_cache.shape or dc != d or bs != block_size:

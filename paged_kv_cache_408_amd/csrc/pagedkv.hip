@@ -41,6 +41,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -51,8 +52,23 @@ using pagedkv::fail;
 
 namespace {
 
-constexpr int kWaves = 4;
+// Decode launch shape, fixed at build time: waves per work-group, K/V passes in flight per
+// wave, and whether K/V are read with non-temporal loads (they are streamed exactly once).
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+#ifndef PA_DECODE_DEPTH
+#define PA_DECODE_DEPTH 2
+#endif
+#ifndef PA_DECODE_NT
+#define PA_DECODE_NT 1
+#endif
+constexpr int kWaves = PA_DECODE_WAVES;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kDepth = PA_DECODE_DEPTH;
+constexpr bool kNonTemporal = PA_DECODE_NT != 0;
+static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves per work-group");
+static_assert(kDepth >= 2 && kDepth <= 4, "2 to 4 passes in flight");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMergeGroup = 16;   // partitions merged together at the first merge level
 
@@ -174,6 +190,18 @@ struct alignas(16) U4 { uint32_t x, y, z, w; };
 
 __device__ __forceinline__ U4 ld16(const void* p) { return *reinterpret_cast<const U4*>(p); }
 
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+// 16-byte load of cached K/V: non-temporal when configured (read once, never reused).
+__device__ __forceinline__ U4 ld16_stream(const void* p) {
+    if constexpr (kNonTemporal) {
+        const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+        return U4{v[0], v[1], v[2], v[3]};
+    } else {
+        return ld16(p);
+    }
+}
+
 __device__ __forceinline__ uint32_t u4_get(const U4& v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
@@ -274,9 +302,49 @@ struct Cfg {
 // block size, so partitions start on pass and block boundaries.
 inline int partition_unit(int block_size) { return block_size > 64 ? block_size : 64; }
 
-inline int effective_partition(int requested, int unit) {
-    int pt = requested > 0 ? requested : 512;
-    return (pt + unit - 1) / unit * unit;
+// Compute units of the current device (cached per device; 256 if it cannot be queried).
+int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();   // leave no sticky error for the next launch check
+        return 256;
+    }
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        n = 256;
+    }
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// Partition size in tokens.  An explicit request is rounded up to the granule.  Automatic
+// (requested == 0): one work-group per compute unit -- with fewer (request, KV head) pairs
+// than compute units, each request is cut into ceil(CUs / pairs) equal partitions of
+// ceil(max_seq_len / parts) tokens; with at least as many pairs as compute units, long
+// requests are cut into partitions of kAutoRaggedPartition tokens so that no single
+// work-group holds a long tail.
+constexpr int kAutoRaggedPartition = 2048;
+
+int64_t resolve_partition(int64_t num_seqs, int64_t hkv, int64_t max_seq_len, int requested, int block_size) {
+    const int64_t unit = partition_unit(block_size);
+    int64_t pt;
+    if (requested > 0) {
+        pt = requested;
+    } else {
+        const int64_t pairs = num_seqs * hkv;
+        const int64_t cus = device_cu_count();
+        if (pairs >= cus) {
+            pt = kAutoRaggedPartition;
+        } else {
+            const int64_t parts = (cus + pairs - 1) / pairs;
+            pt = (max_seq_len + parts - 1) / parts;
+        }
+    }
+    pt = (pt + unit - 1) / unit * unit;
+    return pt < unit ? unit : pt;
 }
 
 struct DecodeArgs {
@@ -433,39 +501,21 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeAr
     const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int hq = a.hkv * G;
-
-    const int L_raw = a.seq_lens[b];
-    const bool len_bad = L_raw < 0 || L_raw > a.max_seq_len || L_raw > a.max_blocks * BS;
-    const int L = len_bad ? 0 : L_raw;
-    const int nparts = L > 0 ? (L + a.part_tokens - 1) / a.part_tokens : 1;
-    if (part >= nparts) return;
-
-    QT* out = reinterpret_cast<QT*>(a.out) + (int64_t(b) * hq + int64_t(g) * G) * D;
-    if (L == 0) {   // empty request (zeros) or invalid length (NaN); single partition
-        const float fill = len_bad ? __builtin_nanf("") : 0.0f;
-        for (int i = threadIdx.x; i < G * D; i += kThreads) {
-            if constexpr (QDT == PA_DTYPE_BF16) out[i] = f32_to_bf16(fill); else out[i] = fill;
-        }
-        return;
-    }
-
     const int t0 = part * a.part_tokens;
-    const int t1 = min(L, t0 + a.part_tokens);
-    const int npass = (t1 - t0 + TPP - 1) / TPP;
-    const int nk = npass > w ? (npass - w + kWaves - 1) / kWaves : 0;   // passes w, w+4, ...
-    const int nblk = (L + BS - 1) / BS;
     const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
-    const CT* kbase = reinterpret_cast<const CT*>(a.k_cache);
-    const CT* vbase = reinterpret_cast<const CT*>(a.v_cache);
-    const int64_t head_tile = int64_t(g) * (BS * D);
-    const int64_t block_stride = int64_t(a.hkv) * (BS * D);
 
-    float sc = a.score_scale;
-    float vsc = 1.0f;
-    if constexpr (CDT == PA_DTYPE_FP8_E4M3) {
-        sc *= a.k_scale[g];
-        vsc = a.v_scale[g];
-    }
+    // ---- block ids of this wave's passes, 64 at a time: lane j holds the first (and for
+    // BPP == 2 the second) block of pass w + kWaves * (k0 + j).  The table is read before the
+    // request's length is known (indexes clamped to the row), so its latency overlaps the
+    // length's; `check_entries` then flags ids outside the pool inside the live range and
+    // replaces every such id by 0, so every address stays inside the cache.
+    int ent_a = 0, ent_b = 0;
+    auto read_entries = [&](int k0) {
+        const int e = (t0 + (w + kWaves * (k0 + lane)) * TPP) / BS;
+        ent_a = a.max_blocks > 0 ? table[min(e, a.max_blocks - 1)] : -1;
+        if constexpr (BPP == 2) ent_b = a.max_blocks > 0 ? table[min(e + 1, a.max_blocks - 1)] : -1;
+    };
+    read_entries(0);
 
     // ---- q slice of this lane (K-phase layout): vectors j*KL + kc of the row
     const int krow = lane / KL, kc = lane % KL;
@@ -492,6 +542,36 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeAr
         }
     }
 
+    const int L_raw = a.seq_lens[b];
+    const bool len_bad = L_raw < 0 || L_raw > a.max_seq_len || L_raw > a.max_blocks * BS;
+    const int L = len_bad ? 0 : L_raw;
+    const int nparts = L > 0 ? (L + a.part_tokens - 1) / a.part_tokens : 1;
+    if (part >= nparts) return;
+
+    QT* out = reinterpret_cast<QT*>(a.out) + (int64_t(b) * hq + int64_t(g) * G) * D;
+    if (L == 0) {   // empty request (zeros) or invalid length (NaN); single partition
+        const float fill = len_bad ? __builtin_nanf("") : 0.0f;
+        for (int i = threadIdx.x; i < G * D; i += kThreads) {
+            if constexpr (QDT == PA_DTYPE_BF16) out[i] = f32_to_bf16(fill); else out[i] = fill;
+        }
+        return;
+    }
+
+    const int t1 = min(L, t0 + a.part_tokens);
+    const int npass = (t1 - t0 + TPP - 1) / TPP;
+    const int nk = npass > w ? (npass - w + kWaves - 1) / kWaves : 0;   // passes w, w+kWaves, ...
+    const CT* kbase = reinterpret_cast<const CT*>(a.k_cache);
+    const CT* vbase = reinterpret_cast<const CT*>(a.v_cache);
+    const int64_t head_tile = int64_t(g) * (BS * D);
+    const int64_t block_stride = int64_t(a.hkv) * (BS * D);
+
+    float sc = a.score_scale;
+    float vsc = 1.0f;
+    if constexpr (CDT == PA_DTYPE_FP8_E4M3) {
+        sc *= a.k_scale[g];
+        vsc = a.v_scale[g];
+    }
+
     float m_ref[G], l_run[G], acc[G][EPV];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -503,36 +583,30 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeAr
     bool bad = false;
     const int vrg = lane / VL, vcol = lane % VL;
 
-    // ---- block ids of this wave's passes, 64 at a time: lane j holds the first (and for
-    // BPP == 2 the second) block of pass w + kWaves * (k0 + j); ids outside the pool are
-    // recorded as an error and replaced by 0 so every address stays inside the cache
-    int ent_a = 0, ent_b = 0;
-    auto load_entries = [&](int k0) {
+    auto check_entries = [&](int k0) {
         const int kk = k0 + lane;
-        const int tb = t0 + (w + kWaves * kk) * TPP;
         const bool live = kk < nk;
-        const int e = tb / BS;
-        int id = table[min(e, nblk - 1)];
-        if (id < 0 || id >= a.num_blocks) {
+        if (ent_a < 0 || ent_a >= a.num_blocks) {
             if (live) bad = true;
-            id = 0;
+            ent_a = 0;
         }
-        ent_a = id;
         if constexpr (BPP == 2) {
-            int id2 = table[min(e + 1, nblk - 1)];
-            if (id2 < 0 || id2 >= a.num_blocks) {
+            const int e = (t0 + (w + kWaves * kk) * TPP) / BS;
+            if (ent_b < 0 || ent_b >= a.num_blocks) {
                 if (live && (e + 1) * BS < t1) bad = true;
-                id2 = 0;
+                ent_b = 0;
             }
-            ent_b = id2;
         }
     };
-    load_entries(0);
+    check_entries(0);
 
     // ---- issue the K and V loads of pass k (no masking: rows past the end still lie in a
     // valid block; their contributions are masked in compute)
     auto issue = [&](int k, U4 (&kb)[KVPL], U4 (&vb)[VR]) {
-        if ((k & 63) == 0 && k > 0) load_entries(k);
+        if ((k & 63) == 0 && k > 0) {
+            read_entries(k);
+            check_entries(k);
+        }
         const int tb = t0 + (w + kWaves * k) * TPP;
         const int b0 = __builtin_amdgcn_readlane(ent_a, k & 63);
         const int b1 = BPP == 2 ? __builtin_amdgcn_readlane(ent_b, k & 63) : b0;
@@ -542,14 +616,14 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeAr
             const int row = BPP == 2 ? krow % BS : row0 + krow;
             const CT* p = kbase + (int64_t(blk) * block_stride + head_tile) + (row * D + kc * EPV);
 #pragma unroll
-            for (int j = 0; j < KVPL; ++j) kb[j] = ld16(p + j * KL * EPV);
+            for (int j = 0; j < KVPL; ++j) kb[j] = ld16_stream(p + j * KL * EPV);
         }
 #pragma unroll
         for (int r = 0; r < VR; ++r) {
             const int rt = vrg + r * VRG;
             const int blk = (BPP == 2 && rt >= BS) ? b1 : b0;
             const int row = BPP == 2 ? rt % BS : row0 + rt;
-            vb[r] = ld16(vbase + (int64_t(blk) * block_stride + head_tile) + (row * D + vcol * EPV));
+            vb[r] = ld16_stream(vbase + (int64_t(blk) * block_stride + head_tile) + (row * D + vcol * EPV));
         }
     };
 
@@ -656,17 +730,31 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeAr
         wave_sync_lds();   // s_p is rewritten by the next pass
     };
 
-    // ---- software-pipelined pass loop: the loads of pass k+1 are in flight while pass k
-    // is computed (two register sets, alternating)
+    // ---- software-pipelined pass loop: kDepth register sets in a ring; the loads of passes
+    // k+1 .. k+kDepth-1 are in flight while pass k is computed.  The steady-state loop issues
+    // unconditionally; the tail drains the ring.
     {
-        U4 ka[KVPL], va[VR], kb2[KVPL], vb2[VR];
-        if (nk > 0) issue(0, ka, va);
-        for (int k = 0; k < nk; k += 2) {
-            if (k + 1 < nk) issue(k + 1, kb2, vb2);
-            compute(k, ka, va);
-            if (k + 1 >= nk) break;
-            if (k + 2 < nk) issue(k + 2, ka, va);
-            compute(k + 1, kb2, vb2);
+        U4 kb[kDepth][KVPL], vb[kDepth][VR];
+#pragma unroll
+        for (int i = 0; i < kDepth - 1; ++i)
+            if (i < nk) issue(i, kb[i], vb[i]);
+        int k = 0;
+        for (; k + 2 * kDepth - 2 < nk; k += kDepth) {   // every pass issued below exists
+#pragma unroll
+            for (int i = 0; i < kDepth; ++i) {
+                issue(k + i + kDepth - 1, kb[(i + kDepth - 1) % kDepth], vb[(i + kDepth - 1) % kDepth]);
+                compute(k + i, kb[i], vb[i]);
+            }
+        }
+        for (; k < nk; k += kDepth) {
+#pragma unroll
+            for (int i = 0; i < kDepth; ++i) {
+                if (k + i < nk) {
+                    if (k + i + kDepth - 1 < nk)
+                        issue(k + i + kDepth - 1, kb[(i + kDepth - 1) % kDepth], vb[(i + kDepth - 1) % kDepth]);
+                    compute(k + i, kb[i], vb[i]);
+                }
+            }
         }
     }
 
@@ -911,18 +999,27 @@ int pa_kv_write(const void* k, const void* v, const int64_t* slot_mapping, int64
     return check_launch("pa_kv_write");
 }
 
-int64_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                  int32_t max_seq_len, int32_t partition_tokens, int32_t block_size) {
+int64_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_seq_len, int32_t partition_tokens,
+                                  int32_t block_size) {
     pagedkv::clear_error();
-    if (num_seqs < 0 || num_q_heads <= 0 || (head_dim != 64 && head_dim != 128) || max_seq_len < 0 ||
-        block_size <= 0) {
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || (head_dim != 64 && head_dim != 128) ||
+        max_seq_len < 0 || partition_tokens < 0 || block_size <= 0) {
         return fail(PA_ERR_INVALID, "pa_decode_workspace_bytes: bad sizes");
     }
-    const int unit = partition_unit(block_size);
-    const int pt = effective_partition(partition_tokens, unit);
+    const int64_t pt = resolve_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens, block_size);
     const int64_t parts = max_seq_len > 0 ? (int64_t(max_seq_len) + pt - 1) / pt : 1;
     if (parts <= 1) return 0;
     return ws_layout(int64_t(num_seqs) * num_q_heads, parts, head_dim).bytes;
+}
+
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
+                                   int32_t partition_tokens, int32_t block_size) {
+    pagedkv::clear_error();
+    if (num_seqs < 0 || num_kv_heads <= 0 || max_seq_len < 0 || partition_tokens < 0 || block_size <= 0)
+        return fail(PA_ERR_INVALID, "pa_decode_partition_tokens: bad sizes");
+    const int64_t pt = resolve_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens, block_size);
+    return pt > 0x3fffffff ? 0x3fffffff : static_cast<int32_t>(pt);
 }
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -971,7 +1068,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     a.max_seq_len = max_seq_len;
 
     const int unit = partition_unit(block_size);
-    int pt = effective_partition(partition_tokens, unit);
+    int64_t pt = resolve_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens, block_size);
     int64_t parts = max_seq_len > 0 ? (int64_t(max_seq_len) + pt - 1) / pt : 1;
     if (parts > 1) {
         const WsLayout lay = ws_layout(int64_t(num_seqs) * num_q_heads, parts, head_dim);
@@ -994,9 +1091,10 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
             a.ws_acc = reinterpret_cast<float*>(base + lay.acc_off);
         }
     }
-    if (pt <= 0) pt = unit;
+    if (pt > int64_t(max_seq_len) + unit) pt = (int64_t(max_seq_len) + unit - 1) / unit * unit;   // one partition
+    if (pt < unit) pt = unit;
     if (parts > 65535) return fail(PA_ERR_UNSUPPORTED, "pa_decode: %lld partitions per request", (long long)parts);
-    a.part_tokens = pt;
+    a.part_tokens = static_cast<int>(pt);
     a.max_parts = static_cast<int>(parts);
 
     const int G = num_q_heads / num_kv_heads;

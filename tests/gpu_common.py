@@ -62,7 +62,7 @@ def dev_sentinel_cache(w):
 class GpuSide:
     """The library path: C++ allocator, pa_kv_write, pa_decode."""
 
-    def __init__(self, w, vals, partition_tokens=512, workspace=True):
+    def __init__(self, w, vals, partition_tokens=0, workspace=True):
         self.w = w
         self.alloc = pk.Allocator(w.num_blocks, w.bs, w.free_order)
         self.kc = dev_sentinel_cache(w)
@@ -110,7 +110,7 @@ class GpuSide:
                      self.tables if tables is None else tables, self.lens, self.scale, self.w.bs,
                      max_seq_len=max_seq_len if max_seq_len is not None else int(self.lens_np.max()),
                      k_scale=self.ks, v_scale=self.vs,
-                     partition_tokens=partition_tokens or self.partition_tokens,
+                     partition_tokens=self.partition_tokens if partition_tokens is None else partition_tokens,
                      workspace=None if self.use_workspace else False)
         torch.cuda.synchronize()
         return out

@@ -1,6 +1,7 @@
 """GPU parity at the full workload sizes, in the launch configuration the benchmark times
-(partitions of 512 tokens): the whole cache is compared bit for bit with the oracle's
-write, and sampled requests' outputs with the oracle's attention.  Inputs are drawn on the
+(automatic partitions: one work-group per compute unit), and the long context also in
+partitions of 512 tokens (two merge levels): the whole cache is compared bit for bit with
+the oracle's write, and sampled requests' outputs with the oracle's attention.  Inputs are drawn on the
 device from seeded generators (workloads.device_normal) and copied to the host for the
 oracle."""
 
@@ -31,7 +32,7 @@ def _bits(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def full_case(w, sample_rows):
+def full_case(w, sample_rows, partition_tokens=0):
     T = w.prefill_tokens
     k_pre = workloads.device_normal(w, "k_pre", (T, w.Hkv, w.d))
     v_pre = workloads.device_normal(w, "v_pre", (T, w.Hkv, w.d))
@@ -55,7 +56,7 @@ def full_case(w, sample_rows):
     tab, lens = ga.block_tables(list(range(w.B)), w.max_blocks)
     out = torch.empty_like(q)
     pk.pa_decode(out, q, kc, vc, torch.from_numpy(tab).to(DEV), torch.from_numpy(lens).to(DEV),
-                 1 / math.sqrt(w.d), w.bs, max_seq_len=int(lens.max()), partition_tokens=512)
+                 1 / math.sqrt(w.d), w.bs, max_seq_len=int(lens.max()), partition_tokens=partition_tokens)
     torch.cuda.synchronize()
     # oracle side, from the same stored inputs
     oa = OAlloc(w.num_blocks, w.bs, w.free_order)
@@ -91,5 +92,12 @@ def test_llama_layer_full_sampled():
 
 
 def test_long_context_full():
-    """The 70B-shaped layer at 131072 tokens x 2 requests: 256 partitions merged."""
+    """The 70B-shaped layer at 131072 tokens x 2 requests: 16 partitions of 8192 tokens per
+    request and KV head merged by log-sum-exp."""
     full_case(workloads.long_context(), sample_rows=[0, 1])
+
+
+def test_long_context_full_512():
+    """The same layer in partitions of 512 tokens: 256 partitions per request and KV head,
+    merged in 16 groups of 16 and then across the groups."""
+    full_case(workloads.long_context(), sample_rows=[1], partition_tokens=512)

@@ -30,7 +30,7 @@ def _announce(request):
     yield
 
 
-def run_pair(w, layer=0, partition_tokens=512, rows=None, workspace=True):
+def run_pair(w, layer=0, partition_tokens=0, rows=None, workspace=True):
     vals = workloads.host_values(w, layer)
     g = GpuSide(w, vals, partition_tokens=partition_tokens, workspace=workspace)
     o = OracleSide(w, vals)
@@ -134,7 +134,19 @@ def test_block_dtype_sweep(bs, fmt):
 def test_long_context_scaled():
     """70B-shaped layer (64 q / 8 kv, d 128) at 20000 tokens: 40 partitions of 512 and a
     ragged tail, merged by log-sum-exp."""
-    run_pair(workloads.long_context(B=2, L=20000, seed_index=41, name="long_ctx_20k"))
+    run_pair(workloads.long_context(B=2, L=20000, seed_index=41, name="long_ctx_20k"), partition_tokens=512)
+
+
+def test_long_context_scaled_auto():
+    """The same layer with automatic partitions: 16 (request, KV head) pairs, so each request
+    is cut into 16 equal partitions and merged in one group."""
+    run_pair(workloads.long_context(B=2, L=20000, seed_index=42, name="long_ctx_20k_auto"))
+
+
+def test_auto_partition_uniform_batch():
+    """A batch whose lengths grow past a partition boundary (4101 tokens) with the automatic
+    partition size the benchmark uses: 3 requests x 8 KV heads -> 11 partitions each."""
+    run_pair(workloads.gqa_uniform(B=3, L=4101, layers=1, seed_index=43, name="auto_b3_L4101"))
 
 
 @pytest.mark.parametrize("ptok", [64, 128, 448, 512, 2048])
@@ -228,7 +240,7 @@ def test_shared_prefix_bit_identical_to_private():
     assert np.array_equal(lens, gs.lens_np)
     out = torch.empty_like(gs.q)
     pk.pa_decode(out, gs.q, kc, vc, torch.from_numpy(tab).to(DEV), torch.from_numpy(lens).to(DEV),
-                 gs.scale, w.bs)
+                 gs.scale, w.bs, max_seq_len=int(lens.max()))
     torch.cuda.synchronize()
     assert np.array_equal(out.view(torch.int16).cpu().numpy(), out_shared)
 

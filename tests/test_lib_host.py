@@ -45,7 +45,7 @@ def test_header_symbols_exported():
     out = subprocess.run(["nm", "-D", "--defined-only", pk.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (pa_\w+)", out))
     assert set(names) <= exported
-    assert pk.load().pa_abi_version() == 1
+    assert pk.load().pa_abi_version() == 2
 
 
 def test_errors_are_reported():
@@ -85,12 +85,27 @@ def test_workspace_bytes():
     # 16 requests x 32 heads, 4096 tokens in partitions of 512 -> 8 partitions, 1 group
     rows = 16 * 32 * 8
     want = 16 * 32 * 2 * 4 + rows * 4 + rows * 4 + rows * 128 * 4
-    assert pk.pa_decode_workspace_bytes(16, 32, 128, 4096, 512, 16) == want
-    assert pk.pa_decode_workspace_bytes(4, 8, 64, 200, 512, 16) == 0          # one partition
+    assert pk.pa_decode_workspace_bytes(16, 32, 8, 128, 4096, 512, 16) == want
+    assert pk.pa_decode_workspace_bytes(4, 8, 8, 64, 200, 512, 16) == 0          # one partition
     # 2 requests x 64 heads at 131072 tokens: 256 partitions in 16 groups
     r1, r2 = 2 * 64 * 256, 2 * 64 * 16
     want = 2 * 64 * 17 * 4 + 2 * r1 * 4 + r1 * 128 * 4 + 2 * r2 * 4 + r2 * 128 * 4
-    assert pk.pa_decode_workspace_bytes(2, 64, 128, 131072, 512, 16) == want
+    assert pk.pa_decode_workspace_bytes(2, 64, 8, 128, 131072, 512, 16) == want
+    # automatic partitions (256 compute units when no device can be queried, as on MI355X):
+    # 16 x 8 pairs -> 2 partitions of ceil(4101 / 2) rounded up to 64 tokens
+    assert pk.pa_decode_partition_tokens(16, 8, 4101, 0, 16) == 2112
+    rows = 16 * 32 * 2
+    assert pk.pa_decode_workspace_bytes(16, 32, 8, 128, 4101, 0, 16) == \
+        16 * 32 * 2 * 4 + rows * 4 + rows * 4 + rows * 128 * 4
+    assert pk.pa_decode_partition_tokens(2, 8, 131072, 0, 16) == 8192          # 16 pairs -> 16 partitions
+    assert pk.pa_decode_partition_tokens(256, 8, 8192, 0, 16) == 2048          # >= 256 pairs: 2048
+    assert pk.pa_decode_partition_tokens(256, 8, 8192, 0, 128) == 2048
+    assert pk.pa_decode_partition_tokens(1, 1, 100, 0, 128) == 128             # at least one granule
+    assert pk.pa_decode_partition_tokens(3, 8, 4096, 0, 16) == 384             # 24 pairs -> 11 partitions
+    assert pk.pa_decode_partition_tokens(3, 8, 4096, 500, 16) == 512           # explicit: rounded up to 64
+    assert pk.pa_decode_partition_tokens(3, 8, 4096, 500, 128) == 512
+    with pytest.raises(pk.PagedKVError):
+        pk.pa_decode_partition_tokens(3, 8, 4096, -1, 16)
 
 
 # --------------------------------------------------------------------------- allocator parity
