@@ -16,11 +16,13 @@ Requests grow by one token per step, as in generation.
 
 Reported (one JSON line): `value` = algorithmic bytes of the whole step (every request's
 cached K/V once per KV head, q, out, table entries, lengths; plus the write's rows and
-slots) / wall time per step.  `roofline` = pa_decode (a single kernel launch) measured with
-HIP events around every launch in the timed region on the launch stream.  `cpu_baseline` =
-the float64 oracle timed on a bounded sample of the same per-request work on the host.
+slots) / wall time per step.  `roofline` = pa_decode (a single kernel launch per layer)
+measured with HIP events on the launch stream around each step's 32 back-to-back decode
+launches (the layers' K/V writes are issued first).  `cpu_baseline` = the float64 oracle
+timed on a bounded sample of the same per-request work on the host.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py --workload {ragged_prefix,long_context,sweep}   # other workloads' decode rates
 """
 
 import argparse
@@ -38,7 +40,7 @@ if ROOT not in sys.path:
 
 METRIC = "decode attention KV GB/s and % of HBM peak (GQA 32q/8kv d128, bf16)"
 HBM_PEAK_GBPS = 8000.0
-DECODE_KERNEL = "decode_partial_kernel"
+DECODE_KERNEL = "decode_mfma_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama3_8b_bf16_traffic.md")
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_408_amd", "csrc", "pagedkv.hip")
 
@@ -211,15 +213,14 @@ def run(args):
             pairs = torch.tensor(cow, dtype=torch.int64).to(dev, non_blocking=False)
             for l in range(layers):
                 pk.pa_copy_blocks(kc[l], vc[l], pairs)
-        for l in range(layers):
+        for l in range(layers):          # each layer's new K/V first ...
             wr[l]()
-            if events is not None:
-                e0, e1 = events[l]
-                e0.record()
-                dec[l]()
-                e1.record()
-            else:
-                dec[l]()
+        if events is not None:
+            events[0].record()
+        for l in range(layers):          # ... then the 32 decode launches back to back
+            dec[l]()
+        if events is not None:
+            events[1].record()
         return pin_len[i].numpy().copy()
 
     for i in range(warm):
@@ -227,8 +228,7 @@ def run(args):
     torch.cuda.synchronize()
     log(f"warmup done ({warm} steps); timing {steps} steps")
 
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(layers)]
-           for _ in range(steps)]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     lens_per_step = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -239,7 +239,8 @@ def run(args):
     wall = t1 - t0
     log(f"timed {steps} steps in {wall * 1e3:.2f} ms")
 
-    dec_ms = [e0.elapsed_time(e1) for st in evs for (e0, e1) in st]
+    # HIP events on the launch stream around each step's 32 back-to-back decode launches
+    dec_ms = [e0.elapsed_time(e1) / layers for (e0, e1) in evs for _ in range(layers)]
     dec_bytes = [decode_bytes(L, Hq, Hkv, d, bs, 2, 2) for L in lens_per_step for _ in range(layers)]
     step_bytes = sum(dec_bytes) + steps * layers * kv_write_bytes(B, Hkv, d, 2, 2)
     value = step_bytes / wall / 1e9
@@ -286,16 +287,124 @@ def run(args):
     return result
 
 
+# ----------------------------------------------------------------------------- other workloads
+
+def run_workload(name, args):
+    """One decode step of a non-default workload, timed: the step token's pa_kv_write, then
+    pa_decode, repeated on the same state.  Prints one JSON line per setting (these are
+    measurements for the record, not the benchmark line)."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_408_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    import paged_kv_cache_408_amd as pk
+    import workloads
+
+    dev = torch.device("cuda:0")
+    if name == "ragged_prefix":
+        settings = [workloads.ragged_prefix(bs=16)]
+    elif name == "long_context":
+        settings = [workloads.long_context()]
+    else:  # block-size x KV-dtype sweep on the ragged batch
+        settings = [workloads.ragged_prefix(bs=bs, fmt=fmt) for bs, fmt in workloads.sweep_settings()]
+    for w in settings:
+        alloc = pk.Allocator(w.num_blocks, w.bs, w.free_order)
+        slots = []
+        for op in w.ops:
+            if op[0] == "add":
+                alloc.add(op[1])
+            elif op[0] == "append":
+                slots.append(alloc.append(op[1], op[2])[0])
+            elif op[0] == "fork":
+                alloc.fork(op[1], op[2])
+            elif op[0] == "free":
+                alloc.free(op[1])
+        slots = torch.from_numpy(np.concatenate(slots)).to(dev)
+        cdt = torch.uint8 if w.fmt == "fp8" else torch.bfloat16
+        kc = torch.zeros((w.num_blocks, w.Hkv, w.bs, w.d), dtype=cdt, device=dev)
+        vc = torch.zeros_like(kc)
+        kp = workloads.device_normal(w, "k_pre", (slots.numel(), w.Hkv, w.d))
+        vp = workloads.device_normal(w, "v_pre", (slots.numel(), w.Hkv, w.d))
+        kn = workloads.device_normal(w, "k_new", (w.B, w.Hkv, w.d))
+        vn = workloads.device_normal(w, "v_new", (w.B, w.Hkv, w.d))
+        ks = vs = None
+        if w.fmt == "fp8":   # per-head amax / 448 over the head's values
+            ks = (torch.maximum(kp.float().abs().amax(dim=(0, 2)), kn.float().abs().amax(dim=(0, 2))) / 448).contiguous()
+            vs = (torch.maximum(vp.float().abs().amax(dim=(0, 2)), vn.float().abs().amax(dim=(0, 2))) / 448).contiguous()
+        pk.pa_kv_write(kp, vp, slots, kc, vc, k_scale=ks, v_scale=vs)
+        del kp, vp
+        step_slots, cow = alloc.batch_append(list(range(w.B)), [1] * w.B)
+        assert not cow
+        step_slots = torch.from_numpy(step_slots).to(dev)
+        tab, lens = alloc.block_tables(list(range(w.B)), w.max_blocks)
+        tables, lens_d = torch.from_numpy(tab).to(dev), torch.from_numpy(lens).to(dev)
+        q = workloads.device_normal(w, "q", (w.B, w.Hq, w.d))
+        out = torch.empty_like(q)
+        maxL = int(lens.max())
+        nbytes = pk.pa_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, maxL, args.partition_tokens, w.bs)
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        dec = pk.PreparedDecode(out, q, kc, vc, tables, lens_d, 1.0 / math.sqrt(w.d), w.bs, max_seq_len=maxL,
+                                workspace=ws if nbytes else None, k_scale=ks, v_scale=vs,
+                                partition_tokens=args.partition_tokens)
+        wr = pk.PreparedKVWrite(kn, vn, step_slots, kc, vc, k_scale=ks, v_scale=vs)
+        for _ in range(max(args.warmup, 1)):
+            wr()
+            dec()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for e0, e1 in evs:
+            wr()
+            e0.record()
+            dec()
+            e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        dec_us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+        med = dec_us[len(dec_us) // 2]
+        e = 1 if w.fmt == "fp8" else 2
+        logical = decode_bytes(lens, w.Hq, w.Hkv, w.d, w.bs, e, 2) + (2 * w.Hkv * 4 if w.fmt == "fp8" else 0)
+        st = alloc.stats()
+        unique_kv = st["used_blocks"] * 2 * w.Hkv * w.bs * w.d * e
+        waste = int(sum(-(-int(L) // w.bs) * w.bs - int(L) for L in lens))
+        reserved = int(sum(-(-int(L) // w.bs) * w.bs for L in lens))
+        step_bytes = logical + kv_write_bytes(w.B, w.Hkv, w.d, 2, e)
+        print(json.dumps({
+            "workload": w.name, "metric": "decode attention KV GB/s", "unit": "GB/s",
+            "decode_us_median": round(med, 3), "decode_us_min": round(dec_us[0], 3),
+            "logical_gbps": round(logical / med / 1e3, 1),
+            "unique_kv_gbps": round(unique_kv / med / 1e3, 1),
+            "pct_of_hbm_peak_logical": round(100 * logical / med / 1e3 / HBM_PEAK_GBPS, 2),
+            "step_gbps": round(step_bytes * args.steps / wall / 1e9, 1),
+            "algorithmic_bytes": int(logical), "unique_kv_bytes": int(unique_kv),
+            "batch": w.B, "num_q_heads": w.Hq, "num_kv_heads": w.Hkv, "head_dim": w.d, "block_size": w.bs,
+            "kv_dtype": w.fmt, "max_seq_len": maxL, "total_tokens": int(lens.sum()),
+            "partition_tokens": pk.pa_decode_partition_tokens(w.B, w.Hkv, maxL, args.partition_tokens, w.bs),
+            "final_block_waste_slots": waste, "final_block_waste_pct": round(100 * waste / reserved, 3),
+            "contiguous_waste_pct_at_8192": round(100 * (w.B * 8192 - int(lens.sum())) / (w.B * 8192), 2),
+            "steps": args.steps,
+        }), flush=True)
+        del kc, vc, ws, dec, wr
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--workload", default="llama3_8b", choices=["llama3_8b", "ragged_prefix", "long_context", "sweep"],
+                    help="llama3_8b: the benchmark; the others print per-setting measurements instead")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--partition-tokens", type=int, default=0, help="split-K partition size; 0 = automatic")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="only run pa_copy_blocks over 1 GiB of blocks (for HBM counter calibration)")
+                    help="only run pa_copy_blocks over 1 GiB of blocks (write-counter calibration)")
+    ap.add_argument("--calibrate-read", action="store_true",
+                    help="only run a reduction that reads 1 GiB (read-counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -305,6 +414,12 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.calibrate_read:
+        calibrate_read()
+        return
+    if args.workload != "llama3_8b":
+        run_workload(args.workload, args)
         return
     result = run(args)
     if not args.no_cpu_baseline:
@@ -333,6 +448,18 @@ def calibrate_copy():
     block = Hkv * bs * d * 2
     print(json.dumps({"copy_read_bytes_per_launch": 2 * (N // 2) * block,
                       "copy_write_bytes_per_launch": 2 * (N // 2) * block, "launches": 5}), flush=True)
+
+
+def calibrate_read():
+    """A plain read of known size for scaling the HBM fetch counter: a float32 sum over 1 GiB
+    (read once, a few bytes written), 5 launches."""
+    import torch
+    dev = torch.device("cuda:0")
+    x = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    for _ in range(5):
+        x.sum()
+    torch.cuda.synchronize()
+    print(json.dumps({"read_bytes_per_launch": x.numel() * 4, "launches": 5}), flush=True)
 
 
 if __name__ == "__main__":

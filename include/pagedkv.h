@@ -111,7 +111,7 @@ int pa_kv_write(const void* k, const void* v, const int64_t* slot_mapping, int64
  * automatically (pa_decode_partition_tokens gives the value): with fewer (request, KV head)
  * pairs than the device has compute units, each request is cut into ceil(CUs / pairs) equal
  * partitions of ceil(max_seq_len / parts) tokens (one work-group per compute unit); otherwise
- * partitions are 2048 tokens.  For a given partition size the result depends only on logical
+ * partitions are 512 tokens.  For a given partition size the result depends only on logical
  * positions, so it is bit-identical under any physical placement of the blocks.
  *
  *  out           device, [num_seqs][num_q_heads][head_dim] of q_dtype

@@ -202,6 +202,28 @@ __device__ __forceinline__ U4 ld16_stream(const void* p) {
     }
 }
 
+// Explicitly global (address space 1) and LDS (address space 3) accesses: keep the compiler
+// from falling back to flat instructions, which also count against the LDS wait counter.
+#define PA_GLOBAL __attribute__((address_space(1)))
+#define PA_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ U4 gld16(const void* p) {
+    const u32x4v v = *(const PA_GLOBAL u32x4v*)p;
+    return U4{v[0], v[1], v[2], v[3]};
+}
+__device__ __forceinline__ U4 gld16_stream(const void* p) {
+    const PA_GLOBAL u32x4v* gp = (const PA_GLOBAL u32x4v*)p;
+    const u32x4v v = kNonTemporal ? __builtin_nontemporal_load(gp) : *gp;
+    return U4{v[0], v[1], v[2], v[3]};
+}
+__device__ __forceinline__ int gld_i32(const int32_t* p) { return *(const PA_GLOBAL int32_t*)p; }
+__device__ __forceinline__ float gld_f32(const float* p) { return *(const PA_GLOBAL float*)p; }
+template <typename T>
+__device__ __forceinline__ void gst(T* p, T v) { *(PA_GLOBAL T*)p = v; }
+__device__ __forceinline__ void lds_st16(PA_LDS unsigned char* p, const U4& v) {
+    *(PA_LDS u32x4v*)p = u32x4v{v.x, v.y, v.z, v.w};
+}
+
 __device__ __forceinline__ uint32_t u4_get(const U4& v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
@@ -326,7 +348,7 @@ int device_cu_count() {
 // ceil(max_seq_len / parts) tokens; with at least as many pairs as compute units, long
 // requests are cut into partitions of kAutoRaggedPartition tokens so that no single
 // work-group holds a long tail.
-constexpr int kAutoRaggedPartition = 2048;
+constexpr int kAutoRaggedPartition = 512;
 
 int64_t resolve_partition(int64_t num_seqs, int64_t hkv, int64_t max_seq_len, int requested, int block_size) {
     const int64_t unit = partition_unit(block_size);
@@ -364,6 +386,8 @@ struct DecodeArgs {
     float* ws_l2;
     float* ws_acc2;
     float score_scale;     // scale * log2(e)
+    int list;              // 1: grid walks the compact item list (dynamic LDS: num_seqs + 1 ints)
+    int num_seqs;
     int hkv;
     int64_t num_blocks;
     int max_blocks;
@@ -403,7 +427,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_view(const float* bas
 // partial row per head to (m_dst, l_dst, acc_dst) with the given head stride, by
 // agent-scope stores.
 template <int QDT, int D, int G>
-__device__ void merge_rows(const float* m_src, const float* l_src, const float* acc_src, int64_t row0,
+__device__ __forceinline__ void merge_rows(const float* m_src, const float* l_src, const float* acc_src, int64_t row0,
                            int64_t head_stride, int count, typename Elem<QDT>::T* out, float* m_dst, float* l_dst,
                            float* acc_dst, int64_t dst_head_stride) {
     constexpr int NC = G * D / 4;               // float4 columns
@@ -483,8 +507,104 @@ __device__ void merge_rows(const float* m_src, const float* l_src, const float* 
     }
 }
 
+// End of one partition of one (request, KV head): merges the waves' states held in LDS
+// (m[w][h], l[w][h] and acc[w][h][d] at acc + w * acc_wave_stride; scores in log2 units, acc
+// unnormalised), then writes
+// `out` when the request has a single partition, or the partition's partial row followed by
+// the log-sum-exp merge of the request's partitions by the last work-group to finish, in up
+// to two levels: the last of each group of kMergeGroup partitions merges that group; with
+// more than one group, the last group-merger then merges the groups.  Partials are written
+// with agent-scope stores (coherent across the XCDs' L2s); draining the store counter makes
+// them visible at agent scope before a ticket is taken, and mergers read them with
+// agent-scope loads.  This avoids agent-scope fences, whose L2 write-back/invalidate would
+// serialise the work-groups of an XCD.  Counters are left at zero.  Work-group uniform; ends
+// with a barrier, so the caller may reuse the LDS arrays afterwards.
+template <int QDT, int D, int G>
+__device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int g, int part, int nparts, float vsc, bool any_bad,
+                                 const float* s_m, const float* s_l, const float* s_acc, int acc_wave_stride) {
+    using QT = typename Elem<QDT>::T;
+    __shared__ int s_last;
+    const int hq = a.hkv * G;
+    QT* out = reinterpret_cast<QT*>(a.out) + (int64_t(b) * hq + int64_t(g) * G) * D;
+    const bool single = nparts == 1;
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+        const int h = idx / D, dim = idx - h * D;
+        float M = s_m[h];
+#pragma unroll
+        for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, s_m[ww * G + h]);
+        float num = 0.0f, den = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+            const float f = __builtin_amdgcn_exp2f(s_m[ww * G + h] - M);   // 0 for an idle wave
+            num = fmaf(f, s_acc[ww * acc_wave_stride + h * D + dim], num);
+            den = fmaf(f, s_l[ww * G + h], den);
+        }
+        if (any_bad) {
+            num = __builtin_nanf("");
+            den = __builtin_nanf("");
+            M = __builtin_nanf("");
+        }
+        if (single) {
+            const float o = num / den * vsc;
+            if constexpr (QDT == PA_DTYPE_BF16) gst(out + idx, f32_to_bf16(o)); else gst(out + idx, o);
+        } else {
+            const int64_t row = (int64_t(b) * hq + int64_t(g) * G + h) * a.max_parts + part;
+            store_agent(a.ws_acc + row * D + dim, num * vsc);
+            if (dim == 0) {
+                store_agent(a.ws_m + row, M);
+                store_agent(a.ws_l + row, den);
+            }
+        }
+    }
+    if (single) {
+        __syncthreads();
+        return;
+    }
+    const int ngroups = (nparts + kMergeGroup - 1) / kMergeGroup;
+    const int grp = part / kMergeGroup;
+    const int64_t bg = int64_t(b) * a.hkv + g;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int* ctr = a.ws_ctr + bg * a.max_groups + grp;
+        const int members = min(kMergeGroup, nparts - grp * kMergeGroup);
+        const int ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = ticket == members - 1;
+        if (s_last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    const bool merge1 = s_last;
+    __syncthreads();                 // s_last is rewritten below
+    if (!merge1) return;
+    const int64_t rows1 = (int64_t(b) * hq + int64_t(g) * G) * a.max_parts;    // head h: + h * max_parts
+    const int first = grp * kMergeGroup, count = min(kMergeGroup, nparts - first);
+    if (ngroups == 1) {
+        merge_rows<QDT, D, G>(a.ws_m, a.ws_l, a.ws_acc, rows1 + first, a.max_parts, count, out, nullptr, nullptr,
+                              nullptr, 0);
+        __syncthreads();
+        return;
+    }
+    const int64_t rows2 = (int64_t(b) * hq + int64_t(g) * G) * a.max_groups;
+    merge_rows<QDT, D, G>(a.ws_m, a.ws_l, a.ws_acc, rows1 + first, a.max_parts, count, nullptr, a.ws_m2 + rows2 + grp,
+                          a.ws_l2 + rows2 + grp, a.ws_acc2 + (rows2 + grp) * D, a.max_groups);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int* ctr = a.ws_ctr + int64_t(a.max_groups) * a.hkv * a.num_seqs + bg;
+        const int ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = ticket == ngroups - 1;
+        if (s_last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    const bool merge2 = s_last;
+    __syncthreads();
+    if (!merge2) return;
+    merge_rows<QDT, D, G>(a.ws_m2, a.ws_l2, a.ws_acc2, rows2, a.max_groups, ngroups, out, nullptr, nullptr, nullptr, 0);
+    __syncthreads();
+}
+
 template <int CDT, int QDT, int D, int BS, int G>
-__global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeArgs a) {
     using C = Cfg<CDT, D, BS, G>;
     using CT = typename Elem<CDT>::T;
     using QT = typename Elem<QDT>::T;
@@ -496,10 +616,10 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeAr
     __shared__ float s_m[kWaves][G];
     __shared__ float s_l[kWaves][G];
     __shared__ float s_acc[kWaves][G][D];
-    __shared__ int s_last;
 
     const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, uniform per wave
     const int hq = a.hkv * G;
     const int t0 = part * a.part_tokens;
     const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
@@ -542,7 +662,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeAr
         }
     }
 
-    const int L_raw = a.seq_lens[b];
+    const int L_raw = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
     const bool len_bad = L_raw < 0 || L_raw > a.max_seq_len || L_raw > a.max_blocks * BS;
     const int L = len_bad ? 0 : L_raw;
     const int nparts = L > 0 ? (L + a.part_tokens - 1) / a.part_tokens : 1;
@@ -780,83 +900,398 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeAr
         }
     }
     const bool any_bad = __syncthreads_or(bad);
+    finish_partition<QDT, D, G>(a, b, g, part, nparts, vsc, any_bad, &s_m[0][0], &s_l[0][0], &s_acc[0][0][0],
+                                G * D);
+}
 
-    // ---- merge the waves (fixed order) and write
-    const bool single = nparts == 1;
-    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-        const int h = idx / D, dim = idx - h * D;
-        float M = s_m[0][h];
+// ------------------------------------------------------------------ decode: matrix-core kernel
+//
+// bf16 and fp8 caches.  Passes of 16 tokens per wave, as in decode_valu_kernel, but both
+// contractions run on the matrix cores with the query heads of a KV head padded to 16:
+//  - scores S[token][head] = K_tile[16 x D] . q^T[D x 16] with v_mfma_f32_16x16x32_bf16.  K is
+//    the A operand loaded straight from the cache: lane l holds 8 consecutive dims of token
+//    row l % 16 (fp8 rows are widened to bf16 exactly); q is the B operand, loaded once per
+//    partition with the same dims-to-lanes map.  The result gives lane l the scores of tokens
+//    4 * (l / 16) + i for head l % 16;
+//  - that is exactly the A-operand layout of v_mfma_f32_16x16x16bf16_1k, so the softmax
+//    weights P[head][token] (rounded to bf16) feed out[head][16 dims] += P . V_tile[16 x 16]
+//    directly.  The B operand needs V token-major per dim: each wave writes its V tile to
+//    LDS (16-byte chunks XOR-swizzled by row) and reads it back with ds_read_b64_tr_b16,
+//    which hands lane i of each 16-lane group element i % 4 of the 8 bytes read by lane
+//    4 * e + i / 4 as its element e.
+// Work distribution: with the request lengths' prefix sums in LDS, a grid of about one
+// resident work-group per slot walks a compact list of (request, partition, KV head) items
+// -- first every full partition, then each request's last one -- so no work-group is
+// launched for a partition that does not exist.  Batches too large for the LDS list use a
+// grid over (partition, KV head, request) with early exit instead.
+
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+typedef short i16x4v __attribute__((ext_vector_type(4)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+template <int CDT, int D>
+struct MCfg {
+    static constexpr int E = Elem<CDT>::bytes;          // 2 (bf16) or 1 (fp8)
+    static constexpr int ROWB = D * E;                   // bytes of one cached token row
+    static constexpr int NQK = D / 32;                   // 16x16x32 products per pass (scores)
+    static constexpr int NPV = D / 16;                   // 16x16x16 products per pass (one per 16 dims)
+    static constexpr int KLD = NQK * E / 2;              // 16-byte K loads per lane per pass
+    static constexpr int CPR = ROWB / 16;                // 16-byte chunks per cached row
+    static constexpr int VLD = 16 * CPR / 64;            // 16-byte V loads per lane per pass
+    static constexpr int TROWB = D * 2;                  // bytes per row of the bf16 V tile in LDS
+    static_assert(VLD >= 1 && KLD >= 1, "layout");
+};
+
+constexpr int kMaxListSeqs = 8192;   // batches up to this size use the compact item list
+
+// 16-byte chunk slot of bf16 chunk c in row `row` of an LDS V tile (D / 8 chunks per row).
+template <int D>
+__device__ __forceinline__ int vt_slot(int row, int c) { return c ^ (2 * (row % (D / 16))); }
+
+// Two bf16 values (low halves first) from two exact float32 values that are bf16 numbers.
+__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
+    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+
+// 8 fp8 codes (two dwords) -> 8 bf16 values, exact (every E4M3FN value is a bf16 number).
+__device__ __forceinline__ void e4m3x8_to_bf16(uint32_t w0, uint32_t w1, uint32_t (&o)[4]) {
+    const float2v a = e4m3x2_to_f32<false>(w0), bq = e4m3x2_to_f32<true>(w0);
+    const float2v c = e4m3x2_to_f32<false>(w1), d = e4m3x2_to_f32<true>(w1);
+    o[0] = pack_bf16_exact(a.x, a.y);
+    o[1] = pack_bf16_exact(bq.x, bq.y);
+    o[2] = pack_bf16_exact(c.x, c.y);
+    o[3] = pack_bf16_exact(d.x, d.y);
+}
+
+// float32 -> bf16 bits, round to nearest even (finite, non-negative inputs: softmax weights).
+__device__ __forceinline__ uint32_t weight_to_bf16(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int CDT, int QDT, int D, int BS, int G>
+__global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeArgs a) {
+    using M = MCfg<CDT, D>;
+    using CT = typename Elem<CDT>::T;
+    using QT = typename Elem<QDT>::T;
+    constexpr int TPP = 16;                               // tokens per pass
+    constexpr int BPP = BS < TPP ? TPP / BS : 1;          // blocks touched by one pass (1 or 2)
+    static_assert(QDT == PA_DTYPE_BF16 && (CDT == PA_DTYPE_BF16 || CDT == PA_DTYPE_FP8_E4M3), "bf16 q");
+    static_assert(G <= 16 && BPP <= 2, "shape");
+    static_assert(G * D * 4 <= TPP * M::TROWB, "a wave's merge slice fits in its V tile");
+
+    // per-wave V tile (bf16, swizzled); after a partition's passes the same bytes hold the
+    // wave's accumulator slice acc[G][D] (float) for the merge across waves
+    __shared__ __align__(16) unsigned char s_tile[kWaves][TPP * M::TROWB];
+    __shared__ float s_m[kWaves][G];
+    __shared__ float s_l[kWaves][G];
+    extern __shared__ int s_pref[];                       // compact item list: B + 1 prefix sums
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, uniform per wave
+    const int col = lane & 15, grp4 = lane >> 4;          // MFMA column (head / dim) and row group
+    const int hq = a.hkv * G;
+    const CT* kbase = reinterpret_cast<const CT*>(a.k_cache);
+    const CT* vbase = reinterpret_cast<const CT*>(a.v_cache);
+    const int64_t block_stride = int64_t(a.hkv) * (BS * D);
+    PA_LDS unsigned char* tile = (PA_LDS unsigned char*)&s_tile[w][0];
+
+    auto nparts_of = [&](int L_raw) {
+        const bool bad_len = L_raw < 0 || L_raw > a.max_seq_len || L_raw > a.max_blocks * BS;
+        return (!bad_len && L_raw > 0) ? (L_raw + a.part_tokens - 1) / a.part_tokens : 1;
+    };
+
+    // ---- one partition of one (request, KV head)
+    auto process = [&](int b, int g, int part) {
+        const int t0 = part * a.part_tokens;
+        const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
+
+        // block ids of this wave's passes, 64 at a time (lane j: pass w + kWaves * (k0 + j)),
+        // read before the length is known; `check_entries` flags ids outside the pool inside
+        // the live range and replaces every such id by 0
+        int ent_a = 0, ent_b = 0;
+        auto read_entries = [&](int k0) {
+            const int e = (t0 + (w + kWaves * (k0 + lane)) * TPP) / BS;
+            ent_a = a.max_blocks > 0 ? gld_i32(table + min(e, a.max_blocks - 1)) : -1;
+            if constexpr (BPP == 2) ent_b = a.max_blocks > 0 ? gld_i32(table + min(e + 1, a.max_blocks - 1)) : -1;
+        };
+        read_entries(0);
+
+        // q as the B operand of the score products: head `col` (zero beyond the group), the
+        // dims this lane's K operand holds
+        U4 qb[M::NQK];
+        {
+            const QT* qrow = reinterpret_cast<const QT*>(a.q) + (int64_t(b) * hq + int64_t(g) * G + col) * D;
 #pragma unroll
-        for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, s_m[ww][h]);
-        float num = 0.0f, den = 0.0f;
-#pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) {
-            const float f = __builtin_amdgcn_exp2f(s_m[ww][h] - M);   // 0 for an idle wave
-            num = fmaf(f, s_acc[ww][h][dim], num);
-            den = fmaf(f, s_l[ww][h], den);
-        }
-        if (any_bad) {
-            num = __builtin_nanf("");
-            den = __builtin_nanf("");
-            M = __builtin_nanf("");
-        }
-        if (single) {
-            const float o = num / den * vsc;
-            if constexpr (QDT == PA_DTYPE_BF16) out[idx] = f32_to_bf16(o); else out[idx] = o;
-        } else {
-            // partials go out as agent-scope (coherent) stores, see below
-            const int64_t row = (int64_t(b) * hq + int64_t(g) * G + h) * a.max_parts + part;
-            store_agent(a.ws_acc + row * D + dim, num * vsc);
-            if (dim == 0) {
-                store_agent(a.ws_m + row, M);
-                store_agent(a.ws_l + row, den);
+            for (int j = 0; j < M::NQK; ++j) {
+                const int d0 = M::E == 2 ? 32 * j + 8 * grp4 : 64 * (j >> 1) + 16 * grp4 + 8 * (j & 1);
+                qb[j] = col < G ? gld16(qrow + d0) : U4{0, 0, 0, 0};
             }
         }
-    }
-    if (single) return;
 
-    // ---- log-sum-exp merge of the partitions, in up to two levels: the last work-group
-    // of each group of kMergeGroup partitions to finish merges that group; with more than
-    // one group, the last group-merger then merges the groups.  Partials are written with
-    // agent-scope stores (coherent across the XCDs' L2s); draining the store counter makes
-    // them visible at agent scope before a ticket is taken, and mergers read them with
-    // agent-scope loads.  This avoids agent-scope fences, whose L2 write-back/invalidate
-    // would serialise the work-groups of an XCD.  Counters are left at zero.
-    const int ngroups = (nparts + kMergeGroup - 1) / kMergeGroup;
-    const int grp = part / kMergeGroup;
-    const int64_t bg = int64_t(b) * a.hkv + g;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int* ctr = a.ws_ctr + bg * a.max_groups + grp;
-        const int members = min(kMergeGroup, nparts - grp * kMergeGroup);
-        const int ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = ticket == members - 1;
-        if (s_last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int L_raw = __builtin_amdgcn_readfirstlane(gld_i32(a.seq_lens + b));
+        const bool len_bad = L_raw < 0 || L_raw > a.max_seq_len || L_raw > a.max_blocks * BS;
+        const int L = len_bad ? 0 : L_raw;
+        const int nparts = L > 0 ? (L + a.part_tokens - 1) / a.part_tokens : 1;
+        if (part >= nparts) return;                       // grid mapping only
+        if (L == 0) {   // empty request (zeros) or invalid length (NaN); single partition
+            QT* out = reinterpret_cast<QT*>(a.out) + (int64_t(b) * hq + int64_t(g) * G) * D;
+            const float fill = len_bad ? __builtin_nanf("") : 0.0f;
+            for (int i = threadIdx.x; i < G * D; i += kThreads) gst(out + i, f32_to_bf16(fill));
+            __syncthreads();
+            return;
+        }
+
+        const int t1 = min(L, t0 + a.part_tokens);
+        const int npass = (t1 - t0 + TPP - 1) / TPP;
+        const int nk = npass > w ? (npass - w + kWaves - 1) / kWaves : 0;
+        const int64_t head_tile = int64_t(g) * (BS * D);
+        float sc = a.score_scale;
+        float vsc = 1.0f;
+        if constexpr (CDT == PA_DTYPE_FP8_E4M3) {
+            sc *= __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gld_f32(a.k_scale + g))));
+            vsc = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gld_f32(a.v_scale + g))));
+        }
+
+        bool bad = false;
+        auto check_entries = [&](int k0) {
+            const int kk = k0 + lane;
+            const bool live = kk < nk;
+            if (ent_a < 0 || ent_a >= a.num_blocks) {
+                if (live) bad = true;
+                ent_a = 0;
+            }
+            if constexpr (BPP == 2) {
+                const int e = (t0 + (w + kWaves * kk) * TPP) / BS;
+                if (ent_b < 0 || ent_b >= a.num_blocks) {
+                    if (live && (e + 1) * BS < t1) bad = true;
+                    ent_b = 0;
+                }
+            }
+        };
+        check_entries(0);
+
+        float m_ref = -INFINITY, l_run = 0.0f;            // head `col`
+        f32x4v acc[M::NPV];                               // out[head 4*grp4 + i][16 t + col]
+#pragma unroll
+        for (int t = 0; t < M::NPV; ++t) acc[t] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+
+        // lane byte offsets inside a 16-token tile (loop invariant): K row `col` at 16 * grp4;
+        // V chunk `lane` of each 1 KiB group of chunks
+        const uint32_t k_lane = uint32_t(col) * M::ROWB + 16u * grp4;
+        const uint32_t v_lane = uint32_t(lane / M::CPR) * M::ROWB + 16u * (lane % M::CPR);
+        const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(kbase) + head_tile * M::E;
+        const unsigned char* vbytes = reinterpret_cast<const unsigned char*>(vbase) + head_tile * M::E;
+        const int64_t blk_bytes = block_stride * M::E;
+
+        auto issue = [&](int k, U4 (&kb)[M::KLD], U4 (&vb)[M::VLD]) {
+            if ((k & 63) == 0 && k > 0) {
+                read_entries(k);
+                check_entries(k);
+            }
+            const int tb = t0 + (w + kWaves * k) * TPP;
+            const int b0 = __builtin_amdgcn_readlane(ent_a, k & 63);
+            if constexpr (BPP == 1) {
+                // one block: uniform base + 32-bit lane offset (+ immediate offsets)
+                const uint32_t row0b = uint32_t(tb % BS) * M::ROWB;
+                const unsigned char* kp = kbytes + int64_t(b0) * blk_bytes + row0b;
+                const unsigned char* vp = vbytes + int64_t(b0) * blk_bytes + row0b;
+#pragma unroll
+                for (int j = 0; j < M::KLD; ++j) kb[j] = gld16_stream(kp + (k_lane + 64u * j));
+#pragma unroll
+                for (int r = 0; r < M::VLD; ++r) vb[r] = gld16_stream(vp + (v_lane + 1024u * r));
+            } else {
+                // two blocks of 8 rows: rows 0..7 from the first, 8..15 from the second
+                const int b1 = __builtin_amdgcn_readlane(ent_b, k & 63);
+                const unsigned char* kp = kbytes + int64_t(col >= BS ? b1 : b0) * blk_bytes;
+                const uint32_t krow = k_lane - (col >= BS ? uint32_t(BS) * M::ROWB : 0u);
+#pragma unroll
+                for (int j = 0; j < M::KLD; ++j) kb[j] = gld16_stream(kp + (krow + 64u * j));
+#pragma unroll
+                for (int r = 0; r < M::VLD; ++r) {
+                    const uint32_t off = v_lane + 1024u * r;          // byte offset inside the 16 rows
+                    const bool second = off >= uint32_t(BS) * M::ROWB;
+                    const unsigned char* vp = vbytes + int64_t(second ? b1 : b0) * blk_bytes;
+                    vb[r] = gld16_stream(vp + (off - (second ? uint32_t(BS) * M::ROWB : 0u)));
+                }
+            }
+        };
+
+        auto compute = [&](int k, U4 (&kb)[M::KLD], U4 (&vb)[M::VLD]) {
+            const int tb = t0 + (w + kWaves * k) * TPP;
+            const bool partial = tb + TPP > t1;
+            // V tile -> LDS as bf16 (rows past the end zeroed: they may hold anything)
+#pragma unroll
+            for (int r = 0; r < M::VLD; ++r) {
+                const int ci = 64 * r + lane, vr = ci / M::CPR, c = ci % M::CPR;
+                const uint32_t keep = (partial && tb + vr >= t1) ? 0u : ~0u;
+                const U4 v = U4{vb[r].x & keep, vb[r].y & keep, vb[r].z & keep, vb[r].w & keep};
+                PA_LDS unsigned char* rowp = tile + vr * M::TROWB;
+                if constexpr (M::E == 2) {
+                    lds_st16(rowp + 16 * vt_slot<D>(vr, c), v);
+                } else {
+                    uint32_t lo[4], hi[4];
+                    e4m3x8_to_bf16(v.x, v.y, lo);
+                    e4m3x8_to_bf16(v.z, v.w, hi);
+                    lds_st16(rowp + 16 * vt_slot<D>(vr, 2 * c), U4{lo[0], lo[1], lo[2], lo[3]});
+                    lds_st16(rowp + 16 * vt_slot<D>(vr, 2 * c + 1), U4{hi[0], hi[1], hi[2], hi[3]});
+                }
+            }
+            // scores: S[token][head] over the D dims
+            f32x4v s4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int j = 0; j < M::NQK; ++j) {
+                U4 kv;
+                if constexpr (M::E == 2) {
+                    kv = kb[j];
+                } else {
+                    const U4& src = kb[j >> 1];
+                    uint32_t o[4];
+                    if (j & 1) e4m3x8_to_bf16(src.z, src.w, o); else e4m3x8_to_bf16(src.x, src.y, o);
+                    kv = U4{o[0], o[1], o[2], o[3]};
+                }
+                s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, kv),
+                                                             __builtin_bit_cast(bf16x8v, qb[j]), s4, 0, 0, 0);
+            }
+            float sv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sv[i] = (partial && tb + 4 * grp4 + i >= t1) ? -INFINITY : s4[i] * sc;
+            // online softmax per head (lanes col, col + 16, col + 32, col + 48 share head col);
+            // the state is rescaled only when a score passes the reference by the threshold
+            float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+            mx = pair16_max(pair32_max(mx));
+            if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleThreshold) != 0) {
+                const float m_new = fmaxf(m_ref, mx);
+                const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);   // 0 on the first pass
+                m_ref = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {   // acc rows hold head 4 * grp4 + i: its factor is lane's
+                    const float ai = __int_as_float(
+                        __builtin_amdgcn_ds_bpermute(4 * (4 * grp4 + i), __float_as_int(alpha)));
+#pragma unroll
+                    for (int t = 0; t < M::NPV; ++t) acc[t][i] *= ai;
+                }
+            }
+            uint32_t pw[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pw[i] = weight_to_bf16(__builtin_amdgcn_exp2f(sv[i] - m_ref));
+                l_run += bf16_to_f32(pw[i]);               // the denominator sums the rounded weights
+            }
+            const i16x4v pa = __builtin_bit_cast(i16x4v, make_uint2(pw[0] | (pw[1] << 16), pw[2] | (pw[3] << 16)));
+            // out[head][dims] += P . V, V read back token-major per dim
+            const int vrow = 4 * grp4 + ((lane & 15) >> 2);
+#pragma unroll
+            for (int t = 0; t < M::NPV; ++t) {
+                const int c = 2 * t + ((lane & 3) >> 1);
+                PA_LDS unsigned char* src = tile + vrow * M::TROWB + 16 * vt_slot<D>(vrow, c) + 8 * (lane & 1);
+                const i16x4v vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4v*)src);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vt, acc[t], 0, 0, 0);
+            }
+        };
+
+        {
+            U4 kb[kDepth][M::KLD], vb[kDepth][M::VLD];
+#pragma unroll
+            for (int i = 0; i < kDepth - 1; ++i)
+                if (i < nk) issue(i, kb[i], vb[i]);
+            int k = 0;
+            for (; k + 2 * kDepth - 2 < nk; k += kDepth) {   // every pass issued below exists
+#pragma unroll
+                for (int i = 0; i < kDepth; ++i) {
+                    issue(k + i + kDepth - 1, kb[(i + kDepth - 1) % kDepth], vb[(i + kDepth - 1) % kDepth]);
+                    compute(k + i, kb[i], vb[i]);
+                }
+            }
+            for (; k < nk; k += kDepth) {
+#pragma unroll
+                for (int i = 0; i < kDepth; ++i) {
+                    if (k + i < nk) {
+                        if (k + i + kDepth - 1 < nk)
+                            issue(k + i + kDepth - 1, kb[(i + kDepth - 1) % kDepth], vb[(i + kDepth - 1) % kDepth]);
+                        compute(k + i, kb[i], vb[i]);
+                    }
+                }
+            }
+        }
+
+        // this wave's state -> LDS (the accumulator slice overwrites the wave's own V tile)
+        l_run = pair16_sum(pair32_sum(l_run));
+        PA_LDS float* s_acc_w = (PA_LDS float*)tile;
+        if (grp4 == 0 && col < G) {
+            s_m[w][col] = m_ref;
+            s_l[w][col] = l_run;
+        }
+#pragma unroll
+        for (int t = 0; t < M::NPV; ++t) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int h = 4 * grp4 + i;
+                if (h < G) s_acc_w[h * D + 16 * t + col] = acc[t][i];
+            }
+        }
+        const bool any_bad = __syncthreads_or(bad);
+        finish_partition<QDT, D, G>(a, b, g, part, nparts, vsc, any_bad, &s_m[0][0], &s_l[0][0],
+                                    reinterpret_cast<const float*>(&s_tile[0][0]), int(sizeof(s_tile[0]) / 4));
+    };
+
+    // ---- work items: the compact list (prefix sums of each request's full partitions, all but
+    // its last, in LDS), or one item per work-group of the (partition, KV head, request) grid
+    int F = 0;
+    int64_t total = 1;
+    if (a.list) {
+        const int B = a.num_seqs;
+        const int per = (B + kThreads - 1) / kThreads;
+        const int i0 = min(B, int(threadIdx.x) * per), i1 = min(B, i0 + per);
+        int local = 0;
+        for (int i = i0; i < i1; ++i) local += nparts_of(gld_i32(a.seq_lens + i)) - 1;
+        __shared__ int s_wsum[kWaves];
+        int incl = local;                                 // work-group exclusive scan of `local`
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += y;
+        }
+        if (lane == 63) s_wsum[w] = incl;
+        __syncthreads();
+        int run = incl - local;
+        for (int ww = 0; ww < w; ++ww) run += s_wsum[ww];
+        for (int i = i0; i < i1; ++i) {
+            s_pref[i] = run;
+            run += nparts_of(gld_i32(a.seq_lens + i)) - 1;
+        }
+        if (threadIdx.x == kThreads - 1) s_pref[B] = run;
+        __syncthreads();
+        F = __builtin_amdgcn_readfirstlane(s_pref[B]);
+        total = int64_t(F + B) * a.hkv;
     }
-    __syncthreads();
-    if (!s_last) return;
-    const int64_t rows1 = (int64_t(b) * hq + int64_t(g) * G) * a.max_parts;    // head h: + h * max_parts
-    const int first = grp * kMergeGroup, count = min(kMergeGroup, nparts - first);
-    if (ngroups == 1) {
-        merge_rows<QDT, D, G>(a.ws_m, a.ws_l, a.ws_acc, rows1 + first, a.max_parts, count, out, nullptr, nullptr,
-                              nullptr, 0);
-        return;
+    for (int64_t it = a.list ? blockIdx.x : 0; it < total; it += a.list ? gridDim.x : 1) {
+        int b, g, part;
+        if (a.list) {
+            const int u = static_cast<int>(it / a.hkv);
+            g = static_cast<int>(it % a.hkv);
+            if (u < F) {   // the request whose full partitions cover u
+                int lo = 0, hi = a.num_seqs;
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (s_pref[mid] <= u) lo = mid; else hi = mid;
+                }
+                b = lo;
+                part = u - s_pref[lo];
+            } else {
+                b = u - F;
+                part = nparts_of(gld_i32(a.seq_lens + b)) - 1;
+            }
+        } else {
+            b = blockIdx.z;
+            g = blockIdx.y;
+            part = blockIdx.x;
+        }
+        process(__builtin_amdgcn_readfirstlane(b), __builtin_amdgcn_readfirstlane(g),
+                __builtin_amdgcn_readfirstlane(part));
     }
-    const int64_t rows2 = (int64_t(b) * hq + int64_t(g) * G) * a.max_groups;
-    merge_rows<QDT, D, G>(a.ws_m, a.ws_l, a.ws_acc, rows1 + first, a.max_parts, count, nullptr, a.ws_m2 + rows2 + grp,
-                          a.ws_l2 + rows2 + grp, a.ws_acc2 + (rows2 + grp) * D, a.max_groups);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int* ctr = a.ws_ctr + int64_t(a.max_groups) * gridDim.y * gridDim.z + bg;
-        const int ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = ticket == ngroups - 1;
-        if (s_last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    merge_rows<QDT, D, G>(a.ws_m2, a.ws_l2, a.ws_acc2, rows2, a.max_groups, ngroups, out, nullptr, nullptr, nullptr, 0);
 }
 
 // ------------------------------------------------------------------ workspace clear
@@ -910,10 +1345,43 @@ WsLayout ws_layout(int64_t seqs_x_heads, int64_t parts, int d) {
     return w;
 }
 
+// Resident work-groups per compute unit of a decode kernel at a given dynamic LDS size
+// (cached per kernel instance for the last size asked).
+template <typename K>
+int resident_per_cu(K kernel, int dyn_lds) {
+    static std::atomic<int64_t> cache{-1};
+    const int64_t c = cache.load(std::memory_order_relaxed);
+    if (c >= 0 && int(c >> 32) == dyn_lds) return int(c & 0xffffffff);
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kThreads, dyn_lds) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        n = 1;
+    }
+    cache.store((int64_t(dyn_lds) << 32) | n, std::memory_order_relaxed);
+    return n;
+}
+
 template <int CDT, int QDT, int D, int BS, int G>
-int launch_decode(const DecodeArgs& a, int B, hipStream_t st) {
-    dim3 grid(a.max_parts, a.hkv, B);
-    hipLaunchKernelGGL((decode_partial_kernel<CDT, QDT, D, BS, G>), grid, dim3(kThreads), 0, st, a);
+int launch_decode(DecodeArgs a, int B, hipStream_t st) {
+    if constexpr (CDT == PA_DTYPE_F32) {
+        dim3 grid(a.max_parts, a.hkv, B);
+        hipLaunchKernelGGL((decode_valu_kernel<CDT, QDT, D, BS, G>), grid, dim3(kThreads), 0, st, a);
+    } else {
+        auto kernel = decode_mfma_kernel<CDT, QDT, D, BS, G>;
+        // The (partition, KV head, request) grid is used when all of it is resident at once
+        // (uniform batches: no work-group waits for a slot, none of them is empty); otherwise,
+        // up to kMaxListSeqs requests, the compact item list on about one work-group per slot.
+        const int64_t grid_items = int64_t(B) * a.max_parts * a.hkv;
+        const int lds = (B + 1) * 4;
+        const int64_t slots = B <= kMaxListSeqs ? int64_t(device_cu_count()) * resident_per_cu(kernel, lds) : 0;
+        if (B <= kMaxListSeqs && grid_items > slots) {
+            a.list = 1;
+            hipLaunchKernelGGL(kernel, dim3(static_cast<int>(slots)), dim3(kThreads), lds, st, a);
+        } else {
+            a.list = 0;
+            hipLaunchKernelGGL(kernel, dim3(a.max_parts, a.hkv, B), dim3(kThreads), 0, st, a);
+        }
+    }
     return check_launch("pa_decode");
 }
 
@@ -1062,6 +1530,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     a.k_scale = k_scale;
     a.v_scale = v_scale;
     a.score_scale = scale * kLog2e;
+    a.num_seqs = num_seqs;
     a.hkv = num_kv_heads;
     a.num_blocks = num_blocks;
     a.max_blocks = max_blocks_per_seq;

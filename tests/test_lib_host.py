@@ -98,8 +98,8 @@ def test_workspace_bytes():
     assert pk.pa_decode_workspace_bytes(16, 32, 8, 128, 4101, 0, 16) == \
         16 * 32 * 2 * 4 + rows * 4 + rows * 4 + rows * 128 * 4
     assert pk.pa_decode_partition_tokens(2, 8, 131072, 0, 16) == 8192          # 16 pairs -> 16 partitions
-    assert pk.pa_decode_partition_tokens(256, 8, 8192, 0, 16) == 2048          # >= 256 pairs: 2048
-    assert pk.pa_decode_partition_tokens(256, 8, 8192, 0, 128) == 2048
+    assert pk.pa_decode_partition_tokens(256, 8, 8192, 0, 16) == 512           # >= 256 pairs: 512
+    assert pk.pa_decode_partition_tokens(256, 8, 8192, 0, 128) == 512
     assert pk.pa_decode_partition_tokens(1, 1, 100, 0, 128) == 128             # at least one granule
     assert pk.pa_decode_partition_tokens(3, 8, 4096, 0, 16) == 384             # 24 pairs -> 11 partitions
     assert pk.pa_decode_partition_tokens(3, 8, 4096, 500, 16) == 512           # explicit: rounded up to 64
