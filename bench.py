@@ -65,8 +65,14 @@ def kv_write_bytes(T, Hkv, d, e_in, e_cache):
 
 
 def kernel_source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 (first 16 hex digits) of the kernel source with comments and whitespace removed,
+    so that edits to comments alone do not mark the counters as stale."""
+    with open(KERNEL_SOURCE) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = re.sub(r"\s+", "", text)
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def measured_traffic():
@@ -384,7 +390,8 @@ def run_workload(name, args):
             "kv_dtype": w.fmt, "max_seq_len": maxL, "total_tokens": int(lens.sum()),
             "partition_tokens": pk.pa_decode_partition_tokens(w.B, w.Hkv, maxL, args.partition_tokens, w.bs),
             "final_block_waste_slots": waste, "final_block_waste_pct": round(100 * waste / reserved, 3),
-            "contiguous_waste_pct_at_8192": round(100 * (w.B * 8192 - int(lens.sum())) / (w.B * 8192), 2),
+            "contiguous_waste_pct": round(100 * (w.B * max(8192, maxL) - int(lens.sum())) / (w.B * max(8192, maxL)), 2),
+            "contiguous_reservation_tokens": max(8192, maxL),
             "steps": args.steps,
         }), flush=True)
         del kc, vc, ws, dec, wr

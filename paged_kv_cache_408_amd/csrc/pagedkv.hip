@@ -12,27 +12,21 @@
 // Kernels
 //  kv_write_kernel       one lane per 8 elements of a (token, head) row; bit copy or fp8
 //                        quantisation; slots < 0 or beyond the pool are skipped.
-//  decode_partial_kernel one work-group (4 wave64) per (partition, KV head, request).  The
-//                        G = Hq/Hkv query heads of a KV head share every K/V load, so each
-//                        cached byte is read once.  A wave takes every 4th pass of TPP
-//                        tokens; its block ids sit one per lane in a register (v_readlane
-//                        per pass), and the loads of the next pass are in flight while the
-//                        current one is computed.  Per pass:
-//                          K phase: KL lanes per token row, each lane a few 16-byte loads of
-//                            that row (every group of 4 lanes reads 64 contiguous bytes);
-//                            partial dot products with the lane's slice of q (v_dot2 on
-//                            bf16 pairs), summed across the KL lanes with DPP;
-//                          online softmax against a reference maximum that is only raised
-//                            (with a rescale) when a score passes it by 2^8 -- one ballot
-//                            per pass; p = exp2(s - m) (scores carry scale * log2(e));
-//                          V phase: one 16-byte vector of a row per lane, consecutive lanes
-//                            covering consecutive bytes (1 KiB per wave load); p is handed
-//                            from the K-phase lanes through LDS; acc[h][dims] += p * v.
-//                        The 4 waves' states are merged in LDS; a single-partition request
-//                        writes `out`, otherwise (m, l, acc) goes to the workspace.
-//                        With several partitions, the last work-group of a (request, KV
-//                        head) to finish merges them by log-sum-exp (ticket counter in the
-//                        workspace, agent-scope release/acquire), so one launch does both.
+//  decode_mfma_kernel    bf16 and fp8 caches: one work-group (4 wave64) per (partition, KV
+//                        head, request) work item; scores and P.V on the matrix cores with the
+//                        query heads of a KV head padded to 16 (see its own comment).  Uniform
+//                        batches use a (partition, KV head, request) grid; ragged ones a compact
+//                        work-item list walked by about one work-group per resident slot.
+//  decode_valu_kernel    f32 caches: the same passes with the contractions on the vector ALU
+//                        (lanes per token row for q.k with DPP sums; one 16-byte vector per
+//                        lane for P.V; weights handed over through LDS).
+//  Both: the G = Hq/Hkv query heads of a KV head share every K/V load (each cached byte is
+//  read once, non-temporally); a wave takes every 4th pass of 16 tokens with the next pass's
+//  loads in flight; the online softmax rescales only when a score passes its reference by
+//  2^8; the waves' states are merged in LDS; a single-partition request writes `out`,
+//  otherwise the partition's (m, l, acc) goes to the workspace and the last work-group of the
+//  (request, KV head) merges the partitions by log-sum-exp in the same launch (ticket
+//  counters, agent-scope stores and loads).
 //  zero_kernel           clears a workspace (a plain store kernel, no memset node).
 //  copy_blocks_kernel    whole-block copies for copy-on-write.
 //
