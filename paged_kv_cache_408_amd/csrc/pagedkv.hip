@@ -22,7 +22,7 @@
 //                        lane for P.V; weights handed over through LDS).
 //  Both: the G = Hq/Hkv query heads of a KV head share every K/V load (each cached byte is
 //  read once, non-temporally); a wave takes every 4th pass of 16 tokens with the next pass's
-//  loads in flight; the online softmax rescales only when a score passes its reference by
+//  loads in flight (bf16: in an LDS ring filled by DMA loads); the online softmax rescales only when a score passes its reference by
 //  2^8; the waves' states are merged in LDS; a single-partition request writes `out`,
 //  otherwise the partition's (m, l, acc) goes to the workspace and the last work-group of the
 //  (request, KV head) merges the partitions by log-sum-exp in the same launch (ticket
@@ -57,10 +57,21 @@ namespace {
 #ifndef PA_DECODE_NT
 #define PA_DECODE_NT 1
 #endif
+#ifndef PA_DECODE_STAGES
+#define PA_DECODE_STAGES 2     // bf16 decode: 0 = K/V through registers; n >= 2 = n-stage LDS ring
+                               // (2 keeps two work-groups per compute unit at D = 128)
+#endif
+#ifndef PA_DECODE_STAGES_FP8
+#define PA_DECODE_STAGES_FP8 0 // the same for fp8 caches
+#endif
 constexpr int kWaves = PA_DECODE_WAVES;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kDepth = PA_DECODE_DEPTH;
 constexpr bool kNonTemporal = PA_DECODE_NT != 0;
+constexpr int kStagesBf16 = PA_DECODE_STAGES;
+constexpr int kStagesFp8 = PA_DECODE_STAGES_FP8;
+static_assert(kStagesBf16 == 0 || (kStagesBf16 >= 2 && kStagesBf16 <= 6), "LDS ring of 2 to 6 stages");
+static_assert(kStagesFp8 == 0 || (kStagesFp8 >= 2 && kStagesFp8 <= 6), "LDS ring of 2 to 6 stages");
 static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves per work-group");
 static_assert(kDepth >= 2 && kDepth <= 4, "2 to 4 passes in flight");
 constexpr float kLog2e = 1.4426950408889634f;
@@ -217,6 +228,28 @@ __device__ __forceinline__ void gst(T* p, T v) { *(PA_GLOBAL T*)p = v; }
 __device__ __forceinline__ void lds_st16(PA_LDS unsigned char* p, const U4& v) {
     *(PA_LDS u32x4v*)p = u32x4v{v.x, v.y, v.z, v.w};
 }
+__device__ __forceinline__ U4 lds_ld16(const PA_LDS unsigned char* p) {
+    const u32x4v v = *(const PA_LDS u32x4v*)p;
+    return U4{v[0], v[1], v[2], v[3]};
+}
+__device__ __forceinline__ uint32_t lds_addr(const PA_LDS unsigned char* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// Global -> LDS without registers: every lane's 16 bytes at sbase + voff (non-temporal) land at
+// LDS byte address m0 + 16 * lane.  Issued from inline assembly so that the compiler, which
+// cannot tell the ring's stages apart, does not drain every load before each LDS read; the
+// waits are placed by hand (wait_vmem).  Each use is preceded by the LDS reads of the stage it
+// overwrites having completed (lgkmcnt(0)).
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t m0) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\tglobal_load_lds_dwordx4 %0, %1 nt" :: "v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
+}
+// the same with a 64-bit address per lane
+__device__ __forceinline__ void dma16_lane(const void* addr, uint32_t m0) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\tglobal_load_lds_dwordx4 %0, off nt" :: "v"(addr), "{m0}"(m0) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
 
 __device__ __forceinline__ uint32_t u4_get(const U4& v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
@@ -913,6 +946,14 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeArgs 
 //    LDS (16-byte chunks XOR-swizzled by row) and reads it back with ds_read_b64_tr_b16,
 //    which hands lane i of each 16-lane group element i % 4 of the 8 bytes read by lane
 //    4 * e + i / 4 as its element e.
+// Where K/V travel (chosen per cache type at build time):
+//  - bf16: an LDS ring of kStagesBf16 stages per wave filled by global_load_lds_dwordx4 (HBM
+//    straight to LDS, no registers held for loads in flight).  The DMA places each row's
+//    16-byte chunks XOR-swizzled by row, so K is read back as the A operand and V through
+//    the transpose reads from the stage itself, with no copy;
+//  - fp8: two passes in registers (K converted there; V converted while written to the
+//    bf16 LDS tile).  An fp8 ring would need that copy out of the stage as an extra LDS
+//    round trip per pass, which measured slower.
 // Work distribution: with the request lengths' prefix sums in LDS, a grid of about one
 // resident work-group per slot walks a compact list of (request, partition, KV head) items
 // -- first every full partition, then each request's last one -- so no work-group is
@@ -942,19 +983,13 @@ constexpr int kMaxListSeqs = 8192;   // batches up to this size use the compact 
 template <int D>
 __device__ __forceinline__ int vt_slot(int row, int c) { return c ^ (2 * (row % (D / 16))); }
 
-// Two bf16 values (low halves first) from two exact float32 values that are bf16 numbers.
-__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
-    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
-}
-
 // 8 fp8 codes (two dwords) -> 8 bf16 values, exact (every E4M3FN value is a bf16 number).
 __device__ __forceinline__ void e4m3x8_to_bf16(uint32_t w0, uint32_t w1, uint32_t (&o)[4]) {
-    const float2v a = e4m3x2_to_f32<false>(w0), bq = e4m3x2_to_f32<true>(w0);
-    const float2v c = e4m3x2_to_f32<false>(w1), d = e4m3x2_to_f32<true>(w1);
-    o[0] = pack_bf16_exact(a.x, a.y);
-    o[1] = pack_bf16_exact(bq.x, bq.y);
-    o[2] = pack_bf16_exact(c.x, c.y);
-    o[3] = pack_bf16_exact(d.x, d.y);
+    // gfx950's scaled pair conversion with a scale of 1: one instruction per two values
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w0), 1.0f, false));
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w0), 1.0f, true));
+    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w1), 1.0f, false));
+    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w1), 1.0f, true));
 }
 
 // float32 -> bf16 bits, round to nearest even (finite, non-negative inputs: softmax weights).
@@ -972,11 +1007,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
     constexpr int BPP = BS < TPP ? TPP / BS : 1;          // blocks touched by one pass (1 or 2)
     static_assert(QDT == PA_DTYPE_BF16 && (CDT == PA_DTYPE_BF16 || CDT == PA_DTYPE_FP8_E4M3), "bf16 q");
     static_assert(G <= 16 && BPP <= 2, "shape");
-    static_assert(G * D * 4 <= TPP * M::TROWB, "a wave's merge slice fits in its V tile");
+    constexpr int KT = TPP * M::ROWB;                     // bytes of one cached K (or V) tile
+    constexpr int VTB = TPP * M::TROWB;                   // bytes of one bf16 V tile
+    // LDS per wave: the V tile (registers path) or the ring of K/V stages plus, for fp8, the
+    // bf16 V tile the transpose reads use
+    constexpr int kStages = M::E == 2 ? kStagesBf16 : kStagesFp8;
+    constexpr int WAVE_LDS = kStages > 0 ? kStages * 2 * KT + (M::E == 1 ? VTB : 0) : VTB;
+    static_assert(G * D * 4 <= WAVE_LDS, "a wave's merge slice fits in its LDS");
 
     // per-wave V tile (bf16, swizzled); after a partition's passes the same bytes hold the
     // wave's accumulator slice acc[G][D] (float) for the merge across waves
-    __shared__ __align__(16) unsigned char s_tile[kWaves][TPP * M::TROWB];
+    __shared__ __align__(16) unsigned char s_tile[kWaves][WAVE_LDS];
     __shared__ float s_m[kWaves][G];
     __shared__ float s_l[kWaves][G];
     extern __shared__ int s_pref[];                       // compact item list: B + 1 prefix sums
@@ -1078,68 +1119,238 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
         const unsigned char* vbytes = reinterpret_cast<const unsigned char*>(vbase) + head_tile * M::E;
         const int64_t blk_bytes = block_stride * M::E;
 
-        auto issue = [&](int k, U4 (&kb)[M::KLD], U4 (&vb)[M::VLD]) {
-            if ((k & 63) == 0 && k > 0) {
+        if constexpr (kStages == 0) {
+            auto issue = [&](int k, U4 (&kb)[M::KLD], U4 (&vb)[M::VLD]) {
+                if ((k & 63) == 0 && k > 0) {
+                    read_entries(k);
+                    check_entries(k);
+                }
+                const int tb = t0 + (w + kWaves * k) * TPP;
+                const int b0 = __builtin_amdgcn_readlane(ent_a, k & 63);
+                if constexpr (BPP == 1) {
+                    // one block: uniform base + 32-bit lane offset (+ immediate offsets)
+                    const uint32_t row0b = uint32_t(tb % BS) * M::ROWB;
+                    const unsigned char* kp = kbytes + int64_t(b0) * blk_bytes + row0b;
+                    const unsigned char* vp = vbytes + int64_t(b0) * blk_bytes + row0b;
+    #pragma unroll
+                    for (int j = 0; j < M::KLD; ++j) kb[j] = gld16_stream(kp + (k_lane + 64u * j));
+    #pragma unroll
+                    for (int r = 0; r < M::VLD; ++r) vb[r] = gld16_stream(vp + (v_lane + 1024u * r));
+                } else {
+                    // two blocks of 8 rows: rows 0..7 from the first, 8..15 from the second
+                    const int b1 = __builtin_amdgcn_readlane(ent_b, k & 63);
+                    const unsigned char* kp = kbytes + int64_t(col >= BS ? b1 : b0) * blk_bytes;
+                    const uint32_t krow = k_lane - (col >= BS ? uint32_t(BS) * M::ROWB : 0u);
+    #pragma unroll
+                    for (int j = 0; j < M::KLD; ++j) kb[j] = gld16_stream(kp + (krow + 64u * j));
+    #pragma unroll
+                    for (int r = 0; r < M::VLD; ++r) {
+                        const uint32_t off = v_lane + 1024u * r;          // byte offset inside the 16 rows
+                        const bool second = off >= uint32_t(BS) * M::ROWB;
+                        const unsigned char* vp = vbytes + int64_t(second ? b1 : b0) * blk_bytes;
+                        vb[r] = gld16_stream(vp + (off - (second ? uint32_t(BS) * M::ROWB : 0u)));
+                    }
+                }
+            };
+
+            auto compute = [&](int k, U4 (&kb)[M::KLD], U4 (&vb)[M::VLD]) {
+                const int tb = t0 + (w + kWaves * k) * TPP;
+                const bool partial = tb + TPP > t1;
+                // V tile -> LDS as bf16 (rows past the end zeroed: they may hold anything)
+    #pragma unroll
+                for (int r = 0; r < M::VLD; ++r) {
+                    const int ci = 64 * r + lane, vr = ci / M::CPR, c = ci % M::CPR;
+                    const uint32_t keep = (partial && tb + vr >= t1) ? 0u : ~0u;
+                    const U4 v = U4{vb[r].x & keep, vb[r].y & keep, vb[r].z & keep, vb[r].w & keep};
+                    PA_LDS unsigned char* rowp = tile + vr * M::TROWB;
+                    if constexpr (M::E == 2) {
+                        lds_st16(rowp + 16 * vt_slot<D>(vr, c), v);
+                    } else {
+                        uint32_t lo[4], hi[4];
+                        e4m3x8_to_bf16(v.x, v.y, lo);
+                        e4m3x8_to_bf16(v.z, v.w, hi);
+                        lds_st16(rowp + 16 * vt_slot<D>(vr, 2 * c), U4{lo[0], lo[1], lo[2], lo[3]});
+                        lds_st16(rowp + 16 * vt_slot<D>(vr, 2 * c + 1), U4{hi[0], hi[1], hi[2], hi[3]});
+                    }
+                }
+                // scores: S[token][head] over the D dims
+                f32x4v s4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    #pragma unroll
+                for (int j = 0; j < M::NQK; ++j) {
+                    U4 kv;
+                    if constexpr (M::E == 2) {
+                        kv = kb[j];
+                    } else {
+                        const U4& src = kb[j >> 1];
+                        uint32_t o[4];
+                        if (j & 1) e4m3x8_to_bf16(src.z, src.w, o); else e4m3x8_to_bf16(src.x, src.y, o);
+                        kv = U4{o[0], o[1], o[2], o[3]};
+                    }
+                    s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, kv),
+                                                                 __builtin_bit_cast(bf16x8v, qb[j]), s4, 0, 0, 0);
+                }
+                float sv[4];
+    #pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sv[i] = (partial && tb + 4 * grp4 + i >= t1) ? -INFINITY : s4[i] * sc;
+                // online softmax per head (lanes col, col + 16, col + 32, col + 48 share head col);
+                // the state is rescaled only when a score passes the reference by the threshold
+                float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+                mx = pair16_max(pair32_max(mx));
+                if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleThreshold) != 0) {
+                    const float m_new = fmaxf(m_ref, mx);
+                    const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);   // 0 on the first pass
+                    m_ref = m_new;
+                    l_run *= alpha;
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {   // acc rows hold head 4 * grp4 + i: its factor is lane's
+                        const float ai = __int_as_float(
+                            __builtin_amdgcn_ds_bpermute(4 * (4 * grp4 + i), __float_as_int(alpha)));
+    #pragma unroll
+                        for (int t = 0; t < M::NPV; ++t) acc[t][i] *= ai;
+                    }
+                }
+                uint32_t pw[4];
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pw[i] = weight_to_bf16(__builtin_amdgcn_exp2f(sv[i] - m_ref));
+                    l_run += bf16_to_f32(pw[i]);               // the denominator sums the rounded weights
+                }
+                const i16x4v pa = __builtin_bit_cast(i16x4v, make_uint2(pw[0] | (pw[1] << 16), pw[2] | (pw[3] << 16)));
+                // out[head][dims] += P . V, V read back token-major per dim
+                const int vrow = 4 * grp4 + ((lane & 15) >> 2);
+    #pragma unroll
+                for (int t = 0; t < M::NPV; ++t) {
+                    const int c = 2 * t + ((lane & 3) >> 1);
+                    PA_LDS unsigned char* src = tile + vrow * M::TROWB + 16 * vt_slot<D>(vrow, c) + 8 * (lane & 1);
+                    const i16x4v vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4v*)src);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vt, acc[t], 0, 0, 0);
+                }
+            };
+
+            {
+                U4 kb[kDepth][M::KLD], vb[kDepth][M::VLD];
+    #pragma unroll
+                for (int i = 0; i < kDepth - 1; ++i)
+                    if (i < nk) issue(i, kb[i], vb[i]);
+                int k = 0;
+                for (; k + 2 * kDepth - 2 < nk; k += kDepth) {   // every pass issued below exists
+    #pragma unroll
+                    for (int i = 0; i < kDepth; ++i) {
+                        issue(k + i + kDepth - 1, kb[(i + kDepth - 1) % kDepth], vb[(i + kDepth - 1) % kDepth]);
+                        compute(k + i, kb[i], vb[i]);
+                    }
+                }
+                for (; k < nk; k += kDepth) {
+    #pragma unroll
+                    for (int i = 0; i < kDepth; ++i) {
+                        if (k + i < nk) {
+                            if (k + i + kDepth - 1 < nk)
+                                issue(k + i + kDepth - 1, kb[(i + kDepth - 1) % kDepth], vb[(i + kDepth - 1) % kDepth]);
+                            compute(k + i, kb[i], vb[i]);
+                        }
+                    }
+                }
+            }
+        } else {
+        // ---- K/V through an LDS ring of kStages stages per wave, filled by DMA loads.
+        // A tile's 16-byte chunk position p (row p / CPR) holds data chunk (p % CPR) ^ (row % CPR)
+        // of its row, so that the K reads (16 rows at one chunk) and the V transpose reads spread
+        // over the banks.  Lane `lane` of DMA instruction i fills position 64 i + lane.
+        constexpr int CPR = M::CPR;
+        constexpr int NI = KT / 1024;                     // DMA instructions per tile
+        constexpr int NIP = 2 * NI;                       // per pass (K and V)
+        constexpr int RPI = 64 / CPR;                     // rows per DMA instruction
+        static_assert(KT % 1024 == 0 && NI >= 1, "tile of whole KiB");
+        uint32_t src_off[NI];                             // source byte offset inside the 16 rows
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int pos = 64 * i + lane, row = pos / CPR, slot = pos % CPR;
+            src_off[i] = uint32_t(row) * M::ROWB + 16u * uint32_t(slot ^ (row % CPR));
+        }
+        PA_LDS unsigned char* ring = tile;                // stage s: K at ring + 2 s KT, V at + KT
+        PA_LDS unsigned char* vtile = tile + kStages * 2 * KT;   // fp8: bf16 V tile
+        auto stage_k = [&](int st) { return ring + st * (2 * KT); };
+
+        auto issue_dma = [&](int k, int st) {
+            if ((k & 63) == 0 && k > 0) {   // next 64 passes' block ids (the compiler's wait drains the ring)
                 read_entries(k);
                 check_entries(k);
             }
             const int tb = t0 + (w + kWaves * k) * TPP;
             const int b0 = __builtin_amdgcn_readlane(ent_a, k & 63);
+            PA_LDS unsigned char* dk = stage_k(st);
+            PA_LDS unsigned char* dv = dk + KT;
             if constexpr (BPP == 1) {
-                // one block: uniform base + 32-bit lane offset (+ immediate offsets)
                 const uint32_t row0b = uint32_t(tb % BS) * M::ROWB;
                 const unsigned char* kp = kbytes + int64_t(b0) * blk_bytes + row0b;
                 const unsigned char* vp = vbytes + int64_t(b0) * blk_bytes + row0b;
 #pragma unroll
-                for (int j = 0; j < M::KLD; ++j) kb[j] = gld16_stream(kp + (k_lane + 64u * j));
+                for (int i = 0; i < NI; ++i) dma16(kp, src_off[i], lds_addr(dk + 1024 * i));
 #pragma unroll
-                for (int r = 0; r < M::VLD; ++r) vb[r] = gld16_stream(vp + (v_lane + 1024u * r));
-            } else {
-                // two blocks of 8 rows: rows 0..7 from the first, 8..15 from the second
+                for (int i = 0; i < NI; ++i) dma16(vp, src_off[i], lds_addr(dv + 1024 * i));
+            } else {   // rows 0..7 from the first block, 8..15 from the second
                 const int b1 = __builtin_amdgcn_readlane(ent_b, k & 63);
-                const unsigned char* kp = kbytes + int64_t(col >= BS ? b1 : b0) * blk_bytes;
-                const uint32_t krow = k_lane - (col >= BS ? uint32_t(BS) * M::ROWB : 0u);
 #pragma unroll
-                for (int j = 0; j < M::KLD; ++j) kb[j] = gld16_stream(kp + (krow + 64u * j));
-#pragma unroll
-                for (int r = 0; r < M::VLD; ++r) {
-                    const uint32_t off = v_lane + 1024u * r;          // byte offset inside the 16 rows
-                    const bool second = off >= uint32_t(BS) * M::ROWB;
-                    const unsigned char* vp = vbytes + int64_t(second ? b1 : b0) * blk_bytes;
-                    vb[r] = gld16_stream(vp + (off - (second ? uint32_t(BS) * M::ROWB : 0u)));
+                for (int i = 0; i < NI; ++i) {
+                    if constexpr (RPI <= BS) {   // every row of instruction i in one block
+                        const bool second = i * RPI >= BS;
+                        const uint32_t off = src_off[i] - (second ? uint32_t(BS) * M::ROWB : 0u);
+                        dma16(kbytes + int64_t(second ? b1 : b0) * blk_bytes, off, lds_addr(dk + 1024 * i));
+                        dma16(vbytes + int64_t(second ? b1 : b0) * blk_bytes, off, lds_addr(dv + 1024 * i));
+                    } else {
+                        const int row = (64 * i + lane) / CPR;
+                        const bool second = row >= BS;
+                        const uint32_t off = src_off[i] - (second ? uint32_t(BS) * M::ROWB : 0u);
+                        dma16_lane(kbytes + int64_t(second ? b1 : b0) * blk_bytes + off, lds_addr(dk + 1024 * i));
+                        dma16_lane(vbytes + int64_t(second ? b1 : b0) * blk_bytes + off, lds_addr(dv + 1024 * i));
+                    }
                 }
             }
         };
 
-        auto compute = [&](int k, U4 (&kb)[M::KLD], U4 (&vb)[M::VLD]) {
+        auto compute_dma = [&](int k, int st) {
             const int tb = t0 + (w + kWaves * k) * TPP;
             const bool partial = tb + TPP > t1;
-            // V tile -> LDS as bf16 (rows past the end zeroed: they may hold anything)
+            PA_LDS unsigned char* dk = stage_k(st);
+            PA_LDS unsigned char* dv = dk + KT;
+            // V as a bf16 tile the transpose reads understand (rows past the end zeroed)
+            PA_LDS unsigned char* vt;
+            if constexpr (M::E == 2) {
+                vt = dv;
+                if (partial) {
 #pragma unroll
-            for (int r = 0; r < M::VLD; ++r) {
-                const int ci = 64 * r + lane, vr = ci / M::CPR, c = ci % M::CPR;
-                const uint32_t keep = (partial && tb + vr >= t1) ? 0u : ~0u;
-                const U4 v = U4{vb[r].x & keep, vb[r].y & keep, vb[r].z & keep, vb[r].w & keep};
-                PA_LDS unsigned char* rowp = tile + vr * M::TROWB;
-                if constexpr (M::E == 2) {
-                    lds_st16(rowp + 16 * vt_slot<D>(vr, c), v);
-                } else {
+                    for (int i = 0; i < NI; ++i) {
+                        const int pos = 64 * i + lane;
+                        if (tb + pos / CPR >= t1) lds_st16(dv + 16 * pos, U4{0, 0, 0, 0});
+                    }
+                }
+            } else {
+                vt = vtile;
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    const int pos = 64 * i + lane, row = pos / CPR, c = (pos % CPR) ^ (row % CPR);
+                    const uint32_t keep = (partial && tb + row >= t1) ? 0u : ~0u;
+                    U4 v = lds_ld16(dv + 16 * pos);
+                    v = U4{v.x & keep, v.y & keep, v.z & keep, v.w & keep};
                     uint32_t lo[4], hi[4];
                     e4m3x8_to_bf16(v.x, v.y, lo);
                     e4m3x8_to_bf16(v.z, v.w, hi);
-                    lds_st16(rowp + 16 * vt_slot<D>(vr, 2 * c), U4{lo[0], lo[1], lo[2], lo[3]});
-                    lds_st16(rowp + 16 * vt_slot<D>(vr, 2 * c + 1), U4{hi[0], hi[1], hi[2], hi[3]});
+                    PA_LDS unsigned char* rowp = vtile + row * M::TROWB;
+                    lds_st16(rowp + 16 * ((2 * c) ^ (row % (D / 8))), U4{lo[0], lo[1], lo[2], lo[3]});
+                    lds_st16(rowp + 16 * ((2 * c + 1) ^ (row % (D / 8))), U4{hi[0], hi[1], hi[2], hi[3]});
                 }
             }
-            // scores: S[token][head] over the D dims
+            // scores: K rows as the A operand read from the stage
             f32x4v s4 = {0.0f, 0.0f, 0.0f, 0.0f};
+            const PA_LDS unsigned char* krow = dk + col * M::ROWB;
 #pragma unroll
             for (int j = 0; j < M::NQK; ++j) {
                 U4 kv;
                 if constexpr (M::E == 2) {
-                    kv = kb[j];
+                    kv = lds_ld16(krow + 16 * ((4 * j + grp4) ^ (col % CPR)));
                 } else {
-                    const U4& src = kb[j >> 1];
+                    const U4 src = lds_ld16(krow + 16 * ((4 * (j >> 1) + grp4) ^ (col % CPR)));
                     uint32_t o[4];
                     if (j & 1) e4m3x8_to_bf16(src.z, src.w, o); else e4m3x8_to_bf16(src.x, src.y, o);
                     kv = U4{o[0], o[1], o[2], o[3]};
@@ -1151,8 +1362,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 sv[i] = (partial && tb + 4 * grp4 + i >= t1) ? -INFINITY : s4[i] * sc;
-            // online softmax per head (lanes col, col + 16, col + 32, col + 48 share head col);
-            // the state is rescaled only when a score passes the reference by the threshold
             float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
             mx = pair16_max(pair32_max(mx));
             if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleThreshold) != 0) {
@@ -1161,7 +1370,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
                 m_ref = m_new;
                 l_run *= alpha;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {   // acc rows hold head 4 * grp4 + i: its factor is lane's
+                for (int i = 0; i < 4; ++i) {
                     const float ai = __int_as_float(
                         __builtin_amdgcn_ds_bpermute(4 * (4 * grp4 + i), __float_as_int(alpha)));
 #pragma unroll
@@ -1172,44 +1381,39 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 pw[i] = weight_to_bf16(__builtin_amdgcn_exp2f(sv[i] - m_ref));
-                l_run += bf16_to_f32(pw[i]);               // the denominator sums the rounded weights
+                l_run += bf16_to_f32(pw[i]);
             }
             const i16x4v pa = __builtin_bit_cast(i16x4v, make_uint2(pw[0] | (pw[1] << 16), pw[2] | (pw[3] << 16)));
-            // out[head][dims] += P . V, V read back token-major per dim
             const int vrow = 4 * grp4 + ((lane & 15) >> 2);
 #pragma unroll
             for (int t = 0; t < M::NPV; ++t) {
                 const int c = 2 * t + ((lane & 3) >> 1);
-                PA_LDS unsigned char* src = tile + vrow * M::TROWB + 16 * vt_slot<D>(vrow, c) + 8 * (lane & 1);
-                const i16x4v vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4v*)src);
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vt, acc[t], 0, 0, 0);
+                PA_LDS unsigned char* src = vt + vrow * M::TROWB + 16 * (c ^ (vrow % (D / 8))) + 8 * (lane & 1);
+                const i16x4v vtr = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4v*)src);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vtr, acc[t], 0, 0, 0);
             }
         };
 
-        {
-            U4 kb[kDepth][M::KLD], vb[kDepth][M::VLD];
+        // the compiler's own loads (q, table, length) complete before the ring starts
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-            for (int i = 0; i < kDepth - 1; ++i)
-                if (i < nk) issue(i, kb[i], vb[i]);
-            int k = 0;
-            for (; k + 2 * kDepth - 2 < nk; k += kDepth) {   // every pass issued below exists
-#pragma unroll
-                for (int i = 0; i < kDepth; ++i) {
-                    issue(k + i + kDepth - 1, kb[(i + kDepth - 1) % kDepth], vb[(i + kDepth - 1) % kDepth]);
-                    compute(k + i, kb[i], vb[i]);
-                }
-            }
-            for (; k < nk; k += kDepth) {
-#pragma unroll
-                for (int i = 0; i < kDepth; ++i) {
-                    if (k + i < nk) {
-                        if (k + i + kDepth - 1 < nk)
-                            issue(k + i + kDepth - 1, kb[(i + kDepth - 1) % kDepth], vb[(i + kDepth - 1) % kDepth]);
-                        compute(k + i, kb[i], vb[i]);
-                    }
-                }
-            }
+        for (int i = 0; i < kStages - 1; ++i)
+            if (i < nk) issue_dma(i, i);
+        int k = 0;
+        int st = 0;                                       // stage of pass k
+        for (; k + kStages - 1 < nk; ++k) {               // pass k + kStages - 1 exists
+            const int st_new = st == 0 ? kStages - 1 : st - 1;   // (k + kStages - 1) % kStages
+            issue_dma(k + kStages - 1, st_new);
+            wait_vmem<(kStages - 1) * NIP>();             // all but the newest kStages - 1 passes landed
+            compute_dma(k, st);
+            st = st + 1 == kStages ? 0 : st + 1;
         }
+        for (; k < nk; ++k) {                             // the last passes: drain
+            wait_vmem<0>();
+            compute_dma(k, st);
+            st = st + 1 == kStages ? 0 : st + 1;
+        }
+        }   // kStages
 
         // this wave's state -> LDS (the accumulator slice overwrites the wave's own V tile)
         l_run = pair16_sum(pair32_sum(l_run));
