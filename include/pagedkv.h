@@ -189,18 +189,26 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst, int32_t
  *  - free(seq) drops one reference of each of its blocks in logical order; blocks reaching
  *    zero join the free queue tail in that order;
  *  - any operation that cannot be completed (PA_ERR_NO_BLOCKS, unknown or duplicate ids)
- *    changes nothing; PA_ERR_NO_BLOCKS also counts one exhaustion event ("Conclusion":
- *    blocks can run out mid-generation; preemption is the caller's decision).
+ *    changes nothing; PA_ERR_NO_BLOCKS from an append or a swap-in also counts one
+ *    exhaustion event ("Conclusion": blocks can run out mid-generation; preemption is the
+ *    caller's decision);
+ *  - preemption by swapping ("Conclusion": a preempted request's KV cache is recomputed or
+ *    swapped): a second pool of host blocks, with its own FIFO queue (identity order) and
+ *    refcounts, holds the blocks of swapped-out sequences (pa_swap_out / pa_swap_in below).
+ *    A swapped-out sequence can only be swapped in, freed or queried.
  */
 typedef struct pa_allocator pa_allocator;
 
 typedef struct {
     int64_t free_blocks;        /* blocks in the free queue                              */
     int64_t used_blocks;        /* blocks with refcount > 0                              */
-    int64_t total_refs;         /* sum of refcounts = total block-table entries          */
-    int64_t exhaustion_events;  /* appends refused with PA_ERR_NO_BLOCKS                 */
-    int64_t waste_slots;        /* sum over sequences of ceil(n/bs)*bs - n               */
-    int64_t num_seqs;           /* live sequences                                        */
+    int64_t total_refs;         /* sum of refcounts = resident sequences' table entries  */
+    int64_t exhaustion_events;  /* appends and swap-ins refused with PA_ERR_NO_BLOCKS    */
+    int64_t waste_slots;        /* sum over resident sequences of ceil(n/bs)*bs - n      */
+    int64_t num_seqs;           /* live sequences (resident and swapped out)             */
+    int64_t host_free_blocks;   /* host pool: blocks in its free queue                   */
+    int64_t host_used_blocks;   /* host pool: blocks with refcount > 0                   */
+    int64_t swapped_seqs;       /* sequences whose blocks are in the host pool           */
 } pa_alloc_stats_t;
 
 /* num_blocks > 0, block_size > 0; initial_free_order: host int32 [num_blocks], a
@@ -237,6 +245,61 @@ int pa_alloc_stats(const pa_allocator* a, pa_alloc_stats_t* out);
  * of a buffer of num_blocks). */
 int pa_alloc_dump(const pa_allocator* a, int32_t* refcounts, int32_t* free_order,
                   int32_t* n_free);
+
+/* ---------------------------------------------------------------- preemption by swapping
+ *
+ * "PagedAttention: Optimizing KV Cache Utilization in Large Language Models", "Conclusion":
+ * when blocks run out mid-generation, requests are preempted and their KV cache is
+ * recomputed or swapped.  Swapping here moves whole blocks between the device pool and a
+ * pool of the same block shape in pinned host memory, bit for bit, so a request resumes
+ * with exactly the cache it had (and, decode being independent of block placement, exactly
+ * the outputs it would have had).
+ *
+ * (Re)creates the host pool with num_host_blocks blocks (ids 0..num_host_blocks-1, free
+ * queue in identity order).  PA_ERR_INVALID while any sequence is swapped out. */
+int pa_alloc_set_host_blocks(pa_allocator* a, int32_t num_host_blocks);
+
+/* Swap out the n_seqs listed sequences (distinct, resident).  Their blocks are walked in
+ * list order, each in logical order; every distinct device block gets one host block from
+ * the host queue head and the pair (device id, host id) is written to pairs_out (host int64
+ * [max_pairs][2]) in that order; each reference moves to the host block, and the device
+ * reference is dropped as pa_seq_free would (blocks reaching 0 join the device queue tail).
+ * A block also held by a resident sequence stays allocated for it and is copied.  The caller
+ * copies the pairs with pa_swap_blocks (device pool -> host pool) on the stream that later
+ * writes the freed blocks, before those writes.  PA_ERR_NO_BLOCKS if the host queue holds
+ * fewer blocks than the distinct blocks; PA_ERR_INVALID if they exceed max_pairs. */
+int pa_swap_out(pa_allocator* a, const int64_t* seq_ids, int32_t n_seqs, int64_t* pairs_out,
+                int32_t max_pairs, int32_t* n_pairs_out);
+
+/* Swap the listed sequences (distinct, swapped out) back in: the mirror image of
+ * pa_swap_out, with pairs (host id, device id), device blocks from the device queue head and
+ * host blocks reaching 0 joining the host queue tail.  The caller copies the pairs with
+ * pa_swap_blocks (host pool -> device pool) before the sequences' next decode.
+ * PA_ERR_NO_BLOCKS (one exhaustion event) if the device queue is too short. */
+int pa_swap_in(pa_allocator* a, const int64_t* seq_ids, int32_t n_seqs, int64_t* pairs_out,
+               int32_t max_pairs, int32_t* n_pairs_out);
+
+/* 1 if the sequence is swapped out, 0 if resident, negative status if unknown. */
+int pa_seq_is_swapped(const pa_allocator* a, int64_t seq_id);
+
+/* Host pool state: refcounts [num_host_blocks], free queue in order (*n_free entries). */
+int pa_alloc_dump_host(const pa_allocator* a, int32_t* refcounts, int32_t* free_order,
+                       int32_t* n_free);
+
+/* Whole-block copies between two pools of the same block shape, either of which may be
+ * device memory or pinned host memory (allocated by HIP, e.g. hipHostMalloc): for each pair
+ * i with both ids in range,
+ *     dst_k[src_dst[2i+1]] = src_k[src_dst[2i]]   (all heads, rows and dims), same for v.
+ * The copy is one kernel on `stream` that reads and writes host memory directly over the
+ * host link (no staging).  Every pointer (the four pools over their whole extent and
+ * src_dst over 2 * num_pairs entries) is checked before the launch to lie inside one HIP
+ * allocation, device or pinned host; pageable host memory gives PA_ERR_INVALID.
+ *  src_dst  device or pinned host int64 [num_pairs][2]; destinations pairwise distinct;
+ *           pairs with an id outside [0, src_num_blocks) / [0, dst_num_blocks) are skipped. */
+int pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                   const int64_t* src_dst, int32_t num_pairs, int64_t src_num_blocks,
+                   int64_t dst_num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t block_size, int32_t cache_dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -30,6 +30,24 @@ Readings where the pages are silent (the plainest ones the rest supports):
   join the free queue tail in that order.
 * A multi-token append is all-or-nothing: if the free queue cannot cover it, nothing
   changes and the exhaustion counter is incremented.
+
+Preemption by swapping ("PagedAttention: ...", "Conclusion": requests that run out of
+blocks are preempted and their KV cache recomputed or swapped).  The pages name swapping
+only; the reading taken here:
+
+* Swapped-out blocks go to a second pool of host blocks, with its own FIFO free queue
+  (identity order) and refcounts.
+* Swapping out a set of sequences gives every distinct device block they hold one host
+  block (the pair is reported so the caller copies the block), in the order the blocks are
+  met walking the sequences in the given order, each in logical order.  Every reference of
+  the set moves to the host block, and the device references are dropped exactly as a
+  release drops them.  Swapping in is the same with the pools exchanged.
+* A block that a sequence outside the set also holds is copied and stays with that holder,
+  so the two stop sharing it.
+* A swapped-out sequence cannot be appended to, forked or listed in a block table; it can
+  be swapped in or released (releasing its host blocks).
+* A swap is all-or-nothing; a swap-in refused for lack of device blocks counts as an
+  exhaustion event, a swap-out refused for lack of host blocks does not.
 """
 
 from __future__ import annotations
@@ -48,8 +66,9 @@ class InvalidOp(Exception):
 
 @dataclass
 class _Seq:
-    blocks: list = field(default_factory=list)
+    blocks: list = field(default_factory=list)   # device ids, or host ids while swapped
     n: int = 0
+    swapped: bool = False
 
 
 class Allocator:
@@ -65,6 +84,15 @@ class Allocator:
         self.refcount = [0] * num_blocks
         self.seqs: dict[int, _Seq] = {}
         self.exhaustion_events = 0
+        self.host_free = deque()
+        self.host_refcount = []
+
+    def _resident(self, seq_id: int) -> _Seq:
+        if seq_id not in self.seqs:
+            raise InvalidOp(f"unknown sequence {seq_id}")
+        if self.seqs[seq_id].swapped:
+            raise InvalidOp(f"sequence {seq_id} is swapped out")
+        return self.seqs[seq_id]
 
     # -- operations -------------------------------------------------------------------
     def add(self, seq_id: int) -> None:
@@ -84,11 +112,9 @@ class Allocator:
 
     def append(self, seq_id: int, n_tokens: int):
         """Append n_tokens to a sequence.  Returns (slots, cow_pairs)."""
-        if seq_id not in self.seqs:
-            raise InvalidOp(f"unknown sequence {seq_id}")
+        s = self._resident(seq_id)
         if n_tokens < 0:
             raise InvalidOp("negative token count")
-        s = self.seqs[seq_id]
         if self._blocks_needed(s, n_tokens) > len(self.free):
             self.exhaustion_events += 1
             raise NoBlocks(f"sequence {seq_id}: not enough free blocks")
@@ -116,6 +142,10 @@ class Allocator:
         import copy
         if len(set(seq_ids)) != len(seq_ids):
             raise InvalidOp("a sequence is listed twice")
+        for s, n in zip(seq_ids, n_tokens):             # bad arguments before exhaustion
+            self._resident(s)
+            if n < 0:
+                raise InvalidOp("negative token count")
         trial = copy.deepcopy(self)
         slots, cow = [], []
         try:
@@ -130,11 +160,9 @@ class Allocator:
         return slots, cow
 
     def fork(self, parent: int, child: int) -> None:
-        if parent not in self.seqs:
-            raise InvalidOp(f"unknown sequence {parent}")
+        p = self._resident(parent)
         if child in self.seqs:
             raise InvalidOp(f"sequence {child} already exists")
-        p = self.seqs[parent]
         for b in p.blocks:
             self.refcount[b] += 1
         self.seqs[child] = _Seq(blocks=list(p.blocks), n=p.n)
@@ -143,19 +171,79 @@ class Allocator:
         if seq_id not in self.seqs:
             raise InvalidOp(f"unknown sequence {seq_id}")
         s = self.seqs.pop(seq_id)
+        refcount, free = (self.host_refcount, self.host_free) if s.swapped else (self.refcount, self.free)
         for b in s.blocks:
-            self.refcount[b] -= 1
-            if self.refcount[b] == 0:
-                self.free.append(b)
+            refcount[b] -= 1
+            if refcount[b] == 0:
+                free.append(b)
+
+    # -- preemption by swapping ---------------------------------------------------------
+    def set_host_blocks(self, num_host_blocks: int) -> None:
+        if num_host_blocks < 0:
+            raise InvalidOp("negative host pool size")
+        if any(s.swapped for s in self.seqs.values()):
+            raise InvalidOp("sequences are swapped out")
+        self.host_free = deque(range(num_host_blocks))
+        self.host_refcount = [0] * num_host_blocks
+
+    def _swap(self, seq_ids, to_host: bool):
+        if len(set(seq_ids)) != len(seq_ids):
+            raise InvalidOp("a sequence is listed twice")
+        for sid in seq_ids:
+            if sid not in self.seqs:
+                raise InvalidOp(f"unknown sequence {sid}")
+            if self.seqs[sid].swapped == to_host:
+                raise InvalidOp(f"sequence {sid} is in the wrong state for this swap")
+        if to_host:
+            src_ref, src_free, dst_ref, dst_free = self.refcount, self.free, self.host_refcount, self.host_free
+        else:
+            src_ref, src_free, dst_ref, dst_free = self.host_refcount, self.host_free, self.refcount, self.free
+        distinct = {b for sid in seq_ids for b in self.seqs[sid].blocks}
+        if len(distinct) > len(dst_free):
+            if not to_host:
+                self.exhaustion_events += 1
+            raise NoBlocks("not enough free blocks in the destination pool")
+        moved = {}
+        pairs = []
+        for sid in seq_ids:
+            s = self.seqs[sid]
+            new_blocks = []
+            for b in s.blocks:
+                if b not in moved:
+                    moved[b] = dst_free.popleft()
+                    pairs.append((b, moved[b]))
+                dst_ref[moved[b]] += 1
+                src_ref[b] -= 1
+                if src_ref[b] == 0:
+                    src_free.append(b)
+                new_blocks.append(moved[b])
+            s.blocks = new_blocks
+            s.swapped = to_host
+        return pairs
+
+    def swap_out(self, seq_ids):
+        """Moves the sequences to the host pool.  Returns the (device, host) block pairs."""
+        return self._swap(list(seq_ids), True)
+
+    def swap_in(self, seq_ids):
+        """Moves the sequences back to the device pool.  Returns the (host, device) pairs."""
+        return self._swap(list(seq_ids), False)
+
+    def is_swapped(self, seq_id: int) -> bool:
+        if seq_id not in self.seqs:
+            raise InvalidOp(f"unknown sequence {seq_id}")
+        return self.seqs[seq_id].swapped
+
+    def dump_host(self):
+        """(host refcounts, host free queue in order)."""
+        return list(self.host_refcount), list(self.host_free)
 
     # -- views ------------------------------------------------------------------------
     def block_table(self, seq_ids, max_blocks: int):
         """Rows of physical block ids padded with -1, and the token counts."""
         tables, lens = [], []
         for sid in seq_ids:
-            if sid not in self.seqs:
-                raise InvalidOp(f"unknown sequence {sid}")
-            s = self.seqs[sid]
+            s = self._resident(sid)
             if len(s.blocks) > max_blocks:
                 raise InvalidOp(f"sequence {sid} holds {len(s.blocks)} blocks > {max_blocks}")
             tables.append(list(s.blocks) + [-1] * (max_blocks - len(s.blocks)))
@@ -167,13 +255,17 @@ class Allocator:
         used = sum(1 for r in self.refcount if r > 0)
         waste = 0
         for s in self.seqs.values():
-            waste += -(-s.n // bs) * bs - s.n            # final-block waste per holder
+            if not s.swapped:
+                waste += -(-s.n // bs) * bs - s.n        # final-block waste per resident holder
         return {
             "free": len(self.free),
             "used": used,
             "refs": sum(self.refcount),
             "exhaustion_events": self.exhaustion_events,
             "waste_slots": waste,
+            "host_free": len(self.host_free),
+            "host_used": sum(1 for r in self.host_refcount if r > 0),
+            "swapped_seqs": sum(1 for s in self.seqs.values() if s.swapped),
         }
 
     def dump(self):

@@ -24,7 +24,8 @@ EXPORTED = [
     "pa_decode_partition_tokens", "pa_decode_workspace_init", "pa_decode",
     "pa_copy_blocks", "pa_alloc_create", "pa_alloc_destroy", "pa_seq_add", "pa_seq_append",
     "pa_batch_append", "pa_seq_fork", "pa_seq_free", "pa_block_tables", "pa_alloc_stats",
-    "pa_alloc_dump",
+    "pa_alloc_dump", "pa_alloc_set_host_blocks", "pa_swap_out", "pa_swap_in", "pa_seq_is_swapped",
+    "pa_alloc_dump_host", "pa_swap_blocks",
 ]
 
 
@@ -44,7 +45,8 @@ class UnsupportedError(PagedKVError):
 
 class pa_alloc_stats_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in
-                ("free_blocks", "used_blocks", "total_refs", "exhaustion_events", "waste_slots", "num_seqs")]
+                ("free_blocks", "used_blocks", "total_refs", "exhaustion_events", "waste_slots", "num_seqs",
+                 "host_free_blocks", "host_used_blocks", "swapped_seqs")]
 
 
 _lib = None
@@ -80,6 +82,12 @@ def load(path: str = LIB_PATH):
         "pa_block_tables": (ctypes.c_int, [P, P, I32, I32, P, P]),
         "pa_alloc_stats": (ctypes.c_int, [P, ctypes.POINTER(pa_alloc_stats_t)]),
         "pa_alloc_dump": (ctypes.c_int, [P, P, P, P]),
+        "pa_alloc_set_host_blocks": (ctypes.c_int, [P, I32]),
+        "pa_swap_out": (ctypes.c_int, [P, P, I32, P, I32, P]),
+        "pa_swap_in": (ctypes.c_int, [P, P, I32, P, I32, P]),
+        "pa_seq_is_swapped": (ctypes.c_int, [P, I64]),
+        "pa_alloc_dump_host": (ctypes.c_int, [P, P, P, P]),
+        "pa_swap_blocks": (ctypes.c_int, [P, P, P, P, P, I32, I64, I64, I32, I32, I32, I32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -257,6 +265,34 @@ def pa_copy_blocks(k_cache, v_cache, src_dst, *, stream=None):
     _check(rc)
 
 
+def _dev_or_pinned(t, what):
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{what} must be a device tensor or a pinned host tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def pa_swap_blocks(dst_k, dst_v, src_k, src_v, src_dst, *, stream=None):
+    """Copy whole blocks src_k[s] -> dst_k[d] (and v) for each row (s, d) of src_dst (int64
+    [n, 2]); each pool is a device tensor or a pinned host tensor of the cache layout."""
+    torch = _torch()
+    Ns, Hkv, bs, d = src_k.shape
+    Nd = dst_k.shape[0]
+    for t, n in ((dst_k, "dst_k"), (dst_v, "dst_v"), (src_v, "src_v")):
+        if t.shape[1:] != src_k.shape[1:] or t.dtype != src_k.dtype:
+            raise ValueError(f"{n} does not match src_k's block shape and dtype")
+    if dst_v.shape[0] != Nd or src_v.shape[0] != Ns:
+        raise ValueError("k and v pools differ in block count")
+    if src_dst.dtype != torch.int64 or src_dst.dim() != 2 or src_dst.shape[1] != 2:
+        raise ValueError("src_dst must be int64 [n, 2]")
+    rc = load().pa_swap_blocks(_dev_or_pinned(dst_k, "dst_k"), _dev_or_pinned(dst_v, "dst_v"),
+                               _dev_or_pinned(src_k, "src_k"), _dev_or_pinned(src_v, "src_v"),
+                               _dev_or_pinned(src_dst, "src_dst"), src_dst.shape[0], Ns, Nd, Hkv, d, bs,
+                               _dtype_code(src_k, "src_k"), _stream(stream))
+    _check(rc)
+
+
 # --------------------------------------------------------------------------- host allocator
 
 def _p(a: np.ndarray):
@@ -331,6 +367,43 @@ def pa_alloc_dump(h, num_blocks):
     return ref, free[: int(nf[0])]
 
 
+def pa_alloc_set_host_blocks(h, num_host_blocks):
+    _check(load().pa_alloc_set_host_blocks(h, num_host_blocks))
+
+
+def _swap(fn, h, seq_ids, max_pairs):
+    ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+    pairs = np.empty((max(max_pairs, 1), 2), dtype=np.int64)
+    n = np.zeros(1, dtype=np.int32)
+    _check(fn(h, _p(ids), len(ids), _p(pairs), max_pairs, _p(n)))
+    return pairs[: int(n[0])].copy()
+
+
+def pa_swap_out(h, seq_ids, max_pairs):
+    """Returns the (device block, host block) pairs to copy, int64 [n, 2]."""
+    return _swap(load().pa_swap_out, h, seq_ids, max_pairs)
+
+
+def pa_swap_in(h, seq_ids, max_pairs):
+    """Returns the (host block, device block) pairs to copy, int64 [n, 2]."""
+    return _swap(load().pa_swap_in, h, seq_ids, max_pairs)
+
+
+def pa_seq_is_swapped(h, seq_id) -> bool:
+    rc = load().pa_seq_is_swapped(h, seq_id)
+    if rc < 0:
+        _check(rc)
+    return rc == 1
+
+
+def pa_alloc_dump_host(h, num_host_blocks):
+    ref = np.empty(max(num_host_blocks, 1), dtype=np.int32)
+    free = np.empty(max(num_host_blocks, 1), dtype=np.int32)
+    nf = np.zeros(1, dtype=np.int32)
+    _check(load().pa_alloc_dump_host(h, _p(ref), _p(free), _p(nf)))
+    return ref[:num_host_blocks], free[: int(nf[0])]
+
+
 class Allocator:
     """Owning wrapper of a pa_allocator handle (host only)."""
 
@@ -366,6 +439,22 @@ class Allocator:
 
     def dump(self):
         return pa_alloc_dump(self._h, self.num_blocks)
+
+    def set_host_blocks(self, num_host_blocks):
+        pa_alloc_set_host_blocks(self._h, num_host_blocks)
+        self.num_host_blocks = int(num_host_blocks)
+
+    def swap_out(self, seq_ids):   # at most one pair per device block
+        return pa_swap_out(self._h, seq_ids, self.num_blocks)
+
+    def swap_in(self, seq_ids):    # at most one pair per host block
+        return pa_swap_in(self._h, seq_ids, getattr(self, "num_host_blocks", 0))
+
+    def is_swapped(self, seq_id):
+        return pa_seq_is_swapped(self._h, seq_id)
+
+    def dump_host(self):
+        return pa_alloc_dump_host(self._h, getattr(self, "num_host_blocks", 0))
 
 
 def blocks_for(seq_lens, block_size) -> int:

@@ -10,7 +10,15 @@
 //  - fork shares every block of the parent (reference count + 1);
 //  - appending into a shared, partially filled last block first moves the sequence to a
 //    fresh block (copy-on-write) and reports the pair for the device copy;
-//  - every operation is all-or-nothing: on failure no state changes.
+//  - every operation is all-or-nothing: on failure no state changes;
+//  - preemption by swapping ("PagedAttention: Optimizing KV Cache Utilization in Large
+//    Language Models", "Conclusion": a request may be preempted and its KV cache swapped):
+//    a second pool of host blocks (its own FIFO queue and refcounts) receives the blocks of
+//    swapped-out sequences.  Swap-out walks the listed sequences' blocks in logical order,
+//    gives each distinct device block one host block (pair reported for the copy), moves every
+//    reference to the host block and releases the device references as a free would; swap-in
+//    is the mirror image.  A device block also held by a sequence that stays resident keeps
+//    that holder and is copied, so the swapped set and the resident one stop sharing it.
 //
 // Storage: refcounts and the free queue are flat int32 arrays of num_blocks entries (the
 // queue is a ring: it never holds more than num_blocks ids); each sequence keeps its block
@@ -31,8 +39,31 @@ using pagedkv::fail;
 namespace {
 
 struct Seq {
-    std::vector<int32_t> blocks;
-    int64_t n = 0;  // tokens held
+    std::vector<int32_t> blocks;  // device block ids, or host block ids while swapped out
+    int64_t n = 0;                // tokens held
+    bool swapped = false;
+};
+
+// A FIFO queue of free block ids over a ring of capacity `cap` (it never holds more).
+struct FreeQueue {
+    std::vector<int32_t> ring;
+    int64_t head = 0, count = 0;
+    void reset(int32_t cap) {
+        ring.resize(cap);
+        for (int32_t i = 0; i < cap; ++i) ring[i] = i;
+        head = 0;
+        count = cap;
+    }
+    int32_t pop() {
+        const int32_t b = ring[head];
+        head = (head + 1) % static_cast<int64_t>(ring.size());
+        --count;
+        return b;
+    }
+    void push(int32_t b) {
+        ring[(head + count) % static_cast<int64_t>(ring.size())] = b;
+        ++count;
+    }
 };
 
 }  // namespace
@@ -46,6 +77,9 @@ struct pa_allocator {
     int64_t count = 0;           // ids in the queue
     std::unordered_map<int64_t, Seq> seqs;
     int64_t exhaustion_events = 0;
+    std::vector<int32_t> host_refcount;   // host pool (empty until pa_alloc_set_host_blocks)
+    FreeQueue host_free;
+    int64_t swapped_seqs = 0;
 
     int32_t pop() {
         int32_t b = ring[head];
@@ -154,6 +188,7 @@ int pa_seq_append(pa_allocator* a, int64_t seq_id, int32_t n_tokens, int64_t* sl
     auto it = a->seqs.find(seq_id);
     if (it == a->seqs.end()) return fail(PA_ERR_INVALID, "pa_seq_append: unknown sequence %lld", (long long)seq_id);
     Seq& s = it->second;
+    if (s.swapped) return fail(PA_ERR_INVALID, "pa_seq_append: sequence %lld is swapped out", (long long)seq_id);
     int64_t need = a->blocks_needed(s, n_tokens, 0);
     if (need > a->count) {
         a->exhaustion_events += 1;
@@ -187,6 +222,8 @@ int pa_batch_append(pa_allocator* a, const int64_t* seq_ids, const int32_t* n_to
         if (!ids.emplace(seq_ids[i], 1).second)
             return fail(PA_ERR_INVALID, "pa_batch_append: sequence %lld listed twice", (long long)seq_ids[i]);
         Seq& s = it->second;
+        if (s.swapped)
+            return fail(PA_ERR_INVALID, "pa_batch_append: sequence %lld is swapped out", (long long)seq_ids[i]);
         ss[i] = &s;
         int32_t drop = 0;
         if (n_tokens[i] > 0 && s.n % a->block_size != 0) {
@@ -217,6 +254,7 @@ int pa_seq_fork(pa_allocator* a, int64_t parent, int64_t child) {
     auto it = a->seqs.find(parent);
     if (it == a->seqs.end()) return fail(PA_ERR_INVALID, "pa_seq_fork: unknown parent %lld", (long long)parent);
     if (a->seqs.count(child)) return fail(PA_ERR_INVALID, "pa_seq_fork: child %lld exists", (long long)child);
+    if (it->second.swapped) return fail(PA_ERR_INVALID, "pa_seq_fork: parent %lld is swapped out", (long long)parent);
     Seq c = it->second;  // copy of the block list and token count
     for (int32_t b : c.blocks) a->refcount[b] += 1;
     a->seqs.emplace(child, std::move(c));
@@ -228,8 +266,13 @@ int pa_seq_free(pa_allocator* a, int64_t seq_id) {
     if (!a) return fail(PA_ERR_INVALID, "pa_seq_free: NULL allocator");
     auto it = a->seqs.find(seq_id);
     if (it == a->seqs.end()) return fail(PA_ERR_INVALID, "pa_seq_free: unknown sequence %lld", (long long)seq_id);
-    for (int32_t b : it->second.blocks) {
-        if (--a->refcount[b] == 0) a->push(b);
+    if (it->second.swapped) {   // its references are host blocks
+        for (int32_t b : it->second.blocks)
+            if (--a->host_refcount[b] == 0) a->host_free.push(b);
+        a->swapped_seqs -= 1;
+    } else {
+        for (int32_t b : it->second.blocks)
+            if (--a->refcount[b] == 0) a->push(b);
     }
     a->seqs.erase(it);
     return PA_OK;
@@ -250,6 +293,8 @@ int pa_block_tables(const pa_allocator* a, const int64_t* seq_ids, int32_t n_seq
         if ((int64_t)it->second.blocks.size() > max_blocks)
             return fail(PA_ERR_INVALID, "pa_block_tables: sequence %lld holds %zu blocks > max_blocks %d",
                         (long long)seq_ids[i], it->second.blocks.size(), max_blocks);
+        if (it->second.swapped)
+            return fail(PA_ERR_INVALID, "pa_block_tables: sequence %lld is swapped out", (long long)seq_ids[i]);
         if (it->second.n > INT32_MAX)
             return fail(PA_ERR_INVALID, "pa_block_tables: sequence %lld length exceeds int32", (long long)seq_ids[i]);
         ss[i] = &it->second;
@@ -274,13 +319,19 @@ int pa_alloc_stats(const pa_allocator* a, pa_alloc_stats_t* out) {
     }
     int64_t waste = 0;
     const int64_t bs = a->block_size;
-    for (const auto& kv : a->seqs) waste += (kv.second.n + bs - 1) / bs * bs - kv.second.n;
+    for (const auto& kv : a->seqs)
+        if (!kv.second.swapped) waste += (kv.second.n + bs - 1) / bs * bs - kv.second.n;
     out->free_blocks = a->count;
     out->used_blocks = used;
     out->total_refs = refs;
     out->exhaustion_events = a->exhaustion_events;
     out->waste_slots = waste;
     out->num_seqs = static_cast<int64_t>(a->seqs.size());
+    int64_t host_used = 0;
+    for (int32_t r : a->host_refcount) host_used += r > 0;
+    out->host_free_blocks = a->host_free.count;
+    out->host_used_blocks = host_used;
+    out->swapped_seqs = a->swapped_seqs;
     return PA_OK;
 }
 
@@ -290,6 +341,143 @@ int pa_alloc_dump(const pa_allocator* a, int32_t* refcounts, int32_t* free_order
     std::memcpy(refcounts, a->refcount.data(), a->refcount.size() * sizeof(int32_t));
     for (int64_t i = 0; i < a->count; ++i) free_order[i] = a->ring[(a->head + i) % a->num_blocks];
     *n_free = static_cast<int32_t>(a->count);
+    return PA_OK;
+}
+
+int pa_alloc_set_host_blocks(pa_allocator* a, int32_t num_host_blocks) {
+    pagedkv::clear_error();
+    if (!a) return fail(PA_ERR_INVALID, "pa_alloc_set_host_blocks: NULL allocator");
+    if (num_host_blocks < 0) return fail(PA_ERR_INVALID, "pa_alloc_set_host_blocks: %d < 0", num_host_blocks);
+    if (a->swapped_seqs > 0)
+        return fail(PA_ERR_INVALID, "pa_alloc_set_host_blocks: %lld sequences are swapped out",
+                    (long long)a->swapped_seqs);
+    a->host_refcount.assign(num_host_blocks, 0);
+    a->host_free.reset(num_host_blocks);
+    return PA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Moves the listed sequences' references from one pool to the other.  `from_ref` / `to_ref`
+// are the refcounts of the pools, `release` returns a block whose count reaches 0 to its
+// pool's free queue and `grant` pops the other pool's free head.  Validation (ids, state,
+// room, buffer size) has been done by the caller.
+template <class Release, class Grant>
+int32_t move_refs(const std::vector<Seq*>& ss, std::vector<int32_t>& from_ref,
+                  std::vector<int32_t>& to_ref, Release release, Grant grant, int64_t* pairs_out) {
+    std::unordered_map<int32_t, int32_t> map;   // block in the old pool -> block in the new
+    int32_t np = 0;
+    for (Seq* s : ss) {
+        for (int32_t& b : s->blocks) {
+            auto it = map.find(b);
+            int32_t nb;
+            if (it == map.end()) {
+                nb = grant();
+                to_ref[nb] = 0;
+                map.emplace(b, nb);
+                pairs_out[2 * np] = b;
+                pairs_out[2 * np + 1] = nb;
+                ++np;
+            } else {
+                nb = it->second;
+            }
+            to_ref[nb] += 1;
+            if (--from_ref[b] == 0) release(b);
+            b = nb;
+        }
+        s->swapped = !s->swapped;
+    }
+    return np;
+}
+
+// Checks the listed sequences (known, distinct, all in state `swapped`) and counts the
+// distinct blocks they hold.
+int collect(pa_allocator* a, const char* fn, const int64_t* seq_ids, int32_t n_seqs, bool swapped,
+            std::vector<Seq*>& ss, int64_t& distinct) {
+    if (n_seqs < 0) return fail(PA_ERR_INVALID, "%s: n_seqs=%d < 0", fn, n_seqs);
+    if (n_seqs > 0 && !seq_ids) return fail(PA_ERR_INVALID, "%s: seq_ids is NULL", fn);
+    std::unordered_map<int64_t, char> ids;
+    std::unordered_map<int32_t, char> blocks;
+    ss.resize(n_seqs);
+    for (int32_t i = 0; i < n_seqs; ++i) {
+        auto it = a->seqs.find(seq_ids[i]);
+        if (it == a->seqs.end()) return fail(PA_ERR_INVALID, "%s: unknown sequence %lld", fn, (long long)seq_ids[i]);
+        if (!ids.emplace(seq_ids[i], 1).second)
+            return fail(PA_ERR_INVALID, "%s: sequence %lld listed twice", fn, (long long)seq_ids[i]);
+        if (it->second.swapped != swapped)
+            return fail(PA_ERR_INVALID, "%s: sequence %lld is %s", fn, (long long)seq_ids[i],
+                        swapped ? "not swapped out" : "already swapped out");
+        ss[i] = &it->second;
+        for (int32_t b : it->second.blocks) blocks.emplace(b, 1);
+    }
+    distinct = static_cast<int64_t>(blocks.size());
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_swap_out(pa_allocator* a, const int64_t* seq_ids, int32_t n_seqs, int64_t* pairs_out,
+                int32_t max_pairs, int32_t* n_pairs_out) {
+    pagedkv::clear_error();
+    if (!a) return fail(PA_ERR_INVALID, "pa_swap_out: NULL allocator");
+    if (!n_pairs_out) return fail(PA_ERR_INVALID, "pa_swap_out: n_pairs_out is NULL");
+    std::vector<Seq*> ss;
+    int64_t distinct = 0;
+    if (int rc = collect(a, "pa_swap_out", seq_ids, n_seqs, false, ss, distinct)) return rc;
+    if (distinct > max_pairs || (distinct > 0 && !pairs_out))
+        return fail(PA_ERR_INVALID, "pa_swap_out: %lld pairs do not fit the buffer of %d", (long long)distinct, max_pairs);
+    if (distinct > a->host_free.count)
+        return fail(PA_ERR_NO_BLOCKS, "pa_swap_out: %lld host blocks needed, %lld free", (long long)distinct,
+                    (long long)a->host_free.count);
+    *n_pairs_out = move_refs(
+        ss, a->refcount, a->host_refcount, [a](int32_t b) { a->push(b); },
+        [a]() { return a->host_free.pop(); }, pairs_out);
+    a->swapped_seqs += n_seqs;
+    return PA_OK;
+}
+
+int pa_swap_in(pa_allocator* a, const int64_t* seq_ids, int32_t n_seqs, int64_t* pairs_out,
+               int32_t max_pairs, int32_t* n_pairs_out) {
+    pagedkv::clear_error();
+    if (!a) return fail(PA_ERR_INVALID, "pa_swap_in: NULL allocator");
+    if (!n_pairs_out) return fail(PA_ERR_INVALID, "pa_swap_in: n_pairs_out is NULL");
+    std::vector<Seq*> ss;
+    int64_t distinct = 0;
+    if (int rc = collect(a, "pa_swap_in", seq_ids, n_seqs, true, ss, distinct)) return rc;
+    if (distinct > max_pairs || (distinct > 0 && !pairs_out))
+        return fail(PA_ERR_INVALID, "pa_swap_in: %lld pairs do not fit the buffer of %d", (long long)distinct, max_pairs);
+    if (distinct > a->count) {
+        a->exhaustion_events += 1;
+        return fail(PA_ERR_NO_BLOCKS, "pa_swap_in: %lld blocks needed, %lld free", (long long)distinct,
+                    (long long)a->count);
+    }
+    *n_pairs_out = move_refs(
+        ss, a->host_refcount, a->refcount, [a](int32_t b) { a->host_free.push(b); },
+        [a]() { return a->pop(); }, pairs_out);
+    a->swapped_seqs -= n_seqs;
+    return PA_OK;
+}
+
+int pa_seq_is_swapped(const pa_allocator* a, int64_t seq_id) {
+    pagedkv::clear_error();
+    if (!a) return fail(PA_ERR_INVALID, "pa_seq_is_swapped: NULL allocator");
+    auto it = a->seqs.find(seq_id);
+    if (it == a->seqs.end()) return fail(PA_ERR_INVALID, "pa_seq_is_swapped: unknown sequence %lld", (long long)seq_id);
+    return it->second.swapped ? 1 : 0;
+}
+
+int pa_alloc_dump_host(const pa_allocator* a, int32_t* refcounts, int32_t* free_order, int32_t* n_free) {
+    pagedkv::clear_error();
+    if (!a || !n_free) return fail(PA_ERR_INVALID, "pa_alloc_dump_host: NULL argument");
+    const int64_t nh = static_cast<int64_t>(a->host_refcount.size());
+    if (nh > 0 && (!refcounts || !free_order)) return fail(PA_ERR_INVALID, "pa_alloc_dump_host: NULL argument");
+    if (nh > 0) std::memcpy(refcounts, a->host_refcount.data(), nh * sizeof(int32_t));
+    for (int64_t i = 0; i < a->host_free.count; ++i) free_order[i] = a->host_free.ring[(a->host_free.head + i) % nh];
+    *n_free = static_cast<int32_t>(a->host_free.count);
     return PA_OK;
 }
 

@@ -28,7 +28,9 @@
 //  (request, KV head) merges the partitions by log-sum-exp in the same launch (ticket
 //  counters, agent-scope stores and loads).
 //  zero_kernel           clears a workspace (a plain store kernel, no memset node).
-//  copy_blocks_kernel    whole-block copies for copy-on-write.
+//  copy_blocks_kernel    whole-block copies: copy-on-write inside a pool, and swapping blocks
+//                        between the device pool and a pinned host pool (read and written
+//                        over the host link by the kernel itself).
 //
 // Reduction order depends only on logical token positions (never on physical block ids),
 // so results are bit-identical under any placement of the blocks.
@@ -311,9 +313,12 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
 
 // ------------------------------------------------------------------ block copy
 
-__global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
-                                                          const int64_t* __restrict__ pairs, int num_pairs,
-                                                          int64_t num_blocks, int64_t block_bytes) {
+// Whole-block copies from one pool to another (or within one pool: copy-on-write).  Either
+// pool may be pinned host memory, which the loads and stores reach over the host link.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* dk, uint8_t* dv, const uint8_t* sk,
+                                                          const uint8_t* sv, const int64_t* __restrict__ pairs,
+                                                          int num_pairs, int64_t src_blocks, int64_t dst_blocks,
+                                                          int64_t block_bytes) {
     const int64_t vec_per_block = block_bytes / 16;
     const int64_t total = int64_t(num_pairs) * vec_per_block;
     for (int64_t gid = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; gid < total;
@@ -321,9 +326,11 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ 
         const int64_t pi = gid / vec_per_block;
         const int64_t off = (gid - pi * vec_per_block) * 16;
         const int64_t src = pairs[2 * pi], dst = pairs[2 * pi + 1];
-        if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) continue;
-        *reinterpret_cast<U4*>(kc + dst * block_bytes + off) = ld16(kc + src * block_bytes + off);
-        *reinterpret_cast<U4*>(vc + dst * block_bytes + off) = ld16(vc + src * block_bytes + off);
+        if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) continue;
+        const U4 k = ld16(sk + src * block_bytes + off);
+        const U4 v = ld16(sv + src * block_bytes + off);
+        *reinterpret_cast<U4*>(dk + dst * block_bytes + off) = k;
+        *reinterpret_cast<U4*>(dv + dst * block_bytes + off) = v;
     }
 }
 
@@ -1511,6 +1518,33 @@ int check_launch(const char* what) {
     return PA_OK;
 }
 
+// The address a kernel uses for the byte range [p, p + bytes) when that range lies inside
+// one HIP allocation in device memory or pinned host memory; anything else (pageable host
+// memory, a range running past its allocation) is refused before a launch could fault.
+int device_view(const void* p, int64_t bytes, const char* fn, const char* what, const void** out) {
+    hipPointerAttribute_t at{};
+    if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+        (void)hipGetLastError();   // leave no sticky error for the next call to report
+        return fail(PA_ERR_INVALID, "%s: %s is not memory known to HIP", fn, what);
+    }
+    if (at.type != hipMemoryTypeDevice && at.type != hipMemoryTypeHost)
+        return fail(PA_ERR_INVALID, "%s: %s is neither device nor pinned host memory (type %d)", fn, what,
+                    static_cast<int>(at.type));
+    void* start = nullptr;
+    size_t size = 0;
+    if (hipPointerGetAttribute(&start, HIP_POINTER_ATTRIBUTE_RANGE_START_ADDR, const_cast<void*>(p)) != hipSuccess ||
+        hipPointerGetAttribute(&size, HIP_POINTER_ATTRIBUTE_RANGE_SIZE, const_cast<void*>(p)) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(PA_ERR_INVALID, "%s: the allocation holding %s cannot be queried", fn, what);
+    }
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(start), hi = lo + size, q = reinterpret_cast<uintptr_t>(p);
+    if (q < lo || q + static_cast<uintptr_t>(bytes) > hi)
+        return fail(PA_ERR_INVALID, "%s: %s [%p, +%lld) runs past its allocation [%p, +%zu)", fn, what, p,
+                    (long long)bytes, start, size);
+    *out = at.type == hipMemoryTypeHost && at.devicePointer ? at.devicePointer : p;
+    return PA_OK;
+}
+
 int grid_for(int64_t work, int per_block) {
     int64_t blocks = (work + per_block - 1) / per_block;
     if (blocks > 65536) blocks = 65536;  // grid-stride loops cover the rest
@@ -1801,9 +1835,40 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst, int32_t
         return fail(PA_ERR_INVALID, "pa_copy_blocks: NULL or misaligned pointer");
     const int grid = grid_for(int64_t(num_pairs) * (block_bytes / 16), 256);
     hipLaunchKernelGGL(copy_blocks_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
-                       static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache), src_dst, num_pairs,
-                       num_blocks, block_bytes);
+                       static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
+                       static_cast<const uint8_t*>(k_cache), static_cast<const uint8_t*>(v_cache), src_dst,
+                       num_pairs, num_blocks, num_blocks, block_bytes);
     return check_launch("pa_copy_blocks");
+}
+
+int pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                   const int64_t* src_dst, int32_t num_pairs, int64_t src_num_blocks,
+                   int64_t dst_num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t block_size, int32_t cache_dtype, void* stream) {
+    pagedkv::clear_error();
+    const int eb = elem_bytes(cache_dtype);
+    if (eb == 0) return fail(PA_ERR_UNSUPPORTED, "pa_swap_blocks: cache dtype %d", cache_dtype);
+    if (num_pairs < 0 || src_num_blocks <= 0 || dst_num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0)
+        return fail(PA_ERR_INVALID, "pa_swap_blocks: bad sizes");
+    const int64_t block_bytes = int64_t(num_kv_heads) * block_size * head_dim * eb;
+    if (block_bytes % 16 != 0) return fail(PA_ERR_UNSUPPORTED, "pa_swap_blocks: block of %lld bytes", (long long)block_bytes);
+    if (num_pairs == 0) return PA_OK;
+    if (!dst_k || !dst_v || !src_k || !src_v || !src_dst || !aligned16(dst_k) || !aligned16(dst_v) ||
+        !aligned16(src_k) || !aligned16(src_v) || reinterpret_cast<uintptr_t>(src_dst) % 8 != 0)
+        return fail(PA_ERR_INVALID, "pa_swap_blocks: NULL or misaligned pointer");
+    const void *dk, *dv, *sk, *sv, *pr;
+    if (int rc = device_view(dst_k, dst_num_blocks * block_bytes, "pa_swap_blocks", "dst_k", &dk)) return rc;
+    if (int rc = device_view(dst_v, dst_num_blocks * block_bytes, "pa_swap_blocks", "dst_v", &dv)) return rc;
+    if (int rc = device_view(src_k, src_num_blocks * block_bytes, "pa_swap_blocks", "src_k", &sk)) return rc;
+    if (int rc = device_view(src_v, src_num_blocks * block_bytes, "pa_swap_blocks", "src_v", &sv)) return rc;
+    if (int rc = device_view(src_dst, int64_t(num_pairs) * 16, "pa_swap_blocks", "src_dst", &pr)) return rc;
+    const int grid = grid_for(int64_t(num_pairs) * (block_bytes / 16), 256);
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<uint8_t*>(const_cast<void*>(dk)), static_cast<uint8_t*>(const_cast<void*>(dv)),
+                       static_cast<const uint8_t*>(sk), static_cast<const uint8_t*>(sv),
+                       static_cast<const int64_t*>(pr), num_pairs, src_num_blocks, dst_num_blocks, block_bytes);
+    return check_launch("pa_swap_blocks");
 }
 
 }  // extern "C"

@@ -3,6 +3,7 @@
 // tests/test_lib_host.py.
 //   create N BS perm...      add S      append S n      batch k S1 n1 ... Sk nk
 //   fork P C                 free S     table S max     dump
+//   host NH                  swapout k S1 ... Sk        swapin k S1 ... Sk
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -84,12 +85,34 @@ int main() {
                 for (int i = 0; i < mb; ++i) std::printf(" %d", t[i]);
             }
             std::printf("\n");
+        } else if (o == "host") {
+            int nh;
+            std::scanf("%d", &nh);
+            std::printf("host %d\n", pa_alloc_set_host_blocks(a, nh));
+        } else if (o == "swapout" || o == "swapin") {
+            int k;
+            std::scanf("%d", &k);
+            std::vector<int64_t> ids(k);
+            for (int i = 0; i < k; ++i) {
+                long long s;
+                std::scanf("%lld", &s);
+                ids[i] = s;
+            }
+            const int maxp = 64;
+            std::vector<int64_t> pairs(2 * maxp);
+            int32_t np = 0;
+            rc = (o == "swapout" ? pa_swap_out : pa_swap_in)(a, ids.data(), k, pairs.data(), maxp, &np);
+            std::printf("%s %d", op, rc);
+            if (rc == 0)
+                for (int i = 0; i < np; ++i) std::printf(" %lld:%lld", (long long)pairs[2 * i], (long long)pairs[2 * i + 1]);
+            std::printf("\n");
         } else if (o == "dump") {
             pa_alloc_stats_t st;
             pa_alloc_stats(a, &st);
-            std::printf("stats %lld %lld %lld %lld %lld %lld\n", (long long)st.free_blocks, (long long)st.used_blocks,
-                        (long long)st.total_refs, (long long)st.exhaustion_events, (long long)st.waste_slots,
-                        (long long)st.num_seqs);
+            std::printf("stats %lld %lld %lld %lld %lld %lld %lld %lld %lld\n", (long long)st.free_blocks,
+                        (long long)st.used_blocks, (long long)st.total_refs, (long long)st.exhaustion_events,
+                        (long long)st.waste_slots, (long long)st.num_seqs, (long long)st.host_free_blocks,
+                        (long long)st.host_used_blocks, (long long)st.swapped_seqs);
         }
     }
     pa_alloc_destroy(a);

@@ -45,7 +45,7 @@ def test_header_symbols_exported():
     out = subprocess.run(["nm", "-D", "--defined-only", pk.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (pa_\w+)", out))
     assert set(names) <= exported
-    assert pk.load().pa_abi_version() == 2
+    assert pk.load().pa_abi_version() == 3
 
 
 def test_errors_are_reported():
@@ -116,9 +116,16 @@ def compare(c: pk.Allocator, o: OAlloc):
     assert list(ref) == oref
     assert list(free) == ofree
     st, ost = c.stats(), o.stats()
-    assert (st["free_blocks"], st["used_blocks"], st["total_refs"], st["exhaustion_events"], st["waste_slots"]) == \
-        (ost["free"], ost["used"], ost["refs"], ost["exhaustion_events"], ost["waste_slots"])
-    ids = sorted(o.seqs)
+    assert (st["free_blocks"], st["used_blocks"], st["total_refs"], st["exhaustion_events"], st["waste_slots"],
+            st["host_free_blocks"], st["host_used_blocks"], st["swapped_seqs"]) == \
+        (ost["free"], ost["used"], ost["refs"], ost["exhaustion_events"], ost["waste_slots"],
+         ost["host_free"], ost["host_used"], ost["swapped_seqs"])
+    if getattr(c, "num_host_blocks", 0):
+        href, hfree = c.dump_host()
+        assert (list(href), list(hfree)) == o.dump_host()
+    for sid in o.seqs:
+        assert c.is_swapped(sid) == o.is_swapped(sid)
+    ids = sorted(sid for sid in o.seqs if not o.is_swapped(sid))
     if ids:
         mb = max(1, max(len(s.blocks) for s in o.seqs.values()))
         t, L = c.block_tables(ids, mb)
@@ -140,6 +147,9 @@ def run_both(c, o, op, *args):
             elif op == "free":
                 (impl.free if impl is c else impl.release)(*args)
                 res.append(("ok",))
+            elif op in ("swap_out", "swap_in"):
+                r = getattr(impl, op)(*args)
+                res.append(("ok", [tuple(map(int, p)) for p in r]))
             else:
                 getattr(impl, op)(*args)
                 res.append(("ok",))
@@ -149,6 +159,47 @@ def run_both(c, o, op, *args):
             res.append(("invalid",))
     assert res[0] == res[1], (op, args, res)
     return res[0]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_allocator_with_swapping_matches_oracle_random(seed):
+    """Random traces mixing appends, forks, frees and swaps of random sequence sets (both
+    states, duplicates and unknown ids included) on small pools so both exhaust."""
+    rng = np.random.default_rng(2000 + seed)
+    N, NH = int(rng.integers(8, 40)), int(rng.integers(4, 40))
+    bs = int(rng.choice([1, 2, 4, 8]))
+    order = rng.permutation(N)
+    c, o = pk.Allocator(N, bs, order), OAlloc(N, bs, order)
+    run_both(c, o, "set_host_blocks", NH)
+    live, nid = [], 0
+    for _ in range(500):
+        r = rng.random()
+        # mostly sequences in the state the operation needs; now and then any live one
+        res = [x for x in live if not o.is_swapped(x)] if rng.random() < 0.9 else live
+        swp = [x for x in live if o.is_swapped(x)] if rng.random() < 0.9 else live
+        if r < 0.1 or not live:
+            run_both(c, o, "add", nid); live.append(nid); nid += 1
+        elif r < 0.4 and res:
+            run_both(c, o, "append", int(rng.choice(res)), int(rng.integers(0, 2 * bs + 2)))
+        elif r < 0.5 and res:
+            p = int(rng.choice(res))
+            if run_both(c, o, "fork", p, nid)[0] == "ok":
+                live.append(nid)
+            nid += 1
+        elif r < 0.85:
+            op, pool = ("swap_out", res) if rng.random() < 0.5 else ("swap_in", swp)
+            if not pool:
+                continue
+            k = int(rng.integers(1, min(5, len(pool)) + 1))
+            ids = [int(x) for x in rng.choice(pool, size=k, replace=False)]
+            if rng.random() < 0.05:
+                ids.append(ids[0])                       # duplicate -> invalid in both
+            run_both(c, o, op, ids)
+        elif r < 0.97:
+            s = int(rng.choice(live)); run_both(c, o, "free", s); live.remove(s)
+        else:
+            run_both(c, o, "set_host_blocks", NH)        # refused while anything is swapped out
+        compare(c, o)
 
 
 @pytest.mark.parametrize("seed", range(8))
@@ -244,11 +295,14 @@ def _driver_script(seed):
     rng = np.random.default_rng(seed)
     N, bs = 24, 4
     perm = rng.permutation(N)
-    lines = [f"create {N} {bs} " + " ".join(map(str, perm))]
+    lines = [f"create {N} {bs} " + " ".join(map(str, perm)), "host 12"]
     live, nid = [], 0
     for _ in range(300):
         r = rng.random()
-        if r < 0.15 or not live:
+        if live and r > 0.9 and rng.random() < 0.6:   # swap a random set (either state)
+            ids = rng.choice(live, size=min(len(live), int(rng.integers(1, 4))), replace=False)
+            lines.append(f"{'swapout' if rng.random() < 0.5 else 'swapin'} {len(ids)} " + " ".join(map(str, ids)))
+        elif r < 0.15 or not live:
             lines.append(f"add {nid}"); live.append(nid); nid += 1
         elif r < 0.5:
             lines.append(f"append {int(rng.choice(live))} {int(rng.integers(0, 10))}")
@@ -301,10 +355,15 @@ def test_allocator_under_asan_ubsan(tmp_path):
                     o.fork(int(f[1]), int(f[2]))
                 elif f[0] == "free":
                     o.release(int(f[1]))
+                elif f[0] == "host":
+                    o.set_host_blocks(int(f[1]))
+                elif f[0] in ("swapout", "swapin"):
+                    ids = [int(x) for x in f[2:]]
+                    (o.swap_out if f[0] == "swapout" else o.swap_in)(ids)
             except (NoBlocks, InvalidOp):
                 pass
             if f[0] == "dump":
                 s = o.stats()
                 want.append(f"stats {s['free']} {s['used']} {s['refs']} {s['exhaustion_events']} "
-                            f"{s['waste_slots']} {len(o.seqs)}")
+                            f"{s['waste_slots']} {len(o.seqs)} {s['host_free']} {s['host_used']} {s['swapped_seqs']}")
         assert got == want

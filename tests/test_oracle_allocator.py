@@ -137,3 +137,141 @@ def test_slots_are_unique_among_live_tokens():
         for sl in slots:
             assert sl not in owner
             owner[sl] = s
+
+
+# --------------------------------------------------------------------------- swapping
+
+def test_hand_traced_swap():
+    """Device pool of 4 blocks of 2 slots (free order [2, 0, 3, 1]), host pool of 3.  Every
+    value worked out by hand from the swap rules: each distinct block met walking the listed
+    sequences in order gets the next host block, references move with it, device references
+    drop as in a release."""
+    a = Allocator(4, 2, [2, 0, 3, 1])
+    a.set_host_blocks(3)
+    a.add(1)
+    a.append(1, 3)                       # blocks [2, 0]
+    a.fork(1, 2)                         # 2 shares [2, 0]
+    a.add(3)
+    a.append(3, 1)                       # block 3
+    assert a.dump() == ([2, 0, 2, 1], [1])
+    pairs = a.swap_out([2, 3])           # 2's blocks 2, 0, then 3's block 3
+    assert pairs == [(2, 0), (0, 1), (3, 2)]
+    assert a.dump() == ([1, 0, 1, 0], [1, 3])          # 2 and 0 still held by 1; 3 freed
+    assert a.dump_host() == ([1, 1, 1], [])
+    assert a.is_swapped(2) and a.is_swapped(3) and not a.is_swapped(1)
+    assert a.stats()["swapped_seqs"] == 2 and a.stats()["waste_slots"] == 1
+    with pytest.raises(NoBlocks):
+        a.swap_out([1])                  # needs 2 host blocks, none free
+    with pytest.raises(InvalidOp):
+        a.append(2, 1)
+    with pytest.raises(InvalidOp):
+        a.block_table([3], 2)
+    a.release(1)                         # device blocks 2, 0 -> free tail
+    assert a.dump() == ([0, 0, 0, 0], [1, 3, 2, 0])
+    pairs = a.swap_in([3, 2])            # 3's host block 2, then 2's host blocks 0, 1
+    assert pairs == [(2, 1), (0, 3), (1, 2)]
+    assert a.dump() == ([0, 1, 1, 1], [0])
+    assert a.dump_host() == ([0, 0, 0], [2, 0, 1])
+    t, L = a.block_table([2, 3], 2)
+    assert t == [[3, 2], [1, -1]] and L == [3, 1]
+
+
+def test_swap_exhaustion_and_invalid_leave_state_unchanged():
+    a = Allocator(4, 2)
+    a.set_host_blocks(2)
+    for s in (0, 1):
+        a.add(s)
+        a.append(s, 4)                   # 0: [0, 1], 1: [2, 3]
+    snap = lambda: (a.dump(), a.dump_host(), {k: (list(v.blocks), v.n, v.swapped) for k, v in a.seqs.items()})
+    before = snap()
+    with pytest.raises(NoBlocks):
+        a.swap_out([0, 1])               # 4 host blocks needed, 2 free
+    assert snap() == before and a.stats()["exhaustion_events"] == 0
+    for bad in (lambda: a.swap_out([0, 0]), lambda: a.swap_out([7]), lambda: a.swap_in([0]),
+                lambda: a.set_host_blocks(-1)):
+        with pytest.raises(InvalidOp):
+            bad()
+        assert snap() == before
+    a.swap_out([0])
+    a.add(2)
+    a.append(2, 4)                       # takes the two freed device blocks
+    before = snap()
+    with pytest.raises(NoBlocks):
+        a.swap_in([0])                   # no device block free
+    assert snap() == before and a.stats()["exhaustion_events"] == 1
+    with pytest.raises(InvalidOp):
+        a.set_host_blocks(4)             # refused while a sequence is swapped out
+    a.release(0)                         # a swapped sequence can be released
+    assert a.dump_host() == ([0, 0], [0, 1]) and a.stats()["swapped_seqs"] == 0
+
+
+def check_pool_invariants(a: Allocator):
+    """Both pools: refcount = number of table entries naming the block, free queue = the
+    blocks with refcount 0, each listed once."""
+    for swapped, ref, free in ((False, a.refcount, a.free), (True, a.host_refcount, a.host_free)):
+        held = [b for s in a.seqs.values() if s.swapped == swapped for b in s.blocks]
+        for b in range(len(ref)):
+            assert ref[b] == held.count(b)
+        assert sorted(free) == [b for b in range(len(ref)) if ref[b] == 0]
+    for s in a.seqs.values():
+        assert len(s.blocks) == -(-s.n // a.block_size) and len(set(s.blocks)) == len(s.blocks)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_swap_preserves_every_sequence_contents(seed):
+    """The page-table definition, with the cache simulated as token ids: tokens are written
+    at the slots the allocator returns, copy-on-write and swap pairs copy whole blocks between
+    the simulated pools, and after every operation each sequence read through its table (in
+    whichever pool holds it) must give exactly the tokens appended to it (a fork inherits its
+    parent's).  A block released while still held, a wrong pair or a lost reference would
+    let a later write or copy overwrite some sequence's tokens."""
+    rng = np.random.default_rng(500 + seed)
+    N, NH, bs = 24, 20, int(rng.choice([1, 2, 4]))
+    a = Allocator(N, bs, rng.permutation(N))
+    a.set_host_blocks(NH)
+    dev = np.full((N, bs), -1, np.int64)
+    host = np.full((NH, bs), -1, np.int64)
+    want = {}
+    live, nid, tok = [], 0, 0
+    swaps = 0
+    for _ in range(600):
+        r = rng.random()
+        try:
+            resident = [s for s in live if not a.seqs[s].swapped]
+            swapped = [s for s in live if a.seqs[s].swapped]
+            if r < 0.1 or not live:
+                a.add(nid); want[nid] = []; live.append(nid); nid += 1
+            elif r < 0.45 and resident:
+                s = int(rng.choice(resident)); n = int(rng.integers(1, 2 * bs + 1))
+                slots, cow = a.append(s, n)
+                for src, dst in cow:
+                    dev[dst] = dev[src]
+                for sl in slots:
+                    dev[sl // bs, sl % bs] = tok
+                    want[s].append(tok)
+                    tok += 1
+            elif r < 0.55 and resident:
+                p = int(rng.choice(resident)); a.fork(p, nid); want[nid] = list(want[p]); live.append(nid); nid += 1
+            elif r < 0.7 and resident:
+                k = int(rng.integers(1, min(4, len(resident)) + 1))
+                ids = [int(x) for x in rng.choice(resident, size=k, replace=False)]
+                for d, h in a.swap_out(ids):
+                    host[h] = dev[d]
+                swaps += 1
+            elif r < 0.85 and swapped:
+                k = int(rng.integers(1, min(4, len(swapped)) + 1))
+                ids = [int(x) for x in rng.choice(swapped, size=k, replace=False)]
+                for h, d in a.swap_in(ids):
+                    dev[d] = host[h]
+                swaps += 1
+            elif live:
+                s = int(rng.choice(live)); a.release(s); live.remove(s); del want[s]
+        except NoBlocks:
+            pass
+        check_pool_invariants(a)
+        for s in live:
+            q = a.seqs[s]
+            pool = host if q.swapped else dev
+            got = [int(pool[q.blocks[j // bs], j % bs]) for j in range(q.n)]
+            assert got == want[s], (s, q)
+    assert swaps > 20
