@@ -23,6 +23,7 @@ timed on a bounded sample of the same per-request work on the host.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
     python bench.py --workload {ragged_prefix,long_context,sweep}   # other workloads' decode rates
+    python bench.py --workload swap     # preemption: swap-out / swap-in rates over the host link
 """
 
 import argparse
@@ -398,10 +399,109 @@ def run_workload(name, args):
         torch.cuda.empty_cache()
 
 
+HOST_LINK_PEAK_GBPS = 64.0   # PCIe 5.0 x16, one direction (32 GT/s x 16 lanes, 128b/130b)
+
+
+def run_swap(args):
+    """Preemption by swapping on the ragged batch (256 requests, bf16, block 16): the 192
+    requests without the shared prefix are swapped out to a pinned host pool and back in,
+    `steps` times.  Timed with HIP events on the launch stream: each pa_swap_blocks launch
+    (device -> host, then host -> device); on the host: the allocator's pa_swap_out /
+    pa_swap_in.  For reference, the copy engine's rate for one contiguous buffer of the same
+    size in each direction (torch copy_ between device and pinned memory)."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_408_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    import paged_kv_cache_408_amd as pk
+    import workloads
+
+    dev = torch.device("cuda:0")
+    w = workloads.ragged_prefix(bs=16)
+    alloc = pk.Allocator(w.num_blocks, w.bs, w.free_order)
+    slots = []
+    for op in w.ops:
+        if op[0] == "add":
+            alloc.add(op[1])
+        elif op[0] == "append":
+            slots.append(alloc.append(op[1], op[2])[0])
+        elif op[0] == "fork":
+            alloc.fork(op[1], op[2])
+        elif op[0] == "free":
+            alloc.free(op[1])
+    slots = torch.from_numpy(np.concatenate(slots)).to(dev)
+    kc = torch.zeros((w.num_blocks, w.Hkv, w.bs, w.d), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    pk.pa_kv_write(workloads.device_normal(w, "k_pre", (slots.numel(), w.Hkv, w.d)),
+                   workloads.device_normal(w, "v_pre", (slots.numel(), w.Hkv, w.d)), slots, kc, vc)
+    victims = list(range(64, w.B))
+    nh = sum(-(-int(w.seq_lens[b]) // w.bs) for b in victims) + 16
+    alloc.set_host_blocks(nh)
+    hk = torch.empty((nh, w.Hkv, w.bs, w.d), dtype=torch.bfloat16).pin_memory()
+    hv = torch.empty_like(hk).pin_memory()
+    block = w.Hkv * w.bs * w.d * 2
+    out_us, in_us, host_out_us, host_in_us, npairs = [], [], [], [], 0
+    stream = torch.cuda.current_stream()
+    for it in range(max(args.warmup, 1) + args.steps):
+        t0 = time.perf_counter()
+        p_out = alloc.swap_out(victims)
+        t1 = time.perf_counter()
+        pd_out = torch.from_numpy(p_out).to(dev)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(stream)
+        pk.pa_swap_blocks(hk, hv, kc, vc, pd_out)
+        e[1].record(stream)
+        t2 = time.perf_counter()
+        p_in = alloc.swap_in(victims)
+        t3 = time.perf_counter()
+        pd_in = torch.from_numpy(p_in).to(dev)
+        e[2].record(stream)
+        pk.pa_swap_blocks(kc, vc, hk, hv, pd_in)
+        e[3].record(stream)
+        torch.cuda.synchronize()
+        if it >= max(args.warmup, 1):
+            out_us.append(e[0].elapsed_time(e[1]) * 1e3)
+            in_us.append(e[2].elapsed_time(e[3]) * 1e3)
+            host_out_us.append((t1 - t0) * 1e6)
+            host_in_us.append((t3 - t2) * 1e6)
+            npairs = len(p_out)
+    nbytes = 2 * npairs * block
+    # the copy engine on one contiguous buffer of the same size, each direction
+    dbuf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    hbuf = torch.empty(nbytes, dtype=torch.uint8).pin_memory()
+    ce = {"d2h": [], "h2d": []}
+    for it in range(3 + args.steps // 2):
+        for name, (dst, src) in (("d2h", (hbuf, dbuf)), ("h2d", (dbuf, hbuf))):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            dst.copy_(src, non_blocking=True)
+            b.record(stream)
+            torch.cuda.synchronize()
+            if it >= 3:
+                ce[name].append(a.elapsed_time(b) * 1e3)
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    for name, us, hus, cus in (("swap_out_device_to_host", out_us, host_out_us, ce["d2h"]),
+                               ("swap_in_host_to_device", in_us, host_in_us, ce["h2d"])):
+        m = med(us)
+        print(json.dumps({
+            "workload": f"{w.name}: {name}", "metric": "swapped KV GB/s", "unit": "GB/s",
+            "requests": len(victims), "block_pairs": npairs, "bytes": nbytes,
+            "kernel_us_median": round(m, 2), "gbps": round(nbytes / m / 1e3, 2),
+            "pct_of_host_link_peak": round(100 * nbytes / m / 1e3 / HOST_LINK_PEAK_GBPS, 1),
+            "host_link_peak_gbps": HOST_LINK_PEAK_GBPS,
+            "copy_engine_contiguous_gbps": round(nbytes / med(cus) / 1e3, 2),
+            "allocator_us_median": round(med(hus), 1), "steps": args.steps,
+        }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--workload", default="llama3_8b", choices=["llama3_8b", "ragged_prefix", "long_context", "sweep"],
+    ap.add_argument("--workload", default="llama3_8b",
+                    choices=["llama3_8b", "ragged_prefix", "long_context", "sweep", "swap"],
                     help="llama3_8b: the benchmark; the others print per-setting measurements instead")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
@@ -424,6 +524,9 @@ def main():
         return
     if args.calibrate_read:
         calibrate_read()
+        return
+    if args.workload == "swap":
+        run_swap(args)
         return
     if args.workload != "llama3_8b":
         run_workload(args.workload, args)

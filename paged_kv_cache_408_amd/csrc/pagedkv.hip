@@ -1530,6 +1530,11 @@ int device_view(const void* p, int64_t bytes, const char* fn, const char* what, 
     if (at.type != hipMemoryTypeDevice && at.type != hipMemoryTypeHost)
         return fail(PA_ERR_INVALID, "%s: %s is neither device nor pinned host memory (type %d)", fn, what,
                     static_cast<int>(at.type));
+    unsigned int host_flags = 0;
+    if (at.type == hipMemoryTypeHost && hipHostGetFlags(&host_flags, const_cast<void*>(p)) != hipSuccess) {
+        (void)hipGetLastError();   // host memory that HIP did not allocate or register
+        return fail(PA_ERR_INVALID, "%s: %s is host memory not allocated by HIP", fn, what);
+    }
     void* start = nullptr;
     size_t size = 0;
     if (hipPointerGetAttribute(&start, HIP_POINTER_ATTRIBUTE_RANGE_START_ADDR, const_cast<void*>(p)) != hipSuccess ||
