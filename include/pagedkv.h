@@ -209,6 +209,9 @@ typedef struct {
     int64_t host_free_blocks;   /* host pool: blocks in its free queue                   */
     int64_t host_used_blocks;   /* host pool: blocks with refcount > 0                   */
     int64_t swapped_seqs;       /* sequences whose blocks are in the host pool           */
+    int64_t cached_blocks;      /* prefix cache: device blocks registered under content  */
+    int64_t cache_hit_blocks;   /* prefix cache: blocks taken from the cache by prompts  */
+    int64_t cache_evictions;    /* prefix cache: registered blocks handed out again      */
 } pa_alloc_stats_t;
 
 /* num_blocks > 0, block_size > 0; initial_free_order: host int32 [num_blocks], a
@@ -232,6 +235,43 @@ int pa_batch_append(pa_allocator* a, const int64_t* seq_ids, const int32_t* n_to
 
 int pa_seq_fork(pa_allocator* a, int64_t parent, int64_t child);
 int pa_seq_free(pa_allocator* a, int64_t seq_id);
+
+/* ---------------------------------------------------------------- prefix caching
+ *
+ * "KV Cache Management", "The Bonus: Zero-Copy Sharing": the KV cache of a system prompt that
+ * many users share is computed and stored once, and every user's block table points at the
+ * same block; "KV Cache Optimization and PagedAttention", first paragraph, names this prefix
+ * caching.  Here a block is registered under its content -- the whole token prefix from
+ * token 0 to the block's end -- when a sequence whose token ids are all known fills it.
+ * Rules:
+ *  - content is compared exactly (token ids and the whole prefix before them);
+ *  - a block whose content is already registered to another block is not registered;
+ *  - a registered block at refcount 0 stays registered while it waits in the free queue; when
+ *    the queue hands it out again its registration is dropped (eviction, in release order);
+ *  - only sequences created empty or by pa_seq_add_prompt and grown by pa_seq_append_tokens
+ *    have known token ids; pa_seq_append / pa_batch_append make them unknown for good (no
+ *    later block of that sequence is registered); fork copies the parent's state; a
+ *    swapped-in sequence's blocks are fresh and unregistered, later ones are registered. */
+
+/* Create sequence seq_id holding the n_tokens prompt tokens: from block 0 on, every block
+ * whose content equals the prompt's prefix is taken from the cache (refcount + 1; a free one
+ * leaves the free queue), stopping at the first block that is not registered; *n_cached_out
+ * receives the tokens so covered (a multiple of block_size), whose K/V the caller does not
+ * write.  The remaining n_tokens - *n_cached_out tokens are appended as by
+ * pa_seq_append_tokens; slots_out (host int64 [n_tokens - *n_cached_out]) receives their
+ * slots.  PA_ERR_NO_BLOCKS (nothing changed, one exhaustion event) if the free blocks not
+ * taken as hits cannot hold the rest. */
+int pa_seq_add_prompt(pa_allocator* a, int64_t seq_id, const int32_t* tokens, int32_t n_tokens,
+                      int32_t* n_cached_out, int64_t* slots_out);
+
+/* pa_seq_append with the new tokens' ids (host int32 [n_tokens]): every block the append
+ * fills is registered under its content. */
+int pa_seq_append_tokens(pa_allocator* a, int64_t seq_id, const int32_t* tokens, int32_t n_tokens,
+                         int64_t* slots_out, int64_t* cow_out, int32_t* n_cow_out);
+
+/* registered[b] = 1 if device block b is registered in the prefix cache, else 0 (host int32
+ * [num_blocks]). */
+int pa_alloc_dump_cached(const pa_allocator* a, int32_t* registered);
 
 /* Rows of physical block ids for the given sequences, padded with -1, and their token
  * counts.  tables_out: host int32 [n_seqs][max_blocks]; seq_lens_out: host int32 [n_seqs].

@@ -48,6 +48,22 @@ only; the reading taken here:
   be swapped in or released (releasing its host blocks).
 * A swap is all-or-nothing; a swap-in refused for lack of device blocks counts as an
   exhaustion event, a swap-out refused for lack of host blocks does not.
+
+Prefix caching ("KV Cache Management", "The Bonus: Zero-Copy Sharing": a system prompt
+shared by many users is computed and stored once and their tables all point at it; "KV
+Cache Optimization and PagedAttention", first paragraph: prefix caching).  Readings:
+
+* A full block is registered under its content, the tuple of every token id from position
+  0 to the block's end, when a sequence whose token ids are all known fills it, unless that
+  content is already registered to another block.
+* A sequence added with its prompt takes, from block 0 on, the registered block of each
+  prefix that ends at a block boundary, and stops at the first one that is not registered;
+  the tokens so covered are reported as cached.  The rest of the prompt is appended.
+* A registered block whose refcount reaches 0 stays registered in the free queue; a hit
+  takes it out of the queue; when the queue hands it out again its registration is dropped.
+* Token ids are known for sequences created empty or by a prompt and grown only by appends
+  that give ids; an append without ids (of at least one token) makes them unknown for good.
+  A fork copies its parent's ids.
 """
 
 from __future__ import annotations
@@ -69,6 +85,7 @@ class _Seq:
     blocks: list = field(default_factory=list)   # device ids, or host ids while swapped
     n: int = 0
     swapped: bool = False
+    tokens: list = field(default_factory=list)   # every token id held, or None if unknown
 
 
 class Allocator:
@@ -86,6 +103,18 @@ class Allocator:
         self.exhaustion_events = 0
         self.host_free = deque()
         self.host_refcount = []
+        self.cache = {}            # token-id prefix (tuple) ending at a block end -> block
+        self.cached_key = {}       # block -> its prefix
+        self.cache_hit_blocks = 0
+        self.cache_evictions = 0
+
+    def _grant(self) -> int:
+        """The free queue's head; a registered block loses its registration."""
+        b = self.free.popleft()
+        if b in self.cached_key:
+            del self.cache[self.cached_key.pop(b)]
+            self.cache_evictions += 1
+        return b
 
     def _resident(self, seq_id: int) -> _Seq:
         if seq_id not in self.seqs:
@@ -110,31 +139,70 @@ class Allocator:
                 need += 1                               # a fresh block for this token
         return need
 
-    def append(self, seq_id: int, n_tokens: int):
-        """Append n_tokens to a sequence.  Returns (slots, cow_pairs)."""
+    def append(self, seq_id: int, n_tokens: int, token_ids=None):
+        """Append n_tokens to a sequence (their ids, if given, register the blocks they
+        fill).  Returns (slots, cow_pairs)."""
         s = self._resident(seq_id)
         if n_tokens < 0:
             raise InvalidOp("negative token count")
+        if token_ids is not None and len(token_ids) != n_tokens:
+            raise InvalidOp("token ids do not match the count")
         if self._blocks_needed(s, n_tokens) > len(self.free):
             self.exhaustion_events += 1
             raise NoBlocks(f"sequence {seq_id}: not enough free blocks")
         bs = self.block_size
+        if token_ids is None and n_tokens > 0:
+            s.tokens = None
         slots, cow = [], []
-        for _ in range(n_tokens):
+        for t in range(n_tokens):
             if s.n % bs == 0:
-                b = self.free.popleft()
+                b = self._grant()
                 self.refcount[b] = 1
                 s.blocks.append(b)
             elif self.refcount[s.blocks[-1]] > 1:
                 old = s.blocks[-1]
-                new = self.free.popleft()
+                new = self._grant()
                 self.refcount[old] -= 1
                 self.refcount[new] = 1
                 s.blocks[-1] = new
                 cow.append((old, new))
             slots.append(s.blocks[-1] * bs + s.n % bs)
             s.n += 1
+            if s.tokens is not None:
+                s.tokens.append(int(token_ids[t]))
+                if s.n % bs == 0 and tuple(s.tokens) not in self.cache:
+                    assert s.blocks[-1] not in self.cached_key
+                    self.cache[tuple(s.tokens)] = s.blocks[-1]
+                    self.cached_key[s.blocks[-1]] = tuple(s.tokens)
         return slots, cow
+
+    def add_prompt(self, seq_id: int, token_ids):
+        """Create a sequence holding the prompt: registered blocks whose prefix matches are
+        taken from block 0 on (up to the first miss), the rest is appended.  Returns
+        (cached tokens, slots of the rest)."""
+        if seq_id in self.seqs:
+            raise InvalidOp(f"sequence {seq_id} already exists")
+        token_ids = [int(t) for t in token_ids]
+        bs = self.block_size
+        hits = []
+        while (len(hits) + 1) * bs <= len(token_ids):
+            key = tuple(token_ids[: (len(hits) + 1) * bs])
+            if key not in self.cache:
+                break
+            hits.append(self.cache[key])
+        n_cached = len(hits) * bs
+        need = -(-(len(token_ids) - n_cached) // bs)
+        if need > len(self.free) - sum(1 for b in hits if self.refcount[b] == 0):
+            self.exhaustion_events += 1
+            raise NoBlocks(f"sequence {seq_id}: not enough free blocks")
+        for b in hits:
+            if self.refcount[b] == 0:
+                self.free.remove(b)
+            self.refcount[b] += 1
+        self.cache_hit_blocks += len(hits)
+        self.seqs[seq_id] = _Seq(blocks=list(hits), n=n_cached, tokens=token_ids[:n_cached])
+        slots, _ = self.append(seq_id, len(token_ids) - n_cached, token_ids[n_cached:])
+        return n_cached, slots
 
     def append_batch(self, seq_ids, n_tokens):
         """Appends to several distinct sequences in order, all or nothing: the appends are
@@ -165,7 +233,8 @@ class Allocator:
             raise InvalidOp(f"sequence {child} already exists")
         for b in p.blocks:
             self.refcount[b] += 1
-        self.seqs[child] = _Seq(blocks=list(p.blocks), n=p.n)
+        self.seqs[child] = _Seq(blocks=list(p.blocks), n=p.n,
+                                tokens=None if p.tokens is None else list(p.tokens))
 
     def release(self, seq_id: int) -> None:
         if seq_id not in self.seqs:
@@ -205,12 +274,13 @@ class Allocator:
             raise NoBlocks("not enough free blocks in the destination pool")
         moved = {}
         pairs = []
+        grant = self.host_free.popleft if to_host else self._grant
         for sid in seq_ids:
             s = self.seqs[sid]
             new_blocks = []
             for b in s.blocks:
                 if b not in moved:
-                    moved[b] = dst_free.popleft()
+                    moved[b] = grant()
                     pairs.append((b, moved[b]))
                 dst_ref[moved[b]] += 1
                 src_ref[b] -= 1
@@ -266,7 +336,14 @@ class Allocator:
             "host_free": len(self.host_free),
             "host_used": sum(1 for r in self.host_refcount if r > 0),
             "swapped_seqs": sum(1 for s in self.seqs.values() if s.swapped),
+            "cached_blocks": len(self.cache),
+            "cache_hit_blocks": self.cache_hit_blocks,
+            "cache_evictions": self.cache_evictions,
         }
+
+    def dump_cached(self):
+        """1 for each block registered in the prefix cache, else 0."""
+        return [1 if b in self.cached_key else 0 for b in range(self.num_blocks)]
 
     def dump(self):
         """(refcounts, free queue in order) for bit-exact comparison."""

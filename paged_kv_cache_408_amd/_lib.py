@@ -25,7 +25,7 @@ EXPORTED = [
     "pa_copy_blocks", "pa_alloc_create", "pa_alloc_destroy", "pa_seq_add", "pa_seq_append",
     "pa_batch_append", "pa_seq_fork", "pa_seq_free", "pa_block_tables", "pa_alloc_stats",
     "pa_alloc_dump", "pa_alloc_set_host_blocks", "pa_swap_out", "pa_swap_in", "pa_seq_is_swapped",
-    "pa_alloc_dump_host", "pa_swap_blocks",
+    "pa_alloc_dump_host", "pa_swap_blocks", "pa_seq_add_prompt", "pa_seq_append_tokens", "pa_alloc_dump_cached",
 ]
 
 
@@ -46,7 +46,8 @@ class UnsupportedError(PagedKVError):
 class pa_alloc_stats_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in
                 ("free_blocks", "used_blocks", "total_refs", "exhaustion_events", "waste_slots", "num_seqs",
-                 "host_free_blocks", "host_used_blocks", "swapped_seqs")]
+                 "host_free_blocks", "host_used_blocks", "swapped_seqs", "cached_blocks", "cache_hit_blocks",
+                 "cache_evictions")]
 
 
 _lib = None
@@ -88,6 +89,9 @@ def load(path: str = LIB_PATH):
         "pa_seq_is_swapped": (ctypes.c_int, [P, I64]),
         "pa_alloc_dump_host": (ctypes.c_int, [P, P, P, P]),
         "pa_swap_blocks": (ctypes.c_int, [P, P, P, P, P, I32, I64, I64, I32, I32, I32, I32, P]),
+        "pa_seq_add_prompt": (ctypes.c_int, [P, I64, P, I32, P, P]),
+        "pa_seq_append_tokens": (ctypes.c_int, [P, I64, P, I32, P, P, P]),
+        "pa_alloc_dump_cached": (ctypes.c_int, [P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -325,6 +329,31 @@ def pa_seq_append(h, seq_id, n_tokens):
     return slots[:n_tokens], [(int(cow[0]), int(cow[1]))] if ncow[0] else []
 
 
+def pa_seq_append_tokens(h, seq_id, token_ids):
+    toks = np.ascontiguousarray(token_ids, dtype=np.int32)
+    n = len(toks)
+    slots = np.empty(max(n, 1), dtype=np.int64)
+    cow = np.empty(2, dtype=np.int64)
+    ncow = np.zeros(1, dtype=np.int32)
+    _check(load().pa_seq_append_tokens(h, seq_id, _p(toks), n, _p(slots), _p(cow), _p(ncow)))
+    return slots[:n], [(int(cow[0]), int(cow[1]))] if ncow[0] else []
+
+
+def pa_seq_add_prompt(h, seq_id, token_ids):
+    """Returns (tokens found in the prefix cache, slots of the remaining tokens)."""
+    toks = np.ascontiguousarray(token_ids, dtype=np.int32)
+    slots = np.empty(max(len(toks), 1), dtype=np.int64)
+    nc = np.zeros(1, dtype=np.int32)
+    _check(load().pa_seq_add_prompt(h, seq_id, _p(toks), len(toks), _p(nc), _p(slots)))
+    return int(nc[0]), slots[: len(toks) - int(nc[0])]
+
+
+def pa_alloc_dump_cached(h, num_blocks):
+    reg = np.empty(num_blocks, dtype=np.int32)
+    _check(load().pa_alloc_dump_cached(h, _p(reg)))
+    return reg
+
+
 def pa_batch_append(h, seq_ids, n_tokens):
     ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
     nt = np.ascontiguousarray(n_tokens, dtype=np.int32)
@@ -419,8 +448,18 @@ class Allocator:
     def add(self, seq_id):
         pa_seq_add(self._h, seq_id)
 
-    def append(self, seq_id, n_tokens):
+    def append(self, seq_id, n_tokens, token_ids=None):
+        if token_ids is not None:
+            if len(token_ids) != n_tokens:
+                raise ValueError("token_ids must hold n_tokens ids")
+            return pa_seq_append_tokens(self._h, seq_id, token_ids)
         return pa_seq_append(self._h, seq_id, n_tokens)
+
+    def add_prompt(self, seq_id, token_ids):
+        return pa_seq_add_prompt(self._h, seq_id, token_ids)
+
+    def dump_cached(self):
+        return pa_alloc_dump_cached(self._h, self.num_blocks)
 
     def batch_append(self, seq_ids, n_tokens):
         return pa_batch_append(self._h, seq_ids, n_tokens)

@@ -18,11 +18,24 @@
 //    gives each distinct device block one host block (pair reported for the copy), moves every
 //    reference to the host block and releases the device references as a free would; swap-in
 //    is the mirror image.  A device block also held by a sequence that stays resident keeps
-//    that holder and is copied, so the swapped set and the resident one stop sharing it.
+//    that holder and is copied, so the swapped set and the resident one stop sharing it;
+//  - prefix caching ("KV Cache Management", "The Bonus: Zero-Copy Sharing": a system prompt
+//    shared by many users is computed and stored once and every user's table points at that
+//    block; "KV Cache Optimization and PagedAttention", first paragraph: prefix caching):
+//    a full block whose token ids are known is registered under its content, the whole token
+//    prefix up to its end.  A new sequence added with its prompt takes, from block 0 on, every
+//    registered block whose content equals its own prefix and stops at the first miss; the
+//    caller computes and writes K/V only from there.  A registered block whose refcount drops
+//    to 0 stays registered in the free queue until the queue hands it out again (then its
+//    registration is dropped: eviction in release order); a hit takes it out of the queue.
 //
-// Storage: refcounts and the free queue are flat int32 arrays of num_blocks entries (the
-// queue is a ring: it never holds more than num_blocks ids); each sequence keeps its block
-// list in a vector, so a table export is a memcpy per sequence.
+// Storage: refcounts are a flat int32 array; the device free queue is an intrusive doubly
+// linked list over block ids (FIFO, and a hit removes a block from its middle in O(1)); the
+// host pool's queue is a ring.  Each sequence keeps its block list in a vector, so a table
+// export is a memcpy per sequence.  Block contents are interned: a node stands for a token
+// prefix ending at a block boundary, keyed exactly by (node of the prefix one block shorter,
+// the block's token ids) in a hash table; nodes live while a block, a longer prefix or a
+// sequence refers to them.
 
 #include <algorithm>
 #include <cstdint>
@@ -42,6 +55,71 @@ struct Seq {
     std::vector<int32_t> blocks;  // device block ids, or host block ids while swapped out
     int64_t n = 0;                // tokens held
     bool swapped = false;
+    bool tracked = true;          // the token id of every token held is known
+    int64_t chain = -1;           // content node of the last full block (-1: none)
+    std::vector<int32_t> partial; // token ids in the partially filled last block (tracked only)
+};
+
+// The device pool's FIFO free queue with O(1) removal of any member: an intrusive doubly
+// linked list over block ids.
+struct FreeList {
+    std::vector<int32_t> nxt, prv;
+    int32_t head = -1, tail = -1;
+    int64_t count = 0;
+    void init(int32_t n) {
+        nxt.assign(n, -1);
+        prv.assign(n, -1);
+        head = tail = -1;
+        count = 0;
+    }
+    void push(int32_t b) {
+        prv[b] = tail;
+        nxt[b] = -1;
+        if (tail >= 0) nxt[tail] = b; else head = b;
+        tail = b;
+        ++count;
+    }
+    void remove(int32_t b) {
+        const int32_t p = prv[b], q = nxt[b];
+        if (p >= 0) nxt[p] = q; else head = q;
+        if (q >= 0) prv[q] = p; else tail = p;
+        --count;
+    }
+    int32_t pop() {
+        const int32_t b = head;
+        remove(b);
+        return b;
+    }
+};
+
+// Content of a full block: the node of the token prefix one block shorter (-1 for the first
+// block) and the block's own token ids.  Compared exactly; the hash (FNV-1a, 64 bit, over the
+// parent id's 8 bytes and each token id's 4 bytes, little end first) only indexes the table.
+struct BlockKey {
+    int64_t parent;
+    std::vector<int32_t> tokens;
+    bool operator==(const BlockKey& o) const { return parent == o.parent && tokens == o.tokens; }
+};
+
+struct BlockKeyHash {
+    size_t operator()(const BlockKey& k) const {
+        uint64_t h = 14695981039346656037ull;
+        auto mix = [&h](uint64_t v, int bytes) {
+            for (int i = 0; i < bytes; ++i) {
+                h ^= (v >> (8 * i)) & 0xffu;
+                h *= 1099511628211ull;
+            }
+        };
+        mix(static_cast<uint64_t>(k.parent), 8);
+        for (int32_t t : k.tokens) mix(static_cast<uint32_t>(t), 4);
+        return static_cast<size_t>(h);
+    }
+};
+
+struct Node {
+    BlockKey key;
+    int32_t block = -1;   // the registered device block holding this content, or -1
+    int64_t refs = 0;     // longer prefixes + sequences ending a full block here + (block >= 0)
 };
 
 // A FIFO queue of free block ids over a ring of capacity `cap` (it never holds more).
@@ -72,24 +150,79 @@ struct pa_allocator {
     int32_t num_blocks = 0;
     int32_t block_size = 0;
     std::vector<int32_t> refcount;
-    std::vector<int32_t> ring;   // free queue storage
-    int64_t head = 0;            // index of the queue head in `ring`
-    int64_t count = 0;           // ids in the queue
+    FreeList freeq;
     std::unordered_map<int64_t, Seq> seqs;
     int64_t exhaustion_events = 0;
     std::vector<int32_t> host_refcount;   // host pool (empty until pa_alloc_set_host_blocks)
     FreeQueue host_free;
     int64_t swapped_seqs = 0;
+    // prefix cache
+    std::unordered_map<BlockKey, int64_t, BlockKeyHash> node_of_key;
+    std::unordered_map<int64_t, Node> nodes;
+    std::vector<int64_t> node_of_block;   // device block -> the node it is registered under, or -1
+    int64_t next_node = 0;
+    int64_t cached_blocks = 0, cache_hit_blocks = 0, cache_evictions = 0;
 
+    // Drops one reference of a node; a node left without references is deleted, which drops
+    // its reference on the prefix one block shorter, and so on.
+    void unref(int64_t id) {
+        while (id >= 0) {
+            auto it = nodes.find(id);
+            if (--it->second.refs > 0) return;
+            const int64_t parent = it->second.key.parent;
+            node_of_key.erase(it->second.key);
+            nodes.erase(it);
+            id = parent;
+        }
+    }
+    // The node of (parent, tokens), created without references if new.
+    int64_t intern(int64_t parent, const std::vector<int32_t>& tokens) {
+        BlockKey k{parent, tokens};
+        auto it = node_of_key.find(k);
+        if (it != node_of_key.end()) return it->second;
+        const int64_t id = next_node++;
+        nodes.emplace(id, Node{k, -1, 0});
+        node_of_key.emplace(std::move(k), id);
+        if (parent >= 0) nodes.find(parent)->second.refs += 1;
+        return id;
+    }
+    // Hands out the free queue's head; a registered block loses its registration.
     int32_t pop() {
-        int32_t b = ring[head];
-        head = (head + 1) % num_blocks;
-        --count;
+        const int32_t b = freeq.pop();
+        const int64_t id = node_of_block[b];
+        if (id >= 0) {
+            node_of_block[b] = -1;
+            nodes.find(id)->second.block = -1;
+            cached_blocks -= 1;
+            cache_evictions += 1;
+            unref(id);
+        }
         return b;
     }
-    void push(int32_t b) {
-        ring[(head + count) % num_blocks] = b;
-        ++count;
+    void push(int32_t b) { freeq.push(b); }
+    // The sequence's token ids stop being known: it leaves the content chain.
+    void untrack(Seq& s) {
+        if (!s.tracked) return;
+        if (s.chain >= 0) unref(s.chain);
+        s.chain = -1;
+        s.partial.clear();
+        s.tracked = false;
+    }
+    // A tracked sequence has just filled block b (its tokens are s.partial): the sequence's
+    // chain moves to that content, and b is registered under it unless another block is.
+    void complete_block(Seq& s, int32_t b) {
+        const int64_t id = intern(s.chain, s.partial);
+        Node& nd = nodes.find(id)->second;
+        nd.refs += 1;                         // the sequence's reference
+        if (s.chain >= 0) unref(s.chain);     // still held by the new node
+        s.chain = id;
+        s.partial.clear();
+        if (nd.block < 0) {
+            nd.block = b;
+            nd.refs += 1;
+            node_of_block[b] = id;
+            cached_blocks += 1;
+        }
     }
     // Blocks one append of n tokens to `s` would take, given `extra_drop` references that
     // earlier appends in the same batch already moved off s's last block.
@@ -104,9 +237,12 @@ struct pa_allocator {
         if (last >= first) need += last - first + 1;
         return need;
     }
-    // Performs an append already known to fit.  Returns the number of COW pairs (0 or 1).
-    int append_fit(Seq& s, int64_t n, int64_t* slots, int64_t* cow) {
+    // Performs an append already known to fit, registering the blocks it fills when the
+    // tokens' ids are given and the sequence is tracked.  Returns the number of COW pairs (0
+    // or 1).
+    int append_fit(Seq& s, int64_t n, int64_t* slots, int64_t* cow, const int32_t* tokens = nullptr) {
         const int64_t bs = block_size;
+        if (!tokens && n > 0) untrack(s);
         int ncow = 0;
         for (int64_t t = 0; t < n; ++t) {
             if (s.n % bs == 0) {
@@ -125,6 +261,10 @@ struct pa_allocator {
             }
             slots[t] = static_cast<int64_t>(s.blocks.back()) * bs + s.n % bs;
             s.n += 1;
+            if (s.tracked) {
+                s.partial.push_back(tokens[t]);
+                if (s.n % bs == 0) complete_block(s, s.blocks.back());
+            }
         }
         return ncow;
     }
@@ -145,7 +285,8 @@ int pa_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* initi
     a->num_blocks = num_blocks;
     a->block_size = block_size;
     a->refcount.assign(num_blocks, 0);
-    a->ring.resize(num_blocks);
+    a->node_of_block.assign(num_blocks, -1);
+    a->freeq.init(num_blocks);
     if (initial_free_order) {
         std::vector<char> seen(num_blocks, 0);
         for (int32_t i = 0; i < num_blocks; ++i) {
@@ -157,13 +298,11 @@ int pa_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* initi
                             i, b);
             }
             seen[b] = 1;
-            a->ring[i] = b;
         }
+        for (int32_t i = 0; i < num_blocks; ++i) a->freeq.push(initial_free_order[i]);
     } else {
-        for (int32_t i = 0; i < num_blocks; ++i) a->ring[i] = i;
+        for (int32_t i = 0; i < num_blocks; ++i) a->freeq.push(i);
     }
-    a->head = 0;
-    a->count = num_blocks;
     *out = a;
     return PA_OK;
 }
@@ -190,12 +329,83 @@ int pa_seq_append(pa_allocator* a, int64_t seq_id, int32_t n_tokens, int64_t* sl
     Seq& s = it->second;
     if (s.swapped) return fail(PA_ERR_INVALID, "pa_seq_append: sequence %lld is swapped out", (long long)seq_id);
     int64_t need = a->blocks_needed(s, n_tokens, 0);
-    if (need > a->count) {
+    if (need > a->freeq.count) {
         a->exhaustion_events += 1;
         return fail(PA_ERR_NO_BLOCKS, "pa_seq_append: sequence %lld needs %lld blocks, %lld free",
-                    (long long)seq_id, (long long)need, (long long)a->count);
+                    (long long)seq_id, (long long)need, (long long)a->freeq.count);
     }
     *n_cow_out = a->append_fit(s, n_tokens, slots_out, cow_out);
+    return PA_OK;
+}
+
+int pa_seq_append_tokens(pa_allocator* a, int64_t seq_id, const int32_t* tokens, int32_t n_tokens,
+                         int64_t* slots_out, int64_t* cow_out, int32_t* n_cow_out) {
+    pagedkv::clear_error();
+    if (!a) return fail(PA_ERR_INVALID, "pa_seq_append_tokens: NULL allocator");
+    if (n_tokens < 0) return fail(PA_ERR_INVALID, "pa_seq_append_tokens: n_tokens=%d < 0", n_tokens);
+    if (n_tokens > 0 && (!slots_out || !tokens)) return fail(PA_ERR_INVALID, "pa_seq_append_tokens: NULL array");
+    if (!cow_out || !n_cow_out) return fail(PA_ERR_INVALID, "pa_seq_append_tokens: cow_out/n_cow_out is NULL");
+    auto it = a->seqs.find(seq_id);
+    if (it == a->seqs.end())
+        return fail(PA_ERR_INVALID, "pa_seq_append_tokens: unknown sequence %lld", (long long)seq_id);
+    Seq& s = it->second;
+    if (s.swapped)
+        return fail(PA_ERR_INVALID, "pa_seq_append_tokens: sequence %lld is swapped out", (long long)seq_id);
+    const int64_t need = a->blocks_needed(s, n_tokens, 0);
+    if (need > a->freeq.count) {
+        a->exhaustion_events += 1;
+        return fail(PA_ERR_NO_BLOCKS, "pa_seq_append_tokens: sequence %lld needs %lld blocks, %lld free",
+                    (long long)seq_id, (long long)need, (long long)a->freeq.count);
+    }
+    *n_cow_out = a->append_fit(s, n_tokens, slots_out, cow_out, tokens);
+    return PA_OK;
+}
+
+int pa_seq_add_prompt(pa_allocator* a, int64_t seq_id, const int32_t* tokens, int32_t n_tokens,
+                      int32_t* n_cached_out, int64_t* slots_out) {
+    pagedkv::clear_error();
+    if (!a) return fail(PA_ERR_INVALID, "pa_seq_add_prompt: NULL allocator");
+    if (n_tokens < 0) return fail(PA_ERR_INVALID, "pa_seq_add_prompt: n_tokens=%d < 0", n_tokens);
+    if (!n_cached_out || (n_tokens > 0 && !tokens))
+        return fail(PA_ERR_INVALID, "pa_seq_add_prompt: NULL argument");
+    if (a->seqs.count(seq_id)) return fail(PA_ERR_INVALID, "pa_seq_add_prompt: sequence %lld exists", (long long)seq_id);
+    const int64_t bs = a->block_size;
+    // the longest run of registered blocks from block 0 whose content is this prompt's prefix
+    std::vector<int32_t> hits;
+    int64_t chain = -1, hit_free = 0;
+    std::vector<int32_t> blk(bs);
+    for (int64_t k = 0; (k + 1) * bs <= n_tokens; ++k) {
+        blk.assign(tokens + k * bs, tokens + (k + 1) * bs);
+        auto it = a->node_of_key.find(BlockKey{chain, blk});
+        if (it == a->node_of_key.end()) break;
+        const int32_t b = a->nodes.find(it->second)->second.block;
+        if (b < 0) break;
+        hits.push_back(b);
+        hit_free += a->refcount[b] == 0;
+        chain = it->second;
+    }
+    const int64_t n_cached = static_cast<int64_t>(hits.size()) * bs;
+    const int64_t need = (n_tokens - n_cached + bs - 1) / bs;   // fresh blocks for the rest
+    if (n_tokens - n_cached > 0 && !slots_out) return fail(PA_ERR_INVALID, "pa_seq_add_prompt: slots_out is NULL");
+    if (need > a->freeq.count - hit_free) {
+        a->exhaustion_events += 1;
+        return fail(PA_ERR_NO_BLOCKS, "pa_seq_add_prompt: sequence %lld needs %lld blocks, %lld free",
+                    (long long)seq_id, (long long)need, (long long)(a->freeq.count - hit_free));
+    }
+    Seq s;
+    for (int32_t b : hits) {
+        if (a->refcount[b] == 0) a->freeq.remove(b);   // a cached block back in use
+        a->refcount[b] += 1;
+        s.blocks.push_back(b);
+    }
+    s.n = n_cached;
+    s.chain = chain;
+    if (chain >= 0) a->nodes.find(chain)->second.refs += 1;
+    a->cache_hit_blocks += static_cast<int64_t>(hits.size());
+    int64_t cow[2];
+    a->append_fit(s, n_tokens - n_cached, slots_out, cow, tokens + n_cached);   // starts a fresh block: no copy
+    a->seqs.emplace(seq_id, std::move(s));
+    *n_cached_out = static_cast<int32_t>(n_cached);
     return PA_OK;
 }
 
@@ -233,10 +443,10 @@ int pa_batch_append(pa_allocator* a, const int64_t* seq_ids, const int32_t* n_to
         }
         need += a->blocks_needed(s, n_tokens[i], drop);
     }
-    if (need > a->count) {
+    if (need > a->freeq.count) {
         a->exhaustion_events += 1;
         return fail(PA_ERR_NO_BLOCKS, "pa_batch_append: batch needs %lld blocks, %lld free",
-                    (long long)need, (long long)a->count);
+                    (long long)need, (long long)a->freeq.count);
     }
     int64_t off = 0;
     int32_t ncow = 0;
@@ -255,8 +465,9 @@ int pa_seq_fork(pa_allocator* a, int64_t parent, int64_t child) {
     if (it == a->seqs.end()) return fail(PA_ERR_INVALID, "pa_seq_fork: unknown parent %lld", (long long)parent);
     if (a->seqs.count(child)) return fail(PA_ERR_INVALID, "pa_seq_fork: child %lld exists", (long long)child);
     if (it->second.swapped) return fail(PA_ERR_INVALID, "pa_seq_fork: parent %lld is swapped out", (long long)parent);
-    Seq c = it->second;  // copy of the block list and token count
+    Seq c = it->second;  // copy of the block list, token count and content chain
     for (int32_t b : c.blocks) a->refcount[b] += 1;
+    if (c.chain >= 0) a->nodes.find(c.chain)->second.refs += 1;
     a->seqs.emplace(child, std::move(c));
     return PA_OK;
 }
@@ -274,6 +485,7 @@ int pa_seq_free(pa_allocator* a, int64_t seq_id) {
         for (int32_t b : it->second.blocks)
             if (--a->refcount[b] == 0) a->push(b);
     }
+    a->untrack(it->second);
     a->seqs.erase(it);
     return PA_OK;
 }
@@ -321,7 +533,7 @@ int pa_alloc_stats(const pa_allocator* a, pa_alloc_stats_t* out) {
     const int64_t bs = a->block_size;
     for (const auto& kv : a->seqs)
         if (!kv.second.swapped) waste += (kv.second.n + bs - 1) / bs * bs - kv.second.n;
-    out->free_blocks = a->count;
+    out->free_blocks = a->freeq.count;
     out->used_blocks = used;
     out->total_refs = refs;
     out->exhaustion_events = a->exhaustion_events;
@@ -332,6 +544,16 @@ int pa_alloc_stats(const pa_allocator* a, pa_alloc_stats_t* out) {
     out->host_free_blocks = a->host_free.count;
     out->host_used_blocks = host_used;
     out->swapped_seqs = a->swapped_seqs;
+    out->cached_blocks = a->cached_blocks;
+    out->cache_hit_blocks = a->cache_hit_blocks;
+    out->cache_evictions = a->cache_evictions;
+    return PA_OK;
+}
+
+int pa_alloc_dump_cached(const pa_allocator* a, int32_t* registered) {
+    pagedkv::clear_error();
+    if (!a || !registered) return fail(PA_ERR_INVALID, "pa_alloc_dump_cached: NULL argument");
+    for (int32_t b = 0; b < a->num_blocks; ++b) registered[b] = a->node_of_block[b] >= 0 ? 1 : 0;
     return PA_OK;
 }
 
@@ -339,8 +561,9 @@ int pa_alloc_dump(const pa_allocator* a, int32_t* refcounts, int32_t* free_order
     pagedkv::clear_error();
     if (!a || !refcounts || !free_order || !n_free) return fail(PA_ERR_INVALID, "pa_alloc_dump: NULL argument");
     std::memcpy(refcounts, a->refcount.data(), a->refcount.size() * sizeof(int32_t));
-    for (int64_t i = 0; i < a->count; ++i) free_order[i] = a->ring[(a->head + i) % a->num_blocks];
-    *n_free = static_cast<int32_t>(a->count);
+    int64_t i = 0;
+    for (int32_t b = a->freeq.head; b >= 0; b = a->freeq.nxt[b]) free_order[i++] = b;
+    *n_free = static_cast<int32_t>(a->freeq.count);
     return PA_OK;
 }
 
@@ -450,10 +673,10 @@ int pa_swap_in(pa_allocator* a, const int64_t* seq_ids, int32_t n_seqs, int64_t*
     if (int rc = collect(a, "pa_swap_in", seq_ids, n_seqs, true, ss, distinct)) return rc;
     if (distinct > max_pairs || (distinct > 0 && !pairs_out))
         return fail(PA_ERR_INVALID, "pa_swap_in: %lld pairs do not fit the buffer of %d", (long long)distinct, max_pairs);
-    if (distinct > a->count) {
+    if (distinct > a->freeq.count) {
         a->exhaustion_events += 1;
         return fail(PA_ERR_NO_BLOCKS, "pa_swap_in: %lld blocks needed, %lld free", (long long)distinct,
-                    (long long)a->count);
+                    (long long)a->freeq.count);
     }
     *n_pairs_out = move_refs(
         ss, a->host_refcount, a->refcount, [a](int32_t b) { a->host_free.push(b); },

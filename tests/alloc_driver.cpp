@@ -4,6 +4,7 @@
 //   create N BS perm...      add S      append S n      batch k S1 n1 ... Sk nk
 //   fork P C                 free S     table S max     dump
 //   host NH                  swapout k S1 ... Sk        swapin k S1 ... Sk
+//   prompt S k t1 ... tk     appendt S k t1 ... tk
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -106,13 +107,32 @@ int main() {
             if (rc == 0)
                 for (int i = 0; i < np; ++i) std::printf(" %lld:%lld", (long long)pairs[2 * i], (long long)pairs[2 * i + 1]);
             std::printf("\n");
+        } else if (o == "prompt" || o == "appendt") {
+            long long s;
+            int k;
+            std::scanf("%lld %d", &s, &k);
+            std::vector<int32_t> toks(k + 1);
+            for (int i = 0; i < k; ++i) std::scanf("%d", &toks[i]);
+            std::vector<int64_t> slots(k + 1);
+            int32_t nc = 0, ncow = 0;
+            int64_t cow[2];
+            if (o == "prompt") rc = pa_seq_add_prompt(a, s, toks.data(), k, &nc, slots.data());
+            else rc = pa_seq_append_tokens(a, s, toks.data(), k, slots.data(), cow, &ncow);
+            std::printf("%s %d", op, rc);
+            if (rc == 0) {
+                const int ns = o == "prompt" ? k - nc : k;
+                std::printf(" cached %d", nc);
+                for (int i = 0; i < ns; ++i) std::printf(" %lld", (long long)slots[i]);
+            }
+            std::printf("\n");
         } else if (o == "dump") {
             pa_alloc_stats_t st;
             pa_alloc_stats(a, &st);
-            std::printf("stats %lld %lld %lld %lld %lld %lld %lld %lld %lld\n", (long long)st.free_blocks,
+            std::printf("stats %lld %lld %lld %lld %lld %lld %lld %lld %lld %lld %lld %lld\n", (long long)st.free_blocks,
                         (long long)st.used_blocks, (long long)st.total_refs, (long long)st.exhaustion_events,
                         (long long)st.waste_slots, (long long)st.num_seqs, (long long)st.host_free_blocks,
-                        (long long)st.host_used_blocks, (long long)st.swapped_seqs);
+                        (long long)st.host_used_blocks, (long long)st.swapped_seqs, (long long)st.cached_blocks,
+                        (long long)st.cache_hit_blocks, (long long)st.cache_evictions);
         }
     }
     pa_alloc_destroy(a);

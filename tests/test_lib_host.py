@@ -117,9 +117,12 @@ def compare(c: pk.Allocator, o: OAlloc):
     assert list(free) == ofree
     st, ost = c.stats(), o.stats()
     assert (st["free_blocks"], st["used_blocks"], st["total_refs"], st["exhaustion_events"], st["waste_slots"],
-            st["host_free_blocks"], st["host_used_blocks"], st["swapped_seqs"]) == \
+            st["host_free_blocks"], st["host_used_blocks"], st["swapped_seqs"], st["cached_blocks"],
+            st["cache_hit_blocks"], st["cache_evictions"]) == \
         (ost["free"], ost["used"], ost["refs"], ost["exhaustion_events"], ost["waste_slots"],
-         ost["host_free"], ost["host_used"], ost["swapped_seqs"])
+         ost["host_free"], ost["host_used"], ost["swapped_seqs"], ost["cached_blocks"],
+         ost["cache_hit_blocks"], ost["cache_evictions"])
+    assert list(c.dump_cached()) == o.dump_cached()
     if getattr(c, "num_host_blocks", 0):
         href, hfree = c.dump_host()
         assert (list(href), list(hfree)) == o.dump_host()
@@ -150,6 +153,9 @@ def run_both(c, o, op, *args):
             elif op in ("swap_out", "swap_in"):
                 r = getattr(impl, op)(*args)
                 res.append(("ok", [tuple(map(int, p)) for p in r]))
+            elif op == "add_prompt":
+                n, sl = impl.add_prompt(*args)
+                res.append(("ok", int(n), list(map(int, sl))))
             else:
                 getattr(impl, op)(*args)
                 res.append(("ok",))
@@ -199,6 +205,52 @@ def test_allocator_with_swapping_matches_oracle_random(seed):
             s = int(rng.choice(live)); run_both(c, o, "free", s); live.remove(s)
         else:
             run_both(c, o, "set_host_blocks", NH)        # refused while anything is swapped out
+        compare(c, o)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_allocator_with_prefix_cache_matches_oracle_random(seed):
+    """Random traces of prompts drawn from a few shared system prompts plus suffixes, appends
+    with and without token ids, forks, frees, swaps and batches, on pools small enough that
+    registered free blocks get evicted; outcomes, pairs, slots, cached-token counts and the
+    whole state (including which blocks are registered) must agree after every operation."""
+    rng = np.random.default_rng(3000 + seed)
+    N, NH = int(rng.integers(10, 48)), int(rng.integers(4, 24))
+    bs = int(rng.choice([1, 2, 4, 8]))
+    order = rng.permutation(N)
+    c, o = pk.Allocator(N, bs, order), OAlloc(N, bs, order)
+    run_both(c, o, "set_host_blocks", NH)
+    systems = [[int(x) for x in rng.integers(0, 4, size=int(rng.integers(1, 5 * bs)))] for _ in range(3)]
+    live, nid = [], 0
+    for _ in range(500):
+        r = rng.random()
+        res = [x for x in live if not o.is_swapped(x)]
+        swp = [x for x in live if o.is_swapped(x)]
+        if r < 0.25 or not live:
+            toks = systems[int(rng.integers(0, 3))] + [int(x) for x in rng.integers(0, 4, size=int(rng.integers(0, 3 * bs)))]
+            if run_both(c, o, "add_prompt", nid, toks)[0] == "ok":
+                live.append(nid)
+            nid += 1
+        elif r < 0.5 and res:
+            s, k = int(rng.choice(res)), int(rng.integers(0, 2 * bs + 1))
+            ids = [int(x) for x in rng.integers(0, 4, size=k)] if rng.random() < 0.85 else None
+            run_both(c, o, "append", s, k, ids)
+        elif r < 0.58 and res:
+            p = int(rng.choice(res))
+            if run_both(c, o, "fork", p, nid)[0] == "ok":
+                live.append(nid)
+            nid += 1
+        elif r < 0.62 and len(res) > 1:
+            ids = [int(x) for x in rng.choice(res, size=2, replace=False)]
+            run_both(c, o, "batch", ids, [int(x) for x in rng.integers(0, bs + 1, size=2)])
+        elif r < 0.72:
+            op, pool = ("swap_out", res) if rng.random() < 0.5 else ("swap_in", swp)
+            if pool:
+                run_both(c, o, op, [int(x) for x in rng.choice(pool, size=min(2, len(pool)), replace=False)])
+        elif r < 0.97:
+            s = int(rng.choice(live)); run_both(c, o, "free", s); live.remove(s)
+        else:
+            run_both(c, o, "add_prompt", int(rng.choice(live)), [1])   # existing id -> invalid in both
         compare(c, o)
 
 
@@ -302,6 +354,12 @@ def _driver_script(seed):
         if live and r > 0.9 and rng.random() < 0.6:   # swap a random set (either state)
             ids = rng.choice(live, size=min(len(live), int(rng.integers(1, 4))), replace=False)
             lines.append(f"{'swapout' if rng.random() < 0.5 else 'swapin'} {len(ids)} " + " ".join(map(str, ids)))
+        elif r > 0.8 and rng.random() < 0.5:            # a prompt from a shared prefix, or appended ids
+            toks = [1, 2, 3, 4, 5, 6][: int(rng.integers(1, 7))] + [int(x) for x in rng.integers(0, 3, size=int(rng.integers(0, 5)))]
+            if live and rng.random() < 0.4:
+                lines.append(f"appendt {int(rng.choice(live))} {len(toks)} " + " ".join(map(str, toks)))
+            else:
+                lines.append(f"prompt {nid} {len(toks)} " + " ".join(map(str, toks))); live.append(nid); nid += 1
         elif r < 0.15 or not live:
             lines.append(f"add {nid}"); live.append(nid); nid += 1
         elif r < 0.5:
@@ -360,10 +418,15 @@ def test_allocator_under_asan_ubsan(tmp_path):
                 elif f[0] in ("swapout", "swapin"):
                     ids = [int(x) for x in f[2:]]
                     (o.swap_out if f[0] == "swapout" else o.swap_in)(ids)
+                elif f[0] == "prompt":
+                    o.add_prompt(int(f[1]), [int(x) for x in f[3:]])
+                elif f[0] == "appendt":
+                    o.append(int(f[1]), int(f[2]), [int(x) for x in f[3:]])
             except (NoBlocks, InvalidOp):
                 pass
             if f[0] == "dump":
                 s = o.stats()
                 want.append(f"stats {s['free']} {s['used']} {s['refs']} {s['exhaustion_events']} "
-                            f"{s['waste_slots']} {len(o.seqs)} {s['host_free']} {s['host_used']} {s['swapped_seqs']}")
+                            f"{s['waste_slots']} {len(o.seqs)} {s['host_free']} {s['host_used']} {s['swapped_seqs']} "
+                            f"{s['cached_blocks']} {s['cache_hit_blocks']} {s['cache_evictions']}")
         assert got == want

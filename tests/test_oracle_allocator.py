@@ -275,3 +275,126 @@ def test_swap_preserves_every_sequence_contents(seed):
             got = [int(pool[q.blocks[j // bs], j % bs]) for j in range(q.n)]
             assert got == want[s], (s, q)
     assert swaps > 20
+
+
+# --------------------------------------------------------------------------- prefix caching
+
+def test_hand_traced_prefix_cache():
+    """6 blocks of 2 slots, free order [4, 1, 5, 0, 2, 3].  Worked out by hand from the rules:
+    a full block is registered under the whole token prefix up to its end; a prompt takes the
+    registered blocks of its block-boundary prefixes from block 0 on, up to the first miss; a
+    registered block at refcount 0 stays registered until the free queue hands it out."""
+    a = Allocator(6, 2, [4, 1, 5, 0, 2, 3])
+    n, slots = a.add_prompt(1, [7, 8, 9, 10, 11])      # nothing cached: blocks 4, 1, 5
+    assert n == 0 and slots == [8, 9, 2, 3, 10]
+    assert a.dump_cached() == [0, 1, 0, 0, 1, 0]       # (7,8) -> 4, (7,8,9,10) -> 1
+    n, slots = a.add_prompt(2, [7, 8, 9, 10, 12, 13])  # two hits, then block 0 for (12, 13)
+    assert n == 4 and slots == [0, 1]
+    assert a.dump() == ([1, 2, 0, 0, 2, 1], [2, 3])
+    assert a.dump_cached() == [1, 1, 0, 0, 1, 0]       # (7,8,9,10,12,13) -> 0
+    n, slots = a.add_prompt(3, [8, 7, 9, 10])          # (8, 7) is not (7, 8): no hit at all
+    assert n == 0 and slots == [4, 5, 6, 7]
+    assert a.dump() == ([1, 2, 1, 1, 2, 1], [])
+    a.release(2)                                       # 4, 1, 0 lose a reference; 0 is free
+    a.release(1)                                       # then 4, 1, 5: 4 and 1 free
+    assert a.dump() == ([0, 0, 1, 1, 0, 0], [0, 4, 1, 5])
+    assert a.dump_cached() == [1, 1, 1, 1, 1, 0]       # free blocks keep their registration
+    n, slots = a.add_prompt(4, [7, 8, 9, 10, 12])      # hits 4 and 1 out of the free queue
+    assert n == 4 and slots == [0]                     # head 0 is handed out: (7,8,9,10,12,13) evicted
+    assert a.dump() == ([1, 1, 1, 1, 1, 0], [5])
+    assert a.dump_cached() == [0, 1, 1, 1, 1, 0]
+    st = a.stats()
+    assert (st["cached_blocks"], st["cache_hit_blocks"], st["cache_evictions"]) == (4, 4, 1)
+    a.append(4, 1)                                     # ids unknown from now on
+    a.append(4, 2, [1, 2])                             # block 0 fills: nothing registered
+    assert a.dump_cached() == [0, 1, 1, 1, 1, 0]
+
+
+def test_prompt_exhaustion_leaves_state_unchanged():
+    a = Allocator(3, 2)
+    a.add_prompt(0, [1, 2, 3, 4])                      # blocks 0, 1 registered
+    a.release(0)                                       # both free but registered
+    snap = (a.dump(), a.dump_cached(), a.stats())
+    with pytest.raises(NoBlocks):
+        a.add_prompt(1, [1, 2, 3, 4, 5, 6, 7, 8])      # 2 hits + 2 fresh > 1 other free block
+    assert (a.dump(), a.dump_cached()) == snap[:2] and a.stats()["exhaustion_events"] == 1
+    n, _ = a.add_prompt(1, [1, 2, 3, 4, 5, 6])         # 2 hits + 1 fresh fits
+    assert n == 4
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_prefix_cache_serves_only_equal_prefixes(seed):
+    """The definition of a cache hit, checked by simulation: every slot of the simulated cache
+    holds the identity of the whole token prefix through that token (the K/V of a token
+    depends on all tokens before it).  Tokens are written only at the slots the allocator
+    returns (a prompt's cached tokens are not written); copy-on-write and swap pairs copy
+    whole blocks.  After every operation each sequence read through its table must give the
+    prefix identities of exactly its own tokens.  Keying blocks by their own tokens only, a
+    hit past a miss or a registration that outlives a block being handed out fail it."""
+    rng = np.random.default_rng(900 + seed)
+    N, NH, bs = 40, 24, int(rng.choice([1, 2, 4]))
+    a = Allocator(N, bs, rng.permutation(N))
+    a.set_host_blocks(NH)
+    ident = {}
+    pid = lambda toks: ident.setdefault(tuple(toks), len(ident))
+    dev = np.full((N, bs), -1, np.int64)
+    host = np.full((NH, bs), -1, np.int64)
+    want = {}                                          # sequence -> its token ids (None: unknown)
+    vals = {}                                          # sequence -> expected slot values
+    systems = [list(rng.integers(0, 3, size=int(rng.integers(1, 4 * bs + 1)))) for _ in range(3)]
+    live, nid, hits = [], 0, 0
+    for _ in range(700):
+        r = rng.random()
+        resident = [s for s in live if not a.seqs[s].swapped]
+        swapped = [s for s in live if a.seqs[s].swapped]
+        try:
+            if r < 0.25 or not live:
+                toks = list(systems[int(rng.integers(0, 3))]) + list(rng.integers(0, 3, size=int(rng.integers(0, 2 * bs))))
+                n_cached, slots = a.add_prompt(nid, toks)
+                hits += n_cached
+                for j, sl in enumerate(slots):
+                    dev[sl // bs, sl % bs] = pid(toks[: n_cached + j + 1])
+                want[nid] = list(toks)
+                vals[nid] = [pid(toks[: j + 1]) for j in range(len(toks))]
+                live.append(nid); nid += 1
+            elif r < 0.5 and resident:
+                s = int(rng.choice(resident)); k = int(rng.integers(1, 2 * bs + 1))
+                known = want[s] is not None and rng.random() < 0.9
+                ids = [int(x) for x in rng.integers(0, 3, size=k)]
+                slots, cow = a.append(s, k, ids if known else None)
+                for src, dst in cow:
+                    dev[dst] = dev[src]
+                if known:
+                    want[s] = want[s] + ids
+                    new = [pid(want[s][: len(vals[s]) + j + 1]) for j in range(k)]
+                else:
+                    want[s] = None
+                    new = [10_000_000 + len(ident) + j for j in range(k)]   # unknown content
+                    ident[("unknown", len(ident))] = len(ident)
+                for sl, v in zip(slots, new):
+                    dev[sl // bs, sl % bs] = v
+                vals[s] = vals[s] + new
+            elif r < 0.6 and resident:
+                p = int(rng.choice(resident)); a.fork(p, nid)
+                want[nid] = None if want[p] is None else list(want[p]); vals[nid] = list(vals[p])
+                live.append(nid); nid += 1
+            elif r < 0.7 and resident:
+                ids = [int(x) for x in rng.choice(resident, size=min(len(resident), 2), replace=False)]
+                for d, h in a.swap_out(ids):
+                    host[h] = dev[d]
+            elif r < 0.8 and swapped:
+                ids = [int(x) for x in rng.choice(swapped, size=min(len(swapped), 2), replace=False)]
+                for h, d in a.swap_in(ids):
+                    dev[d] = host[h]
+            elif live:
+                s = int(rng.choice(live)); a.release(s); live.remove(s)
+        except NoBlocks:
+            pass
+        check_pool_invariants(a)
+        for s in live:
+            q = a.seqs[s]
+            pool = host if q.swapped else dev
+            assert [int(pool[q.blocks[j // bs], j % bs]) for j in range(q.n)] == vals[s], s
+        for key, b in a.cache.items():                 # registered blocks hold their prefix
+            assert [int(x) for x in dev[b]] == [pid(key[: len(key) - bs + i + 1]) for i in range(bs)]
+    assert hits > 0
