@@ -24,6 +24,7 @@ timed on a bounded sample of the same per-request work on the host.
     python bench.py [--steps K] [--warmup W] [--gpus 1]
     python bench.py --workload {ragged_prefix,long_context,sweep}   # other workloads' decode rates
     python bench.py --workload swap     # preemption: swap-out / swap-in rates over the host link
+    python bench.py --workload prefix_cache   # prompts through the prefix cache vs without it
 """
 
 import argparse
@@ -407,8 +408,8 @@ def run_swap(args):
     requests without the shared prefix are swapped out to a pinned host pool and back in,
     `steps` times.  Timed with HIP events on the launch stream: each pa_swap_blocks launch
     (device -> host, then host -> device); on the host: the allocator's pa_swap_out /
-    pa_swap_in.  For reference, the copy engine's rate for one contiguous buffer of the same
-    size in each direction (torch copy_ between device and pinned memory)."""
+    pa_swap_in.  For reference, the HIP runtime's own rate for one contiguous buffer of the
+    same size in each direction (torch copy_ between device and pinned memory)."""
     import numpy as np
     import torch
 
@@ -469,7 +470,7 @@ def run_swap(args):
             host_in_us.append((t3 - t2) * 1e6)
             npairs = len(p_out)
     nbytes = 2 * npairs * block
-    # the copy engine on one contiguous buffer of the same size, each direction
+    # the runtime's copy of one contiguous buffer of the same size, each direction
     dbuf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     hbuf = torch.empty(nbytes, dtype=torch.uint8).pin_memory()
     ce = {"d2h": [], "h2d": []}
@@ -492,8 +493,84 @@ def run_swap(args):
             "kernel_us_median": round(m, 2), "gbps": round(nbytes / m / 1e3, 2),
             "pct_of_host_link_peak": round(100 * nbytes / m / 1e3 / HOST_LINK_PEAK_GBPS, 1),
             "host_link_peak_gbps": HOST_LINK_PEAK_GBPS,
-            "copy_engine_contiguous_gbps": round(nbytes / med(cus) / 1e3, 2),
+            "runtime_copy_contiguous_gbps": round(nbytes / med(cus) / 1e3, 2),
             "allocator_us_median": round(med(hus), 1), "steps": args.steps,
+        }), flush=True)
+
+
+def run_prefix_cache(args):
+    """The ragged batch's prompts (256 requests, bf16, block 16, 32 q / 8 KV heads, d 128;
+    64 of them start with one 1024-token system prompt) arriving one after another, with
+    synthetic token ids, through the prefix cache (pa_seq_add_prompt) and without it
+    (pa_seq_add + pa_seq_append).  Reported per run: host allocator time per prompt, prompt
+    tokens whose K/V the cache already held, K/V bytes written, and the device time of the
+    prefill write (one pa_kv_write of every row that has to be written, HIP events)."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_408_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    import paged_kv_cache_408_amd as pk
+    import workloads
+
+    dev = torch.device("cuda:0")
+    w = workloads.ragged_prefix(bs=16)
+    lens, _ = workloads.ragged_lengths(w.seed_index)
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(408_200)))
+    system = g.integers(0, 32000, size=1024).astype(np.int32)
+    prompts = []
+    for b in range(w.B):
+        L = int(lens[b]) - 1                       # the decode token comes later
+        own = g.integers(0, 32000, size=L).astype(np.int32)
+        prompts.append(np.concatenate([system, own[1024:]]) if b < 64 else own)
+    total = int(sum(len(p) for p in prompts))
+    row_bytes = 2 * w.Hkv * w.d * 2                # K and V of one token, bf16
+    n_blocks = sum(-(-len(p) // w.bs) for p in prompts) + 256   # room for the run without sharing
+    order = np.random.Generator(np.random.PCG64(np.random.SeedSequence(408_201))).permutation(n_blocks)
+    kc = torch.zeros((n_blocks, w.Hkv, w.bs, w.d), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    kv_rows = workloads.device_normal(w, "k_pre", (total, w.Hkv, w.d))
+    for cached in (True, False):
+        host_us, slots_all, n_hit = [], [], 0
+        for rep_i in range(max(args.warmup, 1) + args.steps):
+            al = pk.Allocator(n_blocks, w.bs, order)
+            slots_all, n_hit, t_total = [], 0, 0.0
+            for b, toks in enumerate(prompts):
+                t0 = time.perf_counter()
+                if cached:
+                    nc, sl = al.add_prompt(b, toks)
+                else:
+                    al.add(b)
+                    sl, _ = al.append(b, len(toks))
+                    nc = 0
+                t_total += time.perf_counter() - t0
+                n_hit += nc
+                slots_all.append(sl)
+            host_us.append(t_total * 1e6 / w.B)
+        slots = torch.from_numpy(np.concatenate(slots_all)).to(dev)
+        n_write = slots.numel()
+        kr, vr = kv_rows[:n_write], kv_rows[:n_write]
+        ev = []
+        for rep_i in range(max(args.warmup, 1) + args.steps):
+            a, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            pk.pa_kv_write(kr, vr, slots, kc, vc)
+            b2.record()
+            ev.append((a, b2))
+        torch.cuda.synchronize()
+        wr_us = sorted(a.elapsed_time(b2) * 1e3 for a, b2 in ev[max(args.warmup, 1):])
+        st = al.stats()
+        print(json.dumps({
+            "workload": f"{w.name} prompts {'with' if cached else 'without'} the prefix cache",
+            "metric": "prefill K/V written", "unit": "bytes",
+            "requests": w.B, "prompt_tokens": total, "tokens_from_cache": int(n_hit),
+            "tokens_written": int(n_write), "kv_bytes_written": int(n_write * row_bytes),
+            "kv_bytes_saved": int(n_hit * row_bytes),
+            "used_blocks": st["used_blocks"], "cached_blocks": st["cached_blocks"],
+            "allocator_us_per_prompt": round(sorted(host_us)[len(host_us) // 2], 2),
+            "prefill_write_us": round(wr_us[len(wr_us) // 2], 2), "steps": args.steps,
         }), flush=True)
 
 
@@ -501,7 +578,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", default="llama3_8b",
-                    choices=["llama3_8b", "ragged_prefix", "long_context", "sweep", "swap"],
+                    choices=["llama3_8b", "ragged_prefix", "long_context", "sweep", "swap", "prefix_cache"],
                     help="llama3_8b: the benchmark; the others print per-setting measurements instead")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
@@ -527,6 +604,9 @@ def main():
         return
     if args.workload == "swap":
         run_swap(args)
+        return
+    if args.workload == "prefix_cache":
+        run_prefix_cache(args)
         return
     if args.workload != "llama3_8b":
         run_workload(args.workload, args)

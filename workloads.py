@@ -237,3 +237,65 @@ def device_normal(w: Workload, what: str, shape, layer: int = 0, device="cuda"):
     x = torch.randn(shape, generator=g, device=device, dtype=torch.float32) * w.std
     fmt = w.q_fmt if what == "q" else w.in_fmt
     return x if fmt == "f32" else x.to(torch.bfloat16)
+
+
+# --------------------------------------------------------------------------- prompts
+
+@dataclass
+class PromptWorkload:
+    """Requests arriving with token-id prompts, some starting with one of a few shared
+    system prompts, for prefix caching.  `finished` requests are released right after
+    their prompt is in (their blocks stay registered while free)."""
+    name: str
+    Hq: int
+    Hkv: int
+    d: int
+    bs: int
+    std: float
+    prompts: list          # token ids per request
+    finished: list         # requests released after their prompt is in
+    step_tokens: list      # the decode token of each request
+    num_blocks: int
+    free_order: np.ndarray
+    seed_index: int = 0
+
+
+def prompt_workload(n_req=16, systems=(80, 160, 48), suffix_max=60, Hq=32, Hkv=8, d=128, bs=16,
+                    finished_every=4, seed_index=7, name=None) -> PromptWorkload:
+    """Request i starts with system prompt i % len(systems) and adds a private suffix of
+    0..suffix_max tokens; token ids uniform in [0, 1000).  Every `finished_every`-th request
+    is released after its prompt.  The pool holds every request's blocks without sharing
+    (so a run without the cache fits too), in a seeded order."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(408_000 + seed_index)))
+    sys_toks = [[int(x) for x in g.integers(0, 1000, size=n)] for n in systems]
+    prompts, step = [], []
+    for i in range(n_req):
+        suffix = [int(x) for x in g.integers(0, 1000, size=int(g.integers(0, suffix_max + 1)))]
+        prompts.append(sys_toks[i % len(sys_toks)] + suffix)
+        step.append(int(g.integers(0, 1000)))
+    finished = [i for i in range(n_req) if finished_every and i % finished_every == finished_every - 1]
+    n = sum(-(-(len(p) + 1) // bs) for p in prompts) + 4
+    return PromptWorkload(name or f"prompts{n_req}_bs{bs}_d{d}", Hq=Hq, Hkv=Hkv, d=d, bs=bs, std=0.5,
+                          prompts=prompts, finished=finished, step_tokens=step, num_blocks=n,
+                          free_order=_perm(seed_index, n), seed_index=seed_index)
+
+
+def prefix_kv(token_ids, Hkv: int, d: int, std: float, seed_index: int, fmt: str = "bf16"):
+    """K and V rows [n, Hkv, d] for a token sequence, each row a function of the whole
+    token prefix through it (as a model's K/V are): row j is drawn from a generator seeded
+    by the seed index and a 64-bit FNV-1a digest of token_ids[:j+1].  Equal prefixes give
+    equal rows, different prefixes different ones."""
+    h = 14695981039346656037
+    ks, vs = [], []
+    for t in token_ids:
+        for i in range(4):
+            h ^= (int(t) >> (8 * i)) & 0xFF
+            h = (h * 1099511628211) & 0xFFFFFFFFFFFFFFFF
+        g = np.random.Generator(np.random.PCG64([408_000 + seed_index, h]))
+        x = g.standard_normal(size=(2, Hkv, d), dtype=np.float32) * np.float32(std)
+        ks.append(x[0])
+        vs.append(x[1])
+    if not ks:
+        z = np.zeros((0, Hkv, d), np.float32)
+        return _round_storage(z, fmt), _round_storage(z, fmt)
+    return _round_storage(np.stack(ks), fmt), _round_storage(np.stack(vs), fmt)
