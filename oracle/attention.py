@@ -122,6 +122,46 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, scale: float, block_size
     return out
 
 
+def prefill(q, k_cache, v_cache, block_tables, seq_lens, query_start, scale: float, block_size: int,
+            fmt: str, q_fmt: str, k_scale=None, v_scale=None):
+    """Attention of several new tokens per request through the block table, causal.
+    Returns float64 [T, Hq, d].
+
+    The pages' step before decode: a prompt's K/V are computed once and stored ("KV Cache
+    Management", "Why Does This Exist?": the first 1,000 tokens' keys and values are saved
+    as they are calculated), and every token attends to every token before it ("KV Cache
+    Optimization and PagedAttention", first paragraph).  Readings: the new tokens' K/V are
+    written into the cache first (as for decode), so request b's L_b = seq_lens[b] cached
+    tokens include its n_b = query_start[b+1] - query_start[b] new ones, which are its last
+    n_b tokens; new token i sits at logical position L_b - n_b + i and sees positions
+    0..L_b - n_b + i (itself included), through one softmax.  Earlier tokens of the request
+    (a cached prefix or earlier chunks) are read from the cache like the new ones.
+
+    q: [T, Hq, d] stored, request b's rows query_start[b]..query_start[b+1]-1.
+    """
+    T, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    assert Hq % Hkv == 0
+    G = Hq // Hkv
+    qf = codecs.storage_to_f64(q, q_fmt)
+    scale = float(np.float32(scale))
+    out = np.zeros((T, Hq, d), dtype=np.float64)
+    B = len(seq_lens)
+    for b in range(B):
+        L = int(seq_lens[b])
+        q0, q1 = int(query_start[b]), int(query_start[b + 1])
+        n = q1 - q0
+        assert 0 <= n <= L
+        for g in range(Hkv):
+            K = gather(k_cache, block_tables[b], L, g, block_size, fmt, k_scale)
+            V = gather(v_cache, block_tables[b], L, g, block_size, fmt, v_scale)
+            for i in range(n):
+                pos = L - n + i                                # logical position of new token i
+                for h in range(g * G, (g + 1) * G):
+                    out[q0 + i, h] = attend(qf[q0 + i, h], K[: pos + 1], V[: pos + 1], scale)
+    return out
+
+
 def decode_splitk(q, k_cache, v_cache, block_tables, seq_lens, scale: float, block_size: int,
                   fmt: str, q_fmt: str, k_scale=None, v_scale=None, partition_tokens: int = 512):
     """The same result through partitions [P*p, min(P*(p+1), L)) of each request's tokens:
