@@ -25,6 +25,7 @@ timed on a bounded sample of the same per-request work on the host.
     python bench.py --workload {ragged_prefix,long_context,sweep}   # other workloads' decode rates
     python bench.py --workload swap     # preemption: swap-out / swap-in rates over the host link
     python bench.py --workload prefix_cache   # prompts through the prefix cache vs without it
+    python bench.py --workload prefill  # causal paged prefill: TFLOP/s against the bf16 matrix peak
 """
 
 import argparse
@@ -44,7 +45,7 @@ METRIC = "decode attention KV GB/s and % of HBM peak (GQA 32q/8kv d128, bf16)"
 HBM_PEAK_GBPS = 8000.0
 DECODE_KERNEL = "decode_mfma_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama3_8b_bf16_traffic.md")
-KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_408_amd", "csrc", "pagedkv.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_408_amd", "csrc", f) for f in ("pagedkv.hip", "pa_device.h")]
 
 
 def log(msg):
@@ -67,10 +68,13 @@ def kv_write_bytes(T, Hkv, d, e_in, e_cache):
 
 
 def kernel_source_hash():
-    """sha256 (first 16 hex digits) of the kernel source with comments and whitespace removed,
-    so that edits to comments alone do not mark the counters as stale."""
-    with open(KERNEL_SOURCE) as f:
-        text = f.read()
+    """sha256 (first 16 hex digits) of the decode kernel's sources (the kernel file and the
+    device helpers it includes) with comments and whitespace removed, so that edits to
+    comments alone do not mark the counters as stale."""
+    text = ""
+    for path in KERNEL_SOURCES:
+        with open(path) as f:
+            text += f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     text = re.sub(r"//[^\n]*", "", text)
     text = re.sub(r"\s+", "", text)
@@ -498,6 +502,71 @@ def run_swap(args):
         }), flush=True)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+
+
+def prefill_flops(ctx_lens, n_new, Hq, d):
+    """Algorithmic flops of causal prefill: for every (new token, visible position, q head)
+    one d-long dot product (q.k) and one d-long weighted add (p.v), 2 flops per element each."""
+    pairs = sum(n * c + n * (n + 1) // 2 for c, n in zip(ctx_lens, n_new))
+    return 4 * d * Hq * pairs
+
+
+def run_prefill(args):
+    """Causal paged prefill, Llama-3-8B shape (32 q / 8 KV heads, head_dim 128, bf16, block
+    16) on seeded synthetic K/V and q in a seeded-permutation pool: 16 requests x (1024 cached
+    + 1024 new tokens) (a chunk after a prefix-cache hit), and for the record 4 x 4096 new
+    tokens with no context and 1 x 16384.  pa_prefill timed with HIP events on the launch
+    stream; flops are the algorithmic ones (visible pairs only)."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_408_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    import paged_kv_cache_408_amd as pk
+
+    dev = torch.device("cuda:0")
+    Hq, Hkv, d, bs = 32, 8, 128, 16
+    for B, ctx, n in ((16, 1024, 1024), (4, 0, 4096), (1, 0, 16384)):
+        L = ctx + n
+        nb = -(-L // bs)
+        N = B * nb + 16
+        g = torch.Generator(device=dev)
+        g.manual_seed(408_300 + B)
+        kc = (torch.randn((N, Hkv, bs, d), generator=g, device=dev) * 0.5).to(torch.bfloat16)
+        vc = (torch.randn((N, Hkv, bs, d), generator=g, device=dev) * 0.5).to(torch.bfloat16)
+        perm = torch.from_numpy(np.random.Generator(np.random.PCG64(np.random.SeedSequence(408_301))).permutation(N)[: B * nb])
+        tab = perm.reshape(B, nb).to(torch.int32).to(dev)
+        lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+        qs = (torch.arange(B + 1, dtype=torch.int32) * n).to(dev)
+        q = (torch.randn((B * n, Hq, d), generator=g, device=dev) * 0.5).to(torch.bfloat16)
+        out = torch.empty_like(q)
+        call = lambda: pk.pa_prefill(out, q, kc, vc, tab, lens, qs, 1 / math.sqrt(d), bs, max_query_len=n, max_seq_len=L)
+        for _ in range(max(args.warmup, 1)):
+            call()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b2 in ev:
+            a.record()
+            call()
+            b2.record()
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b2) * 1e3 for a, b2 in ev)
+        med = us[len(us) // 2]
+        fl = prefill_flops([ctx] * B, [n] * B, Hq, d)
+        print(json.dumps({
+            "workload": f"prefill {B} x ({ctx} cached + {n} new), 32 q / 8 kv heads, d 128, bf16, block 16",
+            "metric": "causal prefill TFLOP/s", "unit": "TFLOP/s", "kernel": "prefill_kernel",
+            "us_median": round(med, 2), "us_min": round(us[0], 2), "algorithmic_flops": int(fl),
+            "tflops": round(fl / med / 1e6, 1), "pct_of_bf16_mfma_peak": round(100 * fl / med / 1e6 / MFMA_BF16_PEAK_TFLOPS, 2),
+            "steps": args.steps,
+        }), flush=True)
+        del kc, vc, q, out
+        torch.cuda.empty_cache()
+
+
 def run_prefix_cache(args):
     """The ragged batch's prompts (256 requests, bf16, block 16, 32 q / 8 KV heads, d 128;
     64 of them start with one 1024-token system prompt) arriving one after another, with
@@ -578,7 +647,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", default="llama3_8b",
-                    choices=["llama3_8b", "ragged_prefix", "long_context", "sweep", "swap", "prefix_cache"],
+                    choices=["llama3_8b", "ragged_prefix", "long_context", "sweep", "swap", "prefix_cache", "prefill"],
                     help="llama3_8b: the benchmark; the others print per-setting measurements instead")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
@@ -607,6 +676,9 @@ def main():
         return
     if args.workload == "prefix_cache":
         run_prefix_cache(args)
+        return
+    if args.workload == "prefill":
+        run_prefill(args)
         return
     if args.workload != "llama3_8b":
         run_workload(args.workload, args)

@@ -159,6 +159,42 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               const float* k_scale, const float* v_scale,
               void* workspace, int64_t workspace_bytes, int32_t partition_tokens, void* stream);
 
+/* ---------------------------------------------------------------- prefill attention
+ *
+ * Attention of several new tokens per request through the block table, causal: the step
+ * before decode, where a prompt's (or a chunk of it) keys and values are computed once and
+ * stored ("KV Cache Management", "Why Does This Exist?") and every token attends to every
+ * token before it ("KV Cache Optimization and PagedAttention", first paragraph).  The new
+ * tokens' K/V are written first (pa_kv_write), so for request b with L = seq_lens[b] cached
+ * tokens and n = query_start[b+1] - query_start[b] new ones (its last n tokens), new token i
+ * (q row query_start[b] + i) sits at logical position L - n + i and, for every query head h
+ * with KV head g = h / (num_q_heads / num_kv_heads):
+ *     out[query_start[b] + i][h][:] = sum_{j <= L - n + i} softmax_j(scale * <q_i, K_j>) V_j
+ * with K_j, V_j read through the table as in pa_decode.  Tokens before the new ones (a cached
+ * prefix, earlier chunks) are read from the cache like the new ones.  Scores, softmax and
+ * sums in float32 (the weights multiplied into V rounded to bf16, and the denominator sums
+ * those rounded weights); out rounded to nearest even.
+ *
+ *  out, q        device, [num_query_tokens][num_q_heads][head_dim] bf16
+ *  query_start   device, int32 [num_seqs + 1], non-decreasing, query_start[num_seqs] <=
+ *                num_query_tokens (rows of request b: query_start[b] .. query_start[b+1]-1)
+ *  seq_lens      device, int32 [num_seqs], L >= n
+ *  block_tables  device, int32 [num_seqs][max_blocks_per_seq]
+ *  max_query_len host upper bound of n; max_seq_len host upper bound of L
+ *
+ * Supported: bf16 q and cache, head_dim {64, 128}, block_size {8, 16, 32, 128},
+ * num_q_heads / num_kv_heads in {1, 4, 8}.  One kernel launch; no workspace.  A request whose
+ * query range is inconsistent (decreasing, negative or past num_query_tokens) is not written;
+ * one with n > L, n > max_query_len, L > max_seq_len or L > max_blocks_per_seq * block_size,
+ * or whose table holds an id outside [0, num_blocks) where positions are read, gets NaN in the
+ * rows of the query tiles that cover it (n > max_query_len: its first max_query_len rows). */
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_tables, const int32_t* seq_lens, const int32_t* query_start,
+               float scale, int32_t block_size, int32_t num_seqs, int64_t num_query_tokens,
+               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+               int32_t max_blocks_per_seq, int32_t max_query_len, int32_t max_seq_len,
+               int32_t q_dtype, int32_t cache_dtype, void* stream);
+
 /* ---------------------------------------------------------------- block copy
  *
  * Whole-block copies for copy-on-write ("KV Cache Optimization and PagedAttention", prose

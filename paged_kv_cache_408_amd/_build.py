@@ -29,8 +29,8 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}"]
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-munsafe-fp-atomics"]
-SOURCES = ["pagedkv.hip", "allocator.cpp", "pa_error.cpp"]
-HEADERS = ["pa_error.h"]
+SOURCES = ["pagedkv.hip", "prefill.hip", "allocator.cpp", "pa_error.cpp"]
+HEADERS = ["pa_error.h", "pa_device.h"]
 
 
 def _digest(src: str, flags) -> str:

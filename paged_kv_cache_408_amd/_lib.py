@@ -26,6 +26,7 @@ EXPORTED = [
     "pa_batch_append", "pa_seq_fork", "pa_seq_free", "pa_block_tables", "pa_alloc_stats",
     "pa_alloc_dump", "pa_alloc_set_host_blocks", "pa_swap_out", "pa_swap_in", "pa_seq_is_swapped",
     "pa_alloc_dump_host", "pa_swap_blocks", "pa_seq_add_prompt", "pa_seq_append_tokens", "pa_alloc_dump_cached",
+    "pa_prefill",
 ]
 
 
@@ -92,6 +93,8 @@ def load(path: str = LIB_PATH):
         "pa_seq_add_prompt": (ctypes.c_int, [P, I64, P, I32, P, P]),
         "pa_seq_append_tokens": (ctypes.c_int, [P, I64, P, I32, P, P, P]),
         "pa_alloc_dump_cached": (ctypes.c_int, [P, P]),
+        "pa_prefill": (ctypes.c_int, [P, P, P, P, P, P, P, F32, I32, I32, I64, I32, I32, I32, I64, I32, I32, I32,
+                                      I32, I32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -255,6 +258,30 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, block_siz
                           _dtype_code(q, "q"), _dtype_code(k_cache, "k_cache"),
                           _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), ws_ptr, ws_bytes,
                           int(partition_tokens), _stream(stream))
+    _check(rc)
+
+
+def pa_prefill(out, q, k_cache, v_cache, block_tables, seq_lens, query_start, scale, block_size, *,
+               max_query_len=None, max_seq_len=None, stream=None):
+    """Causal attention of each request's new tokens (q rows query_start[b]..query_start[b+1]-1,
+    the request's last tokens, K/V already written) over its cached tokens; see pa_prefill in
+    include/pagedkv.h.  max_query_len / max_seq_len default to the values read from the
+    device tensors (a synchronising copy)."""
+    T, Hq, d = q.shape
+    N, Hkv, bs, _ = k_cache.shape
+    B = seq_lens.shape[0]
+    if query_start.shape[0] != B + 1:
+        raise ValueError("query_start must hold num_seqs + 1 entries")
+    if max_query_len is None:
+        qs = query_start.cpu()
+        max_query_len = int((qs[1:] - qs[:-1]).max()) if B else 0
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max()) if B else 0
+    rc = load().pa_prefill(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                           _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"),
+                           _dev(query_start, "query_start"), float(scale), int(block_size), B, T, Hq, Hkv, d, N,
+                           block_tables.shape[1], int(max_query_len), int(max_seq_len),
+                           _dtype_code(q, "q"), _dtype_code(k_cache, "k_cache"), _stream(stream))
     _check(rc)
 
 
