@@ -152,6 +152,7 @@ constexpr float kRescaleThreshold = 8.0f;
 
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 typedef short i16x4v __attribute__((ext_vector_type(4)));
+typedef short i16x8v __attribute__((ext_vector_type(8)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 // float32 -> bf16 bits, round to nearest even (finite, non-negative inputs: softmax weights).

@@ -6,21 +6,24 @@
 // saved once; "KV Cache Optimization and PagedAttention", first paragraph: each token attends
 // to every previous token).
 //
-// prefill_kernel: one work-group (4 wave64) per (query tile, KV head, request).  A query tile
-// is 64 rows = 64 / G new tokens x the G query heads of the KV head, 16 rows per wave.  The
+// prefill_kernel: one work-group (8 wave64) per (query tile, KV head, request).  A query tile
+// is 128 rows = 128 / G new tokens x the G query heads of the KV head, 16 rows per wave.  The
 // work-group walks the request's K/V in tiles of 64 tokens, from position 0 up to the tile's
-// last query position, through a double-buffered LDS tile that each wave fills for its 16
+// last query position, through a double-buffered LDS tile that each wave fills for its 8
 // token rows with global_load_lds_dwordx4 (HBM straight to LDS; 16-byte chunks of a row
-// XOR-swizzled by row).  Per 16 KV tokens each wave does what decode does for 16 heads:
-//  - scores S^T[token][row] = K_tile[16 x D] . Q^T[D x 16] with v_mfma_f32_16x16x32_bf16
+// XOR-swizzled by row).  Two work-groups (16 waves, 128 VGPRs each) fit a compute unit.  Per
+// 16 KV tokens each wave does what decode does for 16 heads:
+//  - scores S^T[token][row] = K_step[16 x D] . Q^T[D x 16] with v_mfma_f32_16x16x32_bf16
 //    (K read from LDS as the A operand, the wave's 16 query rows as the B operand, loaded once);
 //  - the causal mask (token position > row position -> -inf), the online softmax per row with
-//    the lazy rescale of the decode kernel, weights rounded to bf16 (the denominator sums the
-//    rounded weights);
-//  - out[row][16 dims] += P . V with v_mfma_f32_16x16x16bf16_1k, V read token-major per dim
-//    with ds_read_b64_tr_b16 from the same LDS tile.
-// 16-token steps past all of a wave's rows are skipped; tiles are loaded once per work-group
-// for all of its rows.  Rows are normalised in registers and written as bf16.
+//    the lazy rescale of the decode kernel, weights rounded to bf16; the denominator, the sum of
+//    the rounded weights, comes from one more product of the weights with a column of ones;
+//  - out[row][16 dims] += P . V with v_mfma_f32_16x16x32_bf16 over 32 tokens, V read
+//    token-major per dim with ds_read_b64_tr_b16 from the same LDS tile (two reads of 4 tokens
+//    form the B operand; the A operand holds the row's weights of the same 8 tokens).
+// The softmax is updated once per 64-token tile (one row maximum, one ballot); 16-token steps
+// past all of a wave's rows are skipped; tiles are loaded once per work-group for all of its
+// rows.  Rows are normalised in registers and written as bf16.
 
 #include "pa_device.h"
 #include "pa_error.h"
@@ -49,10 +52,15 @@ struct PrefillArgs {
     int64_t num_query_tokens;
 };
 
-constexpr int kPWaves = 4;
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 8      // waves per work-group (4 or 8): 8 measured faster
+#endif
+constexpr int kPWaves = PA_PREFILL_WAVES;
+static_assert(kPWaves == 4 || kPWaves == 8, "4 or 8 waves per work-group");
 constexpr int kPThreads = 64 * kPWaves;
 constexpr int kPRows = 16 * kPWaves;   // query rows (token, head) per work-group
-constexpr int kKvTile = 64;            // KV tokens per LDS tile (16 per wave)
+constexpr int kKvTile = 64;            // KV tokens per LDS tile
+constexpr int kRW = kKvTile / kPWaves; // token rows of a tile each wave loads
 
 template <int D, int BS, int G>
 __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs a) {
@@ -61,11 +69,11 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
     constexpr int NQK = D / 32;                 // 16x16x32 products per 16 tokens (scores)
     constexpr int NPV = D / 16;                 // 16-dim output tiles
     constexpr int TQ = kPRows / G;              // new tokens per work-group
-    constexpr int NI = 16 * ROWB / 1024;        // DMA instructions per wave per K (or V) tile
+    constexpr int NI = kRW * ROWB / 1024;       // DMA instructions per wave per K (or V) tile
     constexpr int RPI = 64 / CPR;               // token rows per DMA instruction
     constexpr int TB = kKvTile * ROWB;          // bytes of one K (or V) tile
-    constexpr int WPB = BS < 16 ? 2 : 1;        // blocks behind one wave's 16 token rows
-    static_assert(NI >= 1 && RPI <= BS && (WPB == 1 || 2 * BS == 16), "tile shape");
+    constexpr int WPB = BS < kRW ? 2 : 1;       // blocks behind one wave's kRW token rows
+    static_assert(NI >= 1 && RPI <= BS && (WPB == 1 || 2 * BS == kRW), "tile shape");
     static_assert(G == 1 || G == 4 || G == 8, "query heads per KV head");
 
     __shared__ __align__(16) unsigned char s_kv[2][2][TB];   // [buffer][K, V][64 rows]
@@ -114,7 +122,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
     bool bad = false;
     auto read_entries = [&](int k0) {
         const int tile = k0 + lane;
-        const int e = (kKvTile * tile + 16 * w) / BS;
+        const int e = (kKvTile * tile + kRW * w) / BS;
         ent_a = a.max_blocks > 0 ? gld_i32(table + min(e, a.max_blocks - 1)) : -1;
         if constexpr (WPB == 2) ent_b = a.max_blocks > 0 ? gld_i32(table + min(e + 1, a.max_blocks - 1)) : -1;
         const bool live = tile < ntiles;
@@ -131,13 +139,13 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
     };
     read_entries(0);
 
-    // DMA layout: position p of the wave's 16-row slice holds chunk (p % CPR) ^ (row % CPR) of
-    // row p / CPR; lane `lane` of instruction i fills position 64 i + lane
+    // DMA layout: tile row R holds its chunk c at slot c ^ (R % CPR); lane `lane` of the
+    // wave's instruction i fills position 64 i + lane of the wave's kRW-row slice
     uint32_t src_off[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int pos = 64 * i + lane, row = pos / CPR, slot = pos % CPR;
-        src_off[i] = uint32_t(row) * ROWB + 16u * uint32_t(slot ^ (row % CPR));
+        src_off[i] = uint32_t(row) * ROWB + 16u * uint32_t(slot ^ ((kRW * w + row) % CPR));
     }
     const int64_t blk_bytes = int64_t(a.hkv) * BS * ROWB;
     const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(a.k_cache) + int64_t(g) * BS * ROWB;
@@ -145,10 +153,10 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
 
     auto issue = [&](int k, int bf) {
         if ((k & 63) == 0 && k > 0) read_entries(k);
-        const int pos0 = kKvTile * k + 16 * w;
+        const int pos0 = kKvTile * k + kRW * w;
         const int b0 = __builtin_amdgcn_readlane(ent_a, k & 63);
-        PA_LDS unsigned char* dk = (PA_LDS unsigned char*)&s_kv[bf][0][0] + 16 * w * ROWB;
-        PA_LDS unsigned char* dv = (PA_LDS unsigned char*)&s_kv[bf][1][0] + 16 * w * ROWB;
+        PA_LDS unsigned char* dk = (PA_LDS unsigned char*)&s_kv[bf][0][0] + kRW * w * ROWB;
+        PA_LDS unsigned char* dv = (PA_LDS unsigned char*)&s_kv[bf][1][0] + kRW * w * ROWB;
         if constexpr (WPB == 1) {
             const int64_t off = int64_t(b0) * blk_bytes + int64_t(pos0 % BS) * ROWB;
 #pragma unroll
@@ -168,19 +176,23 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
         }
     };
 
-    float m_ref = -INFINITY, l_run = 0.0f;            // row `col`
+    float m_ref = -INFINITY;                          // row `col`, in scaled units
     f32x4v acc[NPV];                                  // out[row 4 * grp4 + i][16 t + col]
 #pragma unroll
     for (int t = 0; t < NPV; ++t) acc[t] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4v lsum = {0.0f, 0.0f, 0.0f, 0.0f};           // sum of row 4 * grp4 + i's weights (every column)
+    const bf16x8v ones = __builtin_bit_cast(bf16x8v, u32x4v{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
     const float sc = a.score_scale;
+    const bool pos_scale = sc > 0.0f;
+    const float se = pos_scale ? sc : 1.0f;           // scale applied in the exponent
 
     if (ntiles > 0) issue(0, 0);
     for (int k = 0; k < ntiles; ++k) {
         const int bf = k & 1;
         wait_vmem<0>();                               // this wave's rows of tile k have landed
         if (kKvTile * (k + 1) > L) {                  // V rows past the request: zero (may hold anything)
-            PA_LDS unsigned char* dv = (PA_LDS unsigned char*)&s_kv[bf][1][0] + 16 * w * ROWB;
-            const int pos0 = kKvTile * k + 16 * w;
+            PA_LDS unsigned char* dv = (PA_LDS unsigned char*)&s_kv[bf][1][0] + kRW * w * ROWB;
+            const int pos0 = kKvTile * k + kRW * w;
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 const int p = 64 * i + lane;
@@ -191,66 +203,101 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
         if (k + 1 < ntiles) issue(k + 1, bf ^ 1);
         const PA_LDS unsigned char* kt = (const PA_LDS unsigned char*)&s_kv[bf][0][0];
         const PA_LDS unsigned char* vt = (const PA_LDS unsigned char*)&s_kv[bf][1][0];
+        const int p_base = kKvTile * k;
+        if (p_base > wave_max) continue;              // every row of this wave is before this tile
+        const int nst = min(kKvTile / 16, (wave_max - p_base) / 16 + 1);   // steps of 16 with a visible token
+
+        // scores of the tile's steps (independent chains of NQK products)
+        f32x4v s4[kKvTile / 16];
 #pragma unroll
         for (int st = 0; st < kKvTile / 16; ++st) {
-            const int p0 = kKvTile * k + 16 * st;
-            if (p0 > wave_max) break;                 // every row of this wave is before these tokens
-            f32x4v s4 = {0.0f, 0.0f, 0.0f, 0.0f};
-            const int krow = 16 * st + col;
-            const PA_LDS unsigned char* kp = kt + krow * ROWB;
+            s4[st] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+            if (st < nst) {
+                const int krow = 16 * st + col;
+                const PA_LDS unsigned char* kp = kt + krow * ROWB;
 #pragma unroll
-            for (int j = 0; j < NQK; ++j) {
-                const U4 kv = lds_ld16(kp + 16 * ((4 * j + grp4) ^ (krow % CPR)));
-                s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, kv),
-                                                             __builtin_bit_cast(bf16x8v, qb[j]), s4, 0, 0, 0);
-            }
-            float sv[4];
-            const bool diag = p0 + 15 > wave_min;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                sv[i] = (diag && p0 + 4 * grp4 + i > my_pos) ? -INFINITY : s4[i] * sc;
-            float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-            mx = pair16_max(pair32_max(mx));          // over the row's 16 tokens
-            if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleThreshold) != 0) {
-                const float m_new = fmaxf(m_ref, mx);
-                const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);   // 0 on the first step
-                m_ref = m_new;
-                l_run *= alpha;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {         // acc rows 4 * grp4 + i take that row's factor
-                    const float ai = __int_as_float(
-                        __builtin_amdgcn_ds_bpermute(4 * (4 * grp4 + i), __float_as_int(alpha)));
-#pragma unroll
-                    for (int t = 0; t < NPV; ++t) acc[t][i] *= ai;
+                for (int j = 0; j < NQK; ++j) {
+                    const U4 kv = lds_ld16(kp + 16 * ((4 * j + grp4) ^ (krow % CPR)));
+                    s4[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, kv),
+                                                                     __builtin_bit_cast(bf16x8v, qb[j]), s4[st], 0, 0, 0);
                 }
             }
-            uint32_t pw[4];
+        }
+        // causal mask (tiles that reach past the wave's first row only), then one online-softmax
+        // update per tile.  With a positive scale (the usual 1 / sqrt(d)) the maximum is taken on
+        // the raw scores and the scale is folded into the exponent's fused multiply-add.
+        if (!pos_scale) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pw[i] = weight_to_bf16(__builtin_amdgcn_exp2f(sv[i] - m_ref));
-                l_run += bf16_to_f32(pw[i]);
+            for (int st = 0; st < kKvTile / 16; ++st) s4[st] *= sc;
+        }
+        if (p_base + kKvTile - 1 > wave_min) {
+#pragma unroll
+            for (int st = 0; st < kKvTile / 16; ++st) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (p_base + 16 * st + 4 * grp4 + i > my_pos) s4[st][i] = -INFINITY;
             }
-            const i16x4v pa = __builtin_bit_cast(i16x4v, make_uint2(pw[0] | (pw[1] << 16), pw[2] | (pw[3] << 16)));
-            const int vrow = 16 * st + 4 * grp4 + ((lane & 15) >> 2);
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int st = 0; st < kKvTile / 16; ++st)
+            mx = fmaxf(fmaxf(mx, fmaxf(s4[st][0], s4[st][1])), fmaxf(s4[st][2], s4[st][3]));
+        mx = pair16_max(pair32_max(mx)) * se;         // the row's maximum over the tile, scaled
+        if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleThreshold) != 0) {
+            const float m_new = fmaxf(m_ref, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);   // 0 on the first tile
+            m_ref = m_new;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {             // accumulator rows 4 * grp4 + i take that row's factor
+                const float ai = __int_as_float(
+                    __builtin_amdgcn_ds_bpermute(4 * (4 * grp4 + i), __float_as_int(alpha)));
+                lsum[i] *= ai;
+#pragma unroll
+                for (int t = 0; t < NPV; ++t) acc[t][i] *= ai;
+            }
+        }
+        uint32_t pw[kKvTile / 16][2];                 // weights rounded to bf16, in pairs
+#pragma unroll
+        for (int st = 0; st < kKvTile / 16; ++st) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                bf16x2v pr;
+                pr[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s4[st][2 * h], se, -m_ref)));
+                pr[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s4[st][2 * h + 1], se, -m_ref)));
+                pw[st][h] = __builtin_bit_cast(uint32_t, pr);
+            }
+        }
+        // out[row][16 dims] += P . V over 32 tokens per product: the A operand's 8 values of a
+        // lane are its row's weights for tokens 4 grp4 .. +3 of step 2 s and of step 2 s + 1; the
+        // B operand's are the same tokens' V values, two transpose reads
+        const int vsub = 4 * grp4 + ((lane & 15) >> 2);
+#pragma unroll
+        for (int sp = 0; sp < kKvTile / 32; ++sp) {
+            if (2 * sp >= nst) break;
+            const bf16x8v pa = __builtin_bit_cast(bf16x8v, u32x4v{pw[2 * sp][0], pw[2 * sp][1], pw[2 * sp + 1][0],
+                                                                 pw[2 * sp + 1][1]});
+            lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, ones, lsum, 0, 0, 0);   // row sums of the rounded weights
+            const int r0 = 32 * sp + vsub, r1 = r0 + 16;
 #pragma unroll
             for (int t = 0; t < NPV; ++t) {
                 const int c = 2 * t + ((lane & 3) >> 1);
-                const PA_LDS unsigned char* src = vt + vrow * ROWB + 16 * (c ^ (vrow % CPR)) + 8 * (lane & 1);
-                const i16x4v vtr = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4v*)src);
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vtr, acc[t], 0, 0, 0);
+                const i16x4v v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (PA_LDS i16x4v*)(vt + r0 * ROWB + 16 * (c ^ (r0 % CPR)) + 8 * (lane & 1)));
+                const i16x4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (PA_LDS i16x4v*)(vt + r1 * ROWB + 16 * (c ^ (r1 % CPR)) + 8 * (lane & 1)));
+                const i16x8v vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8v, vv), acc[t], 0, 0, 0);
             }
         }
     }
 
     // normalise each row and write it (rows past the request's new tokens are not written)
     const bool any_bad = __syncthreads_or(bad) || len_bad;
-    l_run = pair16_sum(pair32_sum(l_run));
     uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int ri = 16 * w + 4 * grp4 + i;
-        const float li = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (4 * grp4 + i), __float_as_int(l_run)));
-        const float inv = any_bad ? __builtin_nanf("") : 1.0f / li;
+        const float inv = any_bad ? __builtin_nanf("") : 1.0f / lsum[i];
         const int tok = t0q + ri / G;
         if (tok >= n) continue;
         uint16_t* orow = out + (int64_t(q0 + tok) * hq + int64_t(g) * G + ri % G) * D;
