@@ -515,9 +515,9 @@ def prefill_flops(ctx_lens, n_new, Hq, d):
 def run_prefill(args):
     """Causal paged prefill, Llama-3-8B shape (32 q / 8 KV heads, head_dim 128, bf16, block
     16) on seeded synthetic K/V and q in a seeded-permutation pool: 16 requests x (1024 cached
-    + 1024 new tokens) (a chunk after a prefix-cache hit), and for the record 4 x 4096 new
-    tokens with no context and 1 x 16384.  pa_prefill timed with HIP events on the launch
-    stream; flops are the algorithmic ones (visible pairs only)."""
+    + 1024 new tokens) (a chunk after a prefix-cache hit), 4 x 4096 new tokens with no context
+    and 1 x 16384.  Each shape is run warmup + steps times; pa_prefill is timed with HIP events
+    on the launch stream (median); flops are the algorithmic ones (visible pairs only)."""
     import numpy as np
     import torch
 

@@ -11,7 +11,7 @@
 // work-group walks the request's K/V in tiles of 64 tokens, from position 0 up to the tile's
 // last query position, through a double-buffered LDS tile that each wave fills for its 8
 // token rows with global_load_lds_dwordx4 (HBM straight to LDS; 16-byte chunks of a row
-// XOR-swizzled by row).  Two work-groups (16 waves, 128 VGPRs each) fit a compute unit.  Per
+// XOR-swizzled by row so that no LDS read conflicts on banks).  Two work-groups (16 waves, 128 VGPRs each) fit a compute unit.  Per
 // 16 KV tokens each wave does what decode does for 16 heads:
 //  - scores S^T[token][row] = K_step[16 x D] . Q^T[D x 16] with v_mfma_f32_16x16x32_bf16
 //    (K read from LDS as the A operand, the wave's 16 query rows as the B operand, loaded once);
@@ -61,6 +61,19 @@ constexpr int kPThreads = 64 * kPWaves;
 constexpr int kPRows = 16 * kPWaves;   // query rows (token, head) per work-group
 constexpr int kKvTile = 64;            // KV tokens per LDS tile
 constexpr int kRW = kKvTile / kPWaves; // token rows of a tile each wave loads
+
+// Slot XOR of a K/V tile row in LDS: chunk c of tile row R sits at slot c ^ swz(R).  Chosen so
+// that both LDS read patterns are free of bank conflicts (64 banks of 4 bytes):
+//  - the K operand reads one chunk of 16 consecutive rows: the slots must differ among rows that
+//    share banks (D = 128: every row covers all banks once; D = 64: rows of equal parity);
+//  - the transpose reads of V take chunks {2t, 2t + 1} of 4 consecutive rows (from a multiple
+//    of 4) per 16 lanes, 8 rows per 32: those chunk pairs must be disjoint among rows that
+//    share banks.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (D == 128) return ((row & 7) << 1) | ((row >> 3) & 1);
+    else return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+}
 
 template <int D, int BS, int G>
 __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs a) {
@@ -139,13 +152,13 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
     };
     read_entries(0);
 
-    // DMA layout: tile row R holds its chunk c at slot c ^ (R % CPR); lane `lane` of the
+    // DMA layout: tile row R holds its chunk c at slot c ^ swz(R); lane `lane` of the
     // wave's instruction i fills position 64 i + lane of the wave's kRW-row slice
     uint32_t src_off[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int pos = 64 * i + lane, row = pos / CPR, slot = pos % CPR;
-        src_off[i] = uint32_t(row) * ROWB + 16u * uint32_t(slot ^ ((kRW * w + row) % CPR));
+        src_off[i] = uint32_t(row) * ROWB + 16u * uint32_t(slot ^ swz<D>(kRW * w + row));
     }
     const int64_t blk_bytes = int64_t(a.hkv) * BS * ROWB;
     const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(a.k_cache) + int64_t(g) * BS * ROWB;
@@ -217,7 +230,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
                 const PA_LDS unsigned char* kp = kt + krow * ROWB;
 #pragma unroll
                 for (int j = 0; j < NQK; ++j) {
-                    const U4 kv = lds_ld16(kp + 16 * ((4 * j + grp4) ^ (krow % CPR)));
+                    const U4 kv = lds_ld16(kp + 16 * ((4 * j + grp4) ^ swz<D>(krow)));
                     s4[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, kv),
                                                                      __builtin_bit_cast(bf16x8v, qb[j]), s4[st], 0, 0, 0);
                 }
@@ -282,9 +295,9 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
             for (int t = 0; t < NPV; ++t) {
                 const int c = 2 * t + ((lane & 3) >> 1);
                 const i16x4v v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (PA_LDS i16x4v*)(vt + r0 * ROWB + 16 * (c ^ (r0 % CPR)) + 8 * (lane & 1)));
+                    (PA_LDS i16x4v*)(vt + r0 * ROWB + 16 * (c ^ swz<D>(r0)) + 8 * (lane & 1)));
                 const i16x4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (PA_LDS i16x4v*)(vt + r1 * ROWB + 16 * (c ^ (r1 % CPR)) + 8 * (lane & 1)));
+                    (PA_LDS i16x4v*)(vt + r1 * ROWB + 16 * (c ^ swz<D>(r1)) + 8 * (lane & 1)));
                 const i16x8v vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8v, vv), acc[t], 0, 0, 0);
             }
