@@ -24,8 +24,10 @@ Cache layout (the pages fix none): ``cache[num_blocks, Hkv, block_size, d]``; sl
 at block s // block_size, row s % block_size.  Slots < 0 are padding and are skipped.
 
 Storage formats: 'f32' (float32 values), 'bf16' (uint16 bit patterns), 'fp8' (uint8
-E4M3FN codes with a float32 scale per KV head).  The oracle reads the exact stored values
-in float64 and computes the plain definition in float64.
+E4M3FN codes with a float32 scale per KV head), 'mxfp4' (OCP MXFP4: per (block, head) tile
+of bytes holding the 4-bit codes [block_size, d/2] and then the E8M0 scales of every 32 dims
+[block_size, d/32]; see codecs).  The oracle reads the exact stored values in float64 and
+computes the plain definition in float64.
 """
 
 from __future__ import annotations
@@ -56,6 +58,14 @@ def kv_write(k, v, slot_mapping, k_cache, v_cache, block_size: int, fmt: str,
     assert np.all(s < k_cache.shape[0] * block_size), "slot beyond the cache"
     blk, row = s // block_size, s % block_size
     kr, vr = k[live], v[live]
+    if fmt == "mxfp4":
+        for src, cache in ((kr, k_cache), (vr, v_cache)):
+            d = src.shape[-1]
+            codes, scales = codecs.mxfp4_quantize(codecs.bf16_bits_to_f64(src))   # [T, Hkv, d], [T, Hkv, d/32]
+            base = mx_tile_view(cache, block_size, d)
+            base["codes"][blk, :, row] = codecs.pack_nibbles(codes)
+            base["scales"][blk, :, row] = scales
+        return
     if fmt == "fp8":
         ks = np.asarray(k_scale, dtype=np.float32)[None, :, None]
         vs = np.asarray(v_scale, dtype=np.float32)[None, :, None]
@@ -72,13 +82,28 @@ def copy_blocks(k_cache, v_cache, pairs) -> None:
         v_cache[dst] = v_cache[src]
 
 
+def mx_tile_view(cache, block_size: int, d: int):
+    """The two parts of an MXFP4 cache [num_blocks, Hkv, block_size * (d/2 + d/32)] bytes: per
+    (block, head) the codes [block_size, d/2] (two per byte, even dim in the low nibble) and
+    then the E8M0 scales [block_size, d/32], as writable views."""
+    n, h, tb = cache.shape
+    cb = block_size * d // 2
+    assert tb == cb + block_size * d // 32
+    return {"codes": cache[:, :, :cb].reshape(n, h, block_size, d // 2),
+            "scales": cache[:, :, cb:].reshape(n, h, block_size, d // 32)}
+
+
 # ----------------------------------------------------------------------------- gather
 
-def gather(cache, table_row, L: int, kv_head: int, block_size: int, fmt: str, scale=None):
+def gather(cache, table_row, L: int, kv_head: int, block_size: int, fmt: str, scale=None, head_dim=None):
     """K (or V) rows of logical tokens 0..L-1 of one request and head, float64 [L, d]."""
     j = np.arange(L, dtype=np.int64)                       # logical token positions
     blk = np.asarray(table_row, dtype=np.int64)[j // block_size]   # page-table lookup
     assert np.all(blk >= 0), "block table entry -1 inside the sequence"
+    if fmt == "mxfp4":                                     # the tile does not carry head_dim
+        t = mx_tile_view(cache, block_size, int(head_dim))
+        codes = codecs.unpack_nibbles(t["codes"][blk, kv_head, j % block_size])
+        return codecs.mxfp4_dequantize(codes, t["scales"][blk, kv_head, j % block_size])
     out = codecs.storage_to_f64(cache[blk, kv_head, j % block_size], fmt)
     if fmt == "fp8":
         out *= np.float64(np.float32(scale[kv_head]))
@@ -115,8 +140,8 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, scale: float, block_size
     for b in range(B):
         L = int(seq_lens[b])
         for g in range(Hkv):
-            K = gather(k_cache, block_tables[b], L, g, block_size, fmt, k_scale)
-            V = gather(v_cache, block_tables[b], L, g, block_size, fmt, v_scale)
+            K = gather(k_cache, block_tables[b], L, g, block_size, fmt, k_scale, d)
+            V = gather(v_cache, block_tables[b], L, g, block_size, fmt, v_scale, d)
             for h in range(g * G, (g + 1) * G):
                 out[b, h] = attend(qf[b, h], K, V, scale)
     return out
@@ -153,8 +178,8 @@ def prefill(q, k_cache, v_cache, block_tables, seq_lens, query_start, scale: flo
         n = q1 - q0
         assert 0 <= n <= L
         for g in range(Hkv):
-            K = gather(k_cache, block_tables[b], L, g, block_size, fmt, k_scale)
-            V = gather(v_cache, block_tables[b], L, g, block_size, fmt, v_scale)
+            K = gather(k_cache, block_tables[b], L, g, block_size, fmt, k_scale, d)
+            V = gather(v_cache, block_tables[b], L, g, block_size, fmt, v_scale, d)
             for i in range(n):
                 pos = L - n + i                                # logical position of new token i
                 for h in range(g * G, (g + 1) * G):
@@ -180,8 +205,8 @@ def decode_splitk(q, k_cache, v_cache, block_tables, seq_lens, scale: float, blo
         if L == 0:
             continue
         for g in range(Hkv):
-            K = gather(k_cache, block_tables[b], L, g, block_size, fmt, k_scale)
-            V = gather(v_cache, block_tables[b], L, g, block_size, fmt, v_scale)
+            K = gather(k_cache, block_tables[b], L, g, block_size, fmt, k_scale, d)
+            V = gather(v_cache, block_tables[b], L, g, block_size, fmt, v_scale, d)
             for h in range(g * G, (g + 1) * G):
                 parts = []
                 for start in range(0, L, partition_tokens):

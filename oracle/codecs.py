@@ -115,6 +115,98 @@ def e4m3_dequantize(codes: np.ndarray, scale: float) -> np.ndarray:
     return e4m3_bits_to_f64(codes) * np.asarray(scale, dtype=np.float32).astype(np.float64)
 
 
+# ----------------------------------------------------------------------------- 4-bit: OCP MXFP4
+#
+# The pages allow a cache "down to 8-bit or 4-bit" and fix no 4-bit format.  The reading taken
+# here: OCP Microscaling MXFP4 (OCP "Microscaling Formats (MX) Specification" v1.0), the 4-bit
+# format gfx950 converts in hardware.  Each 32 consecutive head dims of one token's K (or V)
+# row form a block sharing one E8M0 scale 2^E; each element is an E2M1 code (1 sign bit, 2
+# exponent bits with bias 1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).
+#   E      = floor(log2(max |x| over the block)) - 2   (2 = the largest E2M1 exponent),
+#            clamped to the E8M0 range [-127, 127]; a block of zeros takes E = -127
+#   code_i = round_to_nearest_even_saturating(x_i / 2^E)   (saturating at 6)
+#   value  = e2m1(code_i) * 2^E
+# A block holding NaN or an infinity stores the NaN scale (0xFF) and zero codes; it decodes to
+# NaN.  The sign of an element is kept also when it rounds to zero (code 8 is -0).
+
+MX_BLOCK = 32
+E2M1_MAX = 6.0
+E8M0_NAN = 0xFF
+
+
+def _e2m1_value(code: int) -> float:
+    """Value of one E2M1 code, from the format definition."""
+    sign = -1.0 if (code >> 3) & 1 else 1.0
+    e = (code >> 1) & 0x3
+    m = code & 0x1
+    if e == 0:
+        return sign * (m / 2.0)                           # subnormal: 0.m * 2^(1-bias)
+    return sign * (1.0 + m / 2.0) * 2.0 ** (e - 1)        # normal: 1.m * 2^(e-bias)
+
+
+E2M1_DECODE = np.array([_e2m1_value(c) for c in range(16)], dtype=np.float64)
+_E2M1_POS = E2M1_DECODE[:8]
+
+
+def e2m1_encode(v: np.ndarray) -> np.ndarray:
+    """float64 values -> E2M1 codes: nearest representable magnitude, ties to the even code
+    (mantissa bit 0), magnitudes beyond 6 saturate to 6; the sign is carried separately."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), E2M1_MAX)
+    hi = np.clip(np.searchsorted(_E2M1_POS, a, side="left"), 0, 7)
+    lo = np.clip(hi - 1, 0, 7)
+    d_hi = np.abs(_E2M1_POS[hi] - a)
+    d_lo = np.abs(a - _E2M1_POS[lo])
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((hi & 1) == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return code | (np.signbit(v).astype(np.uint8) << np.uint8(3))
+
+
+def mx_block_exponent(amax: np.ndarray) -> np.ndarray:
+    """Shared exponent E of blocks with the given max |x| (finite, >= 0)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, e = np.frexp(amax)                                 # amax = f * 2^e, f in [0.5, 1)
+    E = np.where(amax > 0, e - 1 - 2, -127)
+    return np.clip(E, -127, 127).astype(np.int64)
+
+
+def mxfp4_quantize(x: np.ndarray):
+    """Rows x [..., D] (float64, D a multiple of 32) -> (codes uint8 [..., D] in 0..15,
+    E8M0 scale codes uint8 [..., D // 32])."""
+    x = np.asarray(x, dtype=np.float64)
+    blocks = x.reshape(*x.shape[:-1], x.shape[-1] // MX_BLOCK, MX_BLOCK)
+    finite = np.all(np.isfinite(blocks), axis=-1)
+    amax = np.max(np.abs(np.where(np.isfinite(blocks), blocks, 0.0)), axis=-1)
+    E = mx_block_exponent(amax)
+    codes = e2m1_encode(blocks / np.ldexp(1.0, E)[..., None])
+    codes = np.where(finite[..., None], codes, np.uint8(0)).astype(np.uint8)
+    scales = np.where(finite, E + 127, E8M0_NAN).astype(np.uint8)
+    return codes.reshape(x.shape), scales
+
+
+def mxfp4_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Exact float64 values of codes [..., D] under their blocks' E8M0 scales [..., D // 32]."""
+    codes = np.asarray(codes, dtype=np.int64)
+    scales = np.asarray(scales, dtype=np.int64)
+    blocks = E2M1_DECODE[codes].reshape(*codes.shape[:-1], codes.shape[-1] // MX_BLOCK, MX_BLOCK)
+    f = np.where(scales == E8M0_NAN, np.nan, np.ldexp(1.0, scales - 127))
+    return (blocks * f[..., None]).reshape(codes.shape)
+
+
+def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """4-bit codes [..., D] -> bytes [..., D // 2]: element 2i in the low nibble of byte i."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << np.uint8(4))).astype(np.uint8)
+
+
+def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & np.uint8(0xF)
+    out[..., 1::2] = p >> np.uint8(4)
+    return out
+
+
 # ----------------------------------------------------------------------------- storage views
 
 def storage_to_f64(arr: np.ndarray, fmt: str) -> np.ndarray:
