@@ -33,10 +33,15 @@
  *     [num_blocks][num_kv_heads][block_size][head_dim]
  * of the cache storage type; token slot s lives in block s / block_size at row
  * s % block_size.  One (block, head) tile is one contiguous span of
- * block_size * head_dim elements.
+ * block_size * head_dim elements.  An MXFP4 cache ("8-bit or 4-bit": "KV Cache Management",
+ * "Watch Out For") keeps the same [num_blocks][num_kv_heads] tiles, each of
+ *     block_size * head_dim / 2 bytes of E2M1 codes, row-major [block_size][head_dim / 2], two
+ *       per byte (the even dim in the low nibble), then
+ *     block_size * head_dim / 32 bytes of E8M0 scales, row-major [block_size][head_dim / 32]
+ * (one scale 2^(byte - 127) per 32 consecutive dims of a token row; 0xFF is NaN).
  *
  * Supported combinations (others return PA_ERR_UNSUPPORTED):
- *   (q / K,V input / out, cache) in {(f32, f32), (bf16, bf16), (bf16, fp8 e4m3)},
+ *   (q / K,V input / out, cache) in {(f32, f32), (bf16, bf16), (bf16, fp8 e4m3), (bf16, mxfp4)},
  *   head_dim in {64, 128}, block_size in {8, 16, 32, 128},
  *   num_q_heads / num_kv_heads in {1, 4, 8}.
  */
@@ -60,6 +65,7 @@ extern "C" {
 #define PA_DTYPE_F32      0     /* IEEE binary32                                          */
 #define PA_DTYPE_BF16     1     /* bfloat16                                               */
 #define PA_DTYPE_FP8_E4M3 2     /* OCP FP8 E4M3FN (bias 7, max 448, no inf), cache only   */
+#define PA_DTYPE_MXFP4    3     /* OCP MXFP4: E2M1 codes, E8M0 scale per 32 dims; cache only */
 
 /* Message describing the last non-OK status returned on this thread ("" if none). */
 const char* pa_last_error(void);
@@ -76,7 +82,10 @@ int32_t pa_abi_version(void);
  * and the same for v.  enc is a bit copy when cache_dtype == in_dtype; for an fp8 cache
  * (in_dtype bf16) enc_h(x) = e4m3_round_nearest_even_saturate(float32(x / k_scale[h]))
  * (v_scale for v): the float32 quotient is correctly rounded, magnitudes beyond 448
- * saturate to 448, NaN stays NaN.
+ * saturate to 448, NaN stays NaN.  For an MXFP4 cache (in_dtype bf16, k_scale = v_scale =
+ * NULL) each 32 dims of a row are one block: E = floor(log2(max |x|)) - 2 clamped to
+ * [-127, 127] (-127 for a block of zeros), codes = e2m1_round_nearest_even_saturate(x / 2^E),
+ * scale byte E + 127; a block with NaN or infinity stores scale 0xFF and zero codes.
  *
  *  k, v          device, [num_tokens][num_kv_heads][head_dim] of in_dtype
  *  slot_mapping  device, int64 [num_tokens]; < 0 means "skip this token" (padding)

@@ -7,7 +7,8 @@ The names below are the C ABI's; the binding only marshals arguments.
 """
 
 from ._lib import (  # noqa: F401
-    EXPORTED, LIB_PATH, PreparedDecode, PreparedKVWrite, PA_DTYPE_BF16, PA_DTYPE_F32, PA_DTYPE_FP8_E4M3, Allocator, NoBlocksError,
+    EXPORTED, LIB_PATH, PreparedDecode, PreparedKVWrite, PA_DTYPE_BF16, PA_DTYPE_F32, PA_DTYPE_FP8_E4M3, PA_DTYPE_MXFP4,
+    Allocator, NoBlocksError, mxfp4_cache, mx_row_bytes,
     PagedKVError, UnsupportedError, load, pa_alloc_create, pa_alloc_destroy, pa_alloc_dump,
     pa_alloc_stats, pa_batch_append, pa_block_tables, pa_copy_blocks, pa_decode,
     pa_decode_workspace_bytes, pa_decode_partition_tokens, pa_decode_workspace_init, decode_workspace, pa_kv_write, pa_seq_add, pa_seq_append, pa_seq_fork, pa_seq_free,

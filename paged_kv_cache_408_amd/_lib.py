@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_NO_BLOCKS, PA_ERR_DEVICE = 0, -1, -2, -3, -4
-PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_FP8_E4M3 = 0, 1, 2
+PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_FP8_E4M3, PA_DTYPE_MXFP4 = 0, 1, 2, 3
 
 EXPORTED = [
     "pa_last_error", "pa_abi_version", "pa_kv_write", "pa_decode_workspace_bytes",
@@ -130,6 +130,31 @@ def _dtype_code(t, what):
     raise TypeError(f"{what}: unsupported dtype {t.dtype}")
 
 
+def mx_row_bytes(head_dim: int) -> int:
+    """Bytes per token row of an MXFP4 cache: head_dim / 2 of codes + head_dim / 32 of scales."""
+    return head_dim // 2 + head_dim // 32
+
+
+def mxfp4_cache(num_blocks, num_kv_heads, block_size, head_dim, device="cuda"):
+    """A zeroed MXFP4 cache: uint8 [num_blocks, num_kv_heads, block_size, head_dim * 17 / 32]
+    whose (block, head) tile holds the codes [block_size, head_dim / 2] and then the scales
+    [block_size, head_dim / 32] (not interleaved per row: the last two dims only size it)."""
+    torch = _torch()
+    return torch.zeros((num_blocks, num_kv_heads, block_size, mx_row_bytes(head_dim)), dtype=torch.uint8,
+                       device=device)
+
+
+def _cache_geom(cache, what):
+    """(num_blocks, num_kv_heads, block_size, head_dim, cache dtype code) of a cache tensor
+    [N, Hkv, bs, head_dim] (f32 / bf16 / fp8 as uint8 or float8_e4m3fn) or an MXFP4 cache
+    (uint8, last dim head_dim * 17 / 32: 34 or 68)."""
+    torch = _torch()
+    N, H, bs, last = cache.shape
+    if cache.dtype == torch.uint8 and last in (mx_row_bytes(64), mx_row_bytes(128)):
+        return N, H, bs, last * 32 // 17, PA_DTYPE_MXFP4
+    return N, H, bs, last, _dtype_code(cache, what)
+
+
 def _dev(t, what):
     if t is None:
         return None
@@ -152,7 +177,7 @@ def pa_kv_write(k, v, slot_mapping, k_cache, v_cache, *, k_scale=None, v_scale=N
     int64 slots in slot_mapping (< 0 = skip)."""
     torch = _torch()
     T, H, d = k.shape
-    N, Hc, bs, dc = k_cache.shape
+    N, Hc, bs, dc, cdt = _cache_geom(k_cache, "k_cache")
     if v.shape != k.shape or v_cache.shape != k_cache.shape or (Hc, dc) != (H, d):
         raise ValueError(f"shape mismatch: k {tuple(k.shape)} v {tuple(v.shape)} caches {tuple(k_cache.shape)}")
     if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
@@ -164,7 +189,7 @@ def pa_kv_write(k, v, slot_mapping, k_cache, v_cache, *, k_scale=None, v_scale=N
             raise ValueError("slot_mapping holds out-of-range or duplicate slots")
     rc = load().pa_kv_write(_dev(k, "k"), _dev(v, "v"), _dev(slot_mapping, "slot_mapping"), T,
                             _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), N, H, d, bs,
-                            _dtype_code(k, "k"), _dtype_code(k_cache, "k_cache"),
+                            _dtype_code(k, "k"), cdt,
                             _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _stream(stream))
     _check(rc)
 
@@ -224,7 +249,7 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, block_siz
     partition."""
     torch = _torch()
     B, Hq, d = q.shape
-    N, Hkv, bs, dc = k_cache.shape
+    N, Hkv, bs, dc, cdt = _cache_geom(k_cache, "k_cache")
     if out.shape != q.shape or v_cache.shape != k_cache.shape or dc != d or bs != block_size:
         raise ValueError(f"shape mismatch: q {tuple(q.shape)} out {tuple(out.shape)} cache {tuple(k_cache.shape)} "
                          f"block_size {block_size}")
@@ -255,7 +280,7 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, block_siz
     rc = load().pa_decode(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                           _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), float(scale),
                           block_size, B, Hq, Hkv, d, N, max_blocks, int(max_seq_len),
-                          _dtype_code(q, "q"), _dtype_code(k_cache, "k_cache"),
+                          _dtype_code(q, "q"), cdt,
                           _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), ws_ptr, ws_bytes,
                           int(partition_tokens), _stream(stream))
     _check(rc)
@@ -268,7 +293,7 @@ def pa_prefill(out, q, k_cache, v_cache, block_tables, seq_lens, query_start, sc
     include/pagedkv.h.  max_query_len / max_seq_len default to the values read from the
     device tensors (a synchronising copy)."""
     T, Hq, d = q.shape
-    N, Hkv, bs, _ = k_cache.shape
+    N, Hkv, bs, _, cdt = _cache_geom(k_cache, "k_cache")
     B = seq_lens.shape[0]
     if query_start.shape[0] != B + 1:
         raise ValueError("query_start must hold num_seqs + 1 entries")
@@ -281,18 +306,18 @@ def pa_prefill(out, q, k_cache, v_cache, block_tables, seq_lens, query_start, sc
                            _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"),
                            _dev(query_start, "query_start"), float(scale), int(block_size), B, T, Hq, Hkv, d, N,
                            block_tables.shape[1], int(max_query_len), int(max_seq_len),
-                           _dtype_code(q, "q"), _dtype_code(k_cache, "k_cache"), _stream(stream))
+                           _dtype_code(q, "q"), cdt, _stream(stream))
     _check(rc)
 
 
 def pa_copy_blocks(k_cache, v_cache, src_dst, *, stream=None):
     """Copy whole blocks src -> dst (int64 [n, 2] device tensor) in both caches."""
     torch = _torch()
-    N, Hkv, bs, d = k_cache.shape
+    N, Hkv, bs, d, cdt = _cache_geom(k_cache, "k_cache")
     if src_dst.dtype != torch.int64 or src_dst.dim() != 2 or src_dst.shape[1] != 2:
         raise ValueError("src_dst must be int64 [n, 2]")
     rc = load().pa_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(src_dst, "src_dst"),
-                               src_dst.shape[0], N, Hkv, d, bs, _dtype_code(k_cache, "k_cache"), _stream(stream))
+                               src_dst.shape[0], N, Hkv, d, bs, cdt, _stream(stream))
     _check(rc)
 
 
@@ -308,7 +333,7 @@ def pa_swap_blocks(dst_k, dst_v, src_k, src_v, src_dst, *, stream=None):
     """Copy whole blocks src_k[s] -> dst_k[d] (and v) for each row (s, d) of src_dst (int64
     [n, 2]); each pool is a device tensor or a pinned host tensor of the cache layout."""
     torch = _torch()
-    Ns, Hkv, bs, d = src_k.shape
+    Ns, Hkv, bs, d, cdt = _cache_geom(src_k, "src_k")
     Nd = dst_k.shape[0]
     for t, n in ((dst_k, "dst_k"), (dst_v, "dst_v"), (src_v, "src_v")):
         if t.shape[1:] != src_k.shape[1:] or t.dtype != src_k.dtype:
@@ -320,7 +345,7 @@ def pa_swap_blocks(dst_k, dst_v, src_k, src_v, src_dst, *, stream=None):
     rc = load().pa_swap_blocks(_dev_or_pinned(dst_k, "dst_k"), _dev_or_pinned(dst_v, "dst_v"),
                                _dev_or_pinned(src_k, "src_k"), _dev_or_pinned(src_v, "src_v"),
                                _dev_or_pinned(src_dst, "src_dst"), src_dst.shape[0], Ns, Nd, Hkv, d, bs,
-                               _dtype_code(src_k, "src_k"), _stream(stream))
+                               cdt, _stream(stream))
     _check(rc)
 
 
@@ -537,7 +562,7 @@ class PreparedDecode:
     def __init__(self, out, q, k_cache, v_cache, block_tables, seq_lens, scale, block_size, *, max_seq_len,
                  workspace, k_scale=None, v_scale=None, partition_tokens=0, stream=None):
         B, Hq, d = q.shape
-        N, Hkv, bs, dc = k_cache.shape
+        N, Hkv, bs, dc, cdt = _cache_geom(k_cache, "k_cache")
         if out.shape != q.shape or v_cache.shape != k_cache.shape or dc != d or bs != block_size:
             raise ValueError("shape mismatch")
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -545,7 +570,7 @@ class PreparedDecode:
         self._args = (_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                       _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), ctypes.c_float(scale),
                       block_size, B, Hq, Hkv, d, N, block_tables.shape[1], int(max_seq_len),
-                      _dtype_code(q, "q"), _dtype_code(k_cache, "k_cache"), _dev(k_scale, "k_scale"),
+                      _dtype_code(q, "q"), cdt, _dev(k_scale, "k_scale"),
                       _dev(v_scale, "v_scale"), _dev(workspace, "workspace"), ws_bytes, int(partition_tokens),
                       _stream(stream))
         self._fn = load().pa_decode
@@ -561,12 +586,12 @@ class PreparedKVWrite:
 
     def __init__(self, k, v, slot_mapping, k_cache, v_cache, *, k_scale=None, v_scale=None, stream=None):
         T, H, d = k.shape
-        N, Hc, bs, dc = k_cache.shape
+        N, Hc, bs, dc, cdt = _cache_geom(k_cache, "k_cache")
         if v.shape != k.shape or v_cache.shape != k_cache.shape or (Hc, dc) != (H, d) or slot_mapping.shape != (T,):
             raise ValueError("shape mismatch")
         self._keep = (k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale)
         self._args = (_dev(k, "k"), _dev(v, "v"), _dev(slot_mapping, "slot_mapping"), T, _dev(k_cache, "k_cache"),
-                      _dev(v_cache, "v_cache"), N, H, d, bs, _dtype_code(k, "k"), _dtype_code(k_cache, "k_cache"),
+                      _dev(v_cache, "v_cache"), N, H, d, bs, _dtype_code(k, "k"), cdt,
                       _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _stream(stream))
         self._fn = load().pa_kv_write
 

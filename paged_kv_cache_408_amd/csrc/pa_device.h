@@ -19,6 +19,7 @@ template <int DT> struct Elem;
 template <> struct Elem<PA_DTYPE_F32> { using T = float; static constexpr int bytes = 4; };
 template <> struct Elem<PA_DTYPE_BF16> { using T = uint16_t; static constexpr int bytes = 2; };
 template <> struct Elem<PA_DTYPE_FP8_E4M3> { using T = uint8_t; static constexpr int bytes = 1; };
+template <> struct Elem<PA_DTYPE_MXFP4> { using T = uint8_t; static constexpr int bytes = 0; };   // half a byte + scales
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
@@ -116,6 +117,12 @@ __device__ __forceinline__ U4 gld16(const void* p) {
     return U4{v[0], v[1], v[2], v[3]};
 }
 __device__ __forceinline__ int gld_i32(const int32_t* p) { return *(const PA_GLOBAL int32_t*)p; }
+__device__ __forceinline__ uint32_t gld_u8(const void* p) { return *(const PA_GLOBAL uint8_t*)p; }
+__device__ __forceinline__ uint2 gld8(const void* p) {
+    typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+    const u32x2v v = *(const PA_GLOBAL u32x2v*)p;
+    return make_uint2(v[0], v[1]);
+}
 __device__ __forceinline__ float gld_f32(const float* p) { return *(const PA_GLOBAL float*)p; }
 template <typename T>
 __device__ __forceinline__ void gst(T* p, T v) { *(PA_GLOBAL T*)p = v; }
@@ -159,6 +166,24 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint32_t weight_to_bf16(float f) {
     const uint32_t u = __float_as_uint(f);
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ------------------------------------------------------------------ MXFP4 (OCP microscaling, 4-bit)
+
+// E8M0 scale byte -> its float32 value 2^(byte - 127) (0xFF gives infinity, so the block
+// decodes to infinities and NaNs).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t code) {
+    return __uint_as_float(code == 0 ? 0x00400000u : code << 23);
+}
+
+// 8 E2M1 codes (one dword, element 0 in the low nibble) times their block's scale -> 8 bf16
+// values (four dwords, element 0 first).  gfx950's scaled pair conversion; exact, since every
+// E2M1 value times 2^-127 .. 2^125 is a bfloat16 number.
+__device__ __forceinline__ U4 e2m1x8_to_bf16(uint32_t w, float scale) {
+    return U4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3))};
 }
 
 }  // namespace

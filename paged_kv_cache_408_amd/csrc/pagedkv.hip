@@ -180,6 +180,85 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
     }
 }
 
+// One MXFP4 block: 32 bf16 values (16 dwords) -> 16 code bytes (element 0 in the low nibble)
+// and the E8M0 scale byte.  E = floor(log2(max |x|)) - 2 from the exponent field of the largest
+// magnitude (bf16 magnitudes order like their bit patterns), clamped to -127; x / 2^E is exact
+// (a power-of-two scaling that stays below 8) wherever it reaches the rounding thresholds.
+// Round to nearest even on the E2M1 grid with saturation: the code counts the thresholds
+// passed, a tie going to the neighbour whose mantissa bit is 0.
+__device__ __forceinline__ void mx4_quantize(const uint32_t (&x)[16], uint32_t (&codes)[4], uint32_t& scale) {
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = max(amax, max(x[i] & 0x7fffu, (x[i] >> 16) & 0x7fffu));
+    if (amax >= 0x7f80u) {                                // NaN or infinity in the block
+        scale = 0xffu;
+        codes[0] = codes[1] = codes[2] = codes[3] = 0u;
+        return;
+    }
+    const int eb = int(amax >> 7);                        // exponent field of the largest magnitude
+    const int E = eb == 0 ? -127 : max(eb - 127 - 2, -127);
+    const float inv = __uint_as_float(uint32_t(127 - E) << 23);   // 2^-E (E <= 125)
+    scale = uint32_t(E + 127);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t word = x[4 * w + e / 2];
+            const uint32_t b = (e & 1) ? (word >> 16) : (word & 0xffffu);
+            const float a = bf16_to_f32(b & 0x7fffu) * inv;
+            uint32_t q = uint32_t(a > 0.25f) + uint32_t(a >= 0.75f) + uint32_t(a > 1.25f) + uint32_t(a >= 1.75f) +
+                         uint32_t(a > 2.5f) + uint32_t(a >= 3.5f) + uint32_t(a > 5.0f);
+            q |= (b >> 12) & 0x8u;                        // sign
+            c |= q << (4 * e);
+        }
+        codes[w] = c;
+    }
+}
+
+// MXFP4 write: one lane per (token, KV head, block of 32 dims) for K and for V.
+__global__ __launch_bounds__(256) void kv_write_mx4_kernel(const uint16_t* __restrict__ k,
+                                                           const uint16_t* __restrict__ v,
+                                                           const int64_t* __restrict__ slots, int64_t num_tokens,
+                                                           uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+                                                           int64_t num_slots, int hkv, int d, int bs) {
+    const int groups = d / 32;
+    const int64_t tile = int64_t(bs) * (d / 2 + d / 32);    // bytes of one (block, head) tile
+    const int64_t total = num_tokens * hkv * groups;
+    for (int64_t gid = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; gid < total;
+         gid += int64_t(gridDim.x) * blockDim.x) {
+        const int64_t row = gid / groups;                   // (token, head)
+        const int gi = static_cast<int>(gid - row * groups);
+        const int64_t t = row / hkv;
+        const int h = static_cast<int>(row - t * hkv);
+        const int64_t s = slots[t];
+        if (s < 0 || s >= num_slots) continue;
+        const int64_t blk = s / bs, r = s - blk * bs;
+        const int64_t base = (blk * hkv + h) * tile;
+        const int64_t code_off = base + r * (d / 2) + gi * 16;
+        const int64_t scale_off = base + int64_t(bs) * (d / 2) + r * groups + gi;
+        const int64_t src = row * d + gi * 32;
+#pragma unroll
+        for (int kv = 0; kv < 2; ++kv) {
+            const uint16_t* x = kv ? v : k;
+            uint8_t* cache = kv ? vc : kc;
+            uint32_t words[16];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const U4 u = ld16(x + src + 8 * i);
+                words[4 * i] = u.x;
+                words[4 * i + 1] = u.y;
+                words[4 * i + 2] = u.z;
+                words[4 * i + 3] = u.w;
+            }
+            uint32_t codes[4], scale;
+            mx4_quantize(words, codes, scale);
+            *reinterpret_cast<U4*>(cache + code_off) = U4{codes[0], codes[1], codes[2], codes[3]};
+            cache[scale_off] = static_cast<uint8_t>(scale);
+        }
+    }
+}
+
 // ------------------------------------------------------------------ block copy
 
 // Whole-block copies from one pool to another (or within one pool: copy-on-write).  Either
@@ -842,7 +921,24 @@ struct MCfg {
     static constexpr int CPR = ROWB / 16;                // 16-byte chunks per cached row
     static constexpr int VLD = 16 * CPR / 64;            // 16-byte V loads per lane per pass
     static constexpr int TROWB = D * 2;                  // bytes per row of the bf16 V tile in LDS
+    static constexpr int SGB = 0;                        // no per-row scales
     static_assert(VLD >= 1 && KLD >= 1, "layout");
+};
+
+// MXFP4 caches: a pass loads per lane 16 bytes of K codes (D 128; 8 for D 64) of row `col`
+// (dims NQK * 8 * grp4 .. + NQK * 8, one 32-dim block for D 128) and the same of V (row
+// lane / 4, quarter lane % 4), plus each one's block scale: two "loads" of K and of V.
+template <int D>
+struct MCfg<PA_DTYPE_MXFP4, D> {
+    static constexpr int E = 0;                          // marks the 4-bit layout
+    static constexpr int ROWB = D / 2;                   // code bytes of one token row
+    static constexpr int SGB = D / 32;                   // scale bytes of one token row
+    static constexpr int NQK = D / 32;
+    static constexpr int NPV = D / 16;
+    static constexpr int KLD = 2;                        // codes, scale
+    static constexpr int CPR = ROWB / 16;
+    static constexpr int VLD = 2;                        // codes, scale
+    static constexpr int TROWB = D * 2;
 };
 
 constexpr int kMaxListSeqs = 8192;   // batches up to this size use the compact item list
@@ -867,13 +963,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
     using QT = typename Elem<QDT>::T;
     constexpr int TPP = 16;                               // tokens per pass
     constexpr int BPP = BS < TPP ? TPP / BS : 1;          // blocks touched by one pass (1 or 2)
-    static_assert(QDT == PA_DTYPE_BF16 && (CDT == PA_DTYPE_BF16 || CDT == PA_DTYPE_FP8_E4M3), "bf16 q");
+    static_assert(QDT == PA_DTYPE_BF16 &&
+                      (CDT == PA_DTYPE_BF16 || CDT == PA_DTYPE_FP8_E4M3 || CDT == PA_DTYPE_MXFP4), "bf16 q");
+    constexpr bool kMx = CDT == PA_DTYPE_MXFP4;
     static_assert(G <= 16 && BPP <= 2, "shape");
     constexpr int KT = TPP * M::ROWB;                     // bytes of one cached K (or V) tile
     constexpr int VTB = TPP * M::TROWB;                   // bytes of one bf16 V tile
     // LDS per wave: the V tile (registers path) or the ring of K/V stages plus, for fp8, the
     // bf16 V tile the transpose reads use
-    constexpr int kStages = M::E == 2 ? kStagesBf16 : kStagesFp8;
+    constexpr int kStages = kMx ? 0 : M::E == 2 ? kStagesBf16 : kStagesFp8;
     constexpr int WAVE_LDS = kStages > 0 ? kStages * 2 * KT + (M::E == 1 ? VTB : 0) : VTB;
     static_assert(G * D * 4 <= WAVE_LDS, "a wave's merge slice fits in its LDS");
 
@@ -890,7 +988,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
     const int hq = a.hkv * G;
     const CT* kbase = reinterpret_cast<const CT*>(a.k_cache);
     const CT* vbase = reinterpret_cast<const CT*>(a.v_cache);
-    const int64_t block_stride = int64_t(a.hkv) * (BS * D);
     PA_LDS unsigned char* tile = (PA_LDS unsigned char*)&s_tile[w][0];
 
     auto nparts_of = [&](int L_raw) {
@@ -921,7 +1018,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
             const QT* qrow = reinterpret_cast<const QT*>(a.q) + (int64_t(b) * hq + int64_t(g) * G + col) * D;
 #pragma unroll
             for (int j = 0; j < M::NQK; ++j) {
-                const int d0 = M::E == 2 ? 32 * j + 8 * grp4 : 64 * (j >> 1) + 16 * grp4 + 8 * (j & 1);
+                const int d0 = kMx ? M::NQK * 8 * grp4 + 8 * j
+                               : M::E == 2 ? 32 * j + 8 * grp4 : 64 * (j >> 1) + 16 * grp4 + 8 * (j & 1);
                 qb[j] = col < G ? gld16(qrow + d0) : U4{0, 0, 0, 0};
             }
         }
@@ -942,7 +1040,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
         const int t1 = min(L, t0 + a.part_tokens);
         const int npass = (t1 - t0 + TPP - 1) / TPP;
         const int nk = npass > w ? (npass - w + kWaves - 1) / kWaves : 0;
-        const int64_t head_tile = int64_t(g) * (BS * D);
         float sc = a.score_scale;
         float vsc = 1.0f;
         if constexpr (CDT == PA_DTYPE_FP8_E4M3) {
@@ -977,9 +1074,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
         // V chunk `lane` of each 1 KiB group of chunks
         const uint32_t k_lane = uint32_t(col) * M::ROWB + 16u * grp4;
         const uint32_t v_lane = uint32_t(lane / M::CPR) * M::ROWB + 16u * (lane % M::CPR);
-        const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(kbase) + head_tile * M::E;
-        const unsigned char* vbytes = reinterpret_cast<const unsigned char*>(vbase) + head_tile * M::E;
-        const int64_t blk_bytes = block_stride * M::E;
+        // (block, head) tiles: D * E bytes per token row, or for MXFP4 the codes then the scales
+        constexpr int64_t kTile = kMx ? int64_t(BS) * (M::ROWB + M::SGB) : int64_t(BS) * D * M::E;
+        const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(kbase) + int64_t(g) * kTile;
+        const unsigned char* vbytes = reinterpret_cast<const unsigned char*>(vbase) + int64_t(g) * kTile;
+        const int64_t blk_bytes = int64_t(a.hkv) * kTile;
 
         if constexpr (kStages == 0) {
             auto issue = [&](int k, U4 (&kb)[M::KLD], U4 (&vb)[M::VLD]) {
@@ -989,7 +1088,27 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
                 }
                 const int tb = t0 + (w + kWaves * k) * TPP;
                 const int b0 = __builtin_amdgcn_readlane(ent_a, k & 63);
-                if constexpr (BPP == 1) {
+                if constexpr (kMx) {
+                    // K row `col`, V row lane / 4 (quarter lane % 4); rows 8..15 in the second
+                    // block when blocks hold 8 tokens
+                    const int b1 = BPP == 2 ? __builtin_amdgcn_readlane(ent_b, k & 63) : b0;
+                    const int vr = lane >> 2, part = lane & 3;
+                    const int kr = BPP == 2 ? col % BS : tb % BS + col;
+                    const int vrr = BPP == 2 ? vr % BS : tb % BS + vr;
+                    const unsigned char* kt = kbytes + int64_t((BPP == 2 && col >= BS) ? b1 : b0) * blk_bytes;
+                    const unsigned char* vt = vbytes + int64_t((BPP == 2 && vr >= BS) ? b1 : b0) * blk_bytes;
+                    if constexpr (D == 128) {
+                        kb[0] = gld16_stream(kt + kr * M::ROWB + 16 * grp4);
+                        vb[0] = gld16_stream(vt + vrr * M::ROWB + 16 * part);
+                    } else {
+                        const uint2 k8 = gld8(kt + kr * M::ROWB + 8 * grp4);
+                        const uint2 v8 = gld8(vt + vrr * M::ROWB + 8 * part);
+                        kb[0] = U4{k8.x, k8.y, 0u, 0u};
+                        vb[0] = U4{v8.x, v8.y, 0u, 0u};
+                    }
+                    kb[1].x = gld_u8(kt + BS * M::ROWB + kr * M::SGB + (D == 128 ? grp4 : grp4 / 2));
+                    vb[1].x = gld_u8(vt + BS * M::ROWB + vrr * M::SGB + (D == 128 ? part : part / 2));
+                } else if constexpr (BPP == 1) {
                     // one block: uniform base + 32-bit lane offset (+ immediate offsets)
                     const uint32_t row0b = uint32_t(tb % BS) * M::ROWB;
                     const unsigned char* kp = kbytes + int64_t(b0) * blk_bytes + row0b;
@@ -1019,8 +1138,20 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
                 const int tb = t0 + (w + kWaves * k) * TPP;
                 const bool partial = tb + TPP > t1;
                 // V tile -> LDS as bf16 (rows past the end zeroed: they may hold anything)
+                if constexpr (kMx) {
+                    constexpr int NW = D / 32;            // code dwords per lane (8 dims each)
+                    const int vr = lane >> 2, part = lane & 3;
+                    const uint32_t keep = (partial && tb + vr >= t1) ? 0u : ~0u;
+                    const float vsf = e8m0_to_f32(vb[1].x);
+                    PA_LDS unsigned char* rowp = tile + vr * M::TROWB;
     #pragma unroll
-                for (int r = 0; r < M::VLD; ++r) {
+                    for (int wi = 0; wi < NW; ++wi) {
+                        const U4 c = e2m1x8_to_bf16(u4_get(vb[0], wi), vsf);
+                        lds_st16(rowp + 16 * vt_slot<D>(vr, NW * part + wi), U4{c.x & keep, c.y & keep, c.z & keep, c.w & keep});
+                    }
+                }
+    #pragma unroll
+                for (int r = 0; r < (kMx ? 0 : M::VLD); ++r) {
                     const int ci = 64 * r + lane, vr = ci / M::CPR, c = ci % M::CPR;
                     const uint32_t keep = (partial && tb + vr >= t1) ? 0u : ~0u;
                     const U4 v = U4{vb[r].x & keep, vb[r].y & keep, vb[r].z & keep, vb[r].w & keep};
@@ -1037,10 +1168,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
                 }
                 // scores: S[token][head] over the D dims
                 f32x4v s4 = {0.0f, 0.0f, 0.0f, 0.0f};
+                const float ksf = kMx ? e8m0_to_f32(kb[kMx ? 1 : 0].x) : 0.0f;
     #pragma unroll
                 for (int j = 0; j < M::NQK; ++j) {
                     U4 kv;
-                    if constexpr (M::E == 2) {
+                    if constexpr (kMx) {
+                        kv = e2m1x8_to_bf16(u4_get(kb[0], j), ksf);
+                    } else if constexpr (M::E == 2) {
                         kv = kb[j];
                     } else {
                         const U4& src = kb[j >> 1];
@@ -1367,6 +1501,12 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int elem_bytes(int dt) { return dt == PA_DTYPE_F32 ? 4 : dt == PA_DTYPE_BF16 ? 2 : dt == PA_DTYPE_FP8_E4M3 ? 1 : 0; }
 
+// Bytes of one (block, KV head) tile of the cache, or 0 for an unknown type.
+int64_t tile_bytes(int dt, int bs, int d) {
+    if (dt == PA_DTYPE_MXFP4) return int64_t(bs) * (d / 2 + d / 32);
+    return int64_t(bs) * d * elem_bytes(dt);
+}
+
 int check_launch(const char* what) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PA_ERR_DEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));
@@ -1509,7 +1649,7 @@ int dispatch_d(int D, int BS, int G, const DecodeArgs& a, int B, hipStream_t st)
 
 bool supported_pair(int qdt, int cdt) {
     return (qdt == PA_DTYPE_F32 && cdt == PA_DTYPE_F32) || (qdt == PA_DTYPE_BF16 && cdt == PA_DTYPE_BF16) ||
-           (qdt == PA_DTYPE_BF16 && cdt == PA_DTYPE_FP8_E4M3);
+           (qdt == PA_DTYPE_BF16 && cdt == PA_DTYPE_FP8_E4M3) || (qdt == PA_DTYPE_BF16 && cdt == PA_DTYPE_MXFP4);
 }
 
 }  // namespace
@@ -1536,6 +1676,8 @@ int pa_kv_write(const void* k, const void* v, const int64_t* slot_mapping, int64
         return fail(PA_ERR_INVALID, "pa_kv_write: caches must be non-NULL and 16-byte aligned");
     if (cache_dtype == PA_DTYPE_FP8_E4M3 && (!k_scale || !v_scale))
         return fail(PA_ERR_INVALID, "pa_kv_write: fp8 cache needs k_scale and v_scale");
+    if (cache_dtype == PA_DTYPE_MXFP4 && (k_scale || v_scale))
+        return fail(PA_ERR_INVALID, "pa_kv_write: an MXFP4 cache carries its own scales (k_scale, v_scale must be NULL)");
     if (num_tokens == 0) return PA_OK;
     if (!k || !v || !slot_mapping || !aligned16(k) || !aligned16(v))
         return fail(PA_ERR_INVALID, "pa_kv_write: k, v, slot_mapping must be non-NULL; k, v 16-byte aligned");
@@ -1551,10 +1693,15 @@ int pa_kv_write(const void* k, const void* v, const int64_t* slot_mapping, int64
         hipLaunchKernelGGL((kv_write_kernel<PA_DTYPE_BF16, PA_DTYPE_BF16>), dim3(grid), dim3(256), 0, st,
                            (const uint16_t*)k, (const uint16_t*)v, slot_mapping, num_tokens, (uint16_t*)k_cache,
                            (uint16_t*)v_cache, num_slots, num_kv_heads, head_dim, block_size, k_scale, v_scale);
-    } else {
+    } else if (cache_dtype == PA_DTYPE_FP8_E4M3) {
         hipLaunchKernelGGL((kv_write_kernel<PA_DTYPE_BF16, PA_DTYPE_FP8_E4M3>), dim3(grid), dim3(256), 0, st,
                            (const uint16_t*)k, (const uint16_t*)v, slot_mapping, num_tokens, (uint8_t*)k_cache,
                            (uint8_t*)v_cache, num_slots, num_kv_heads, head_dim, block_size, k_scale, v_scale);
+    } else {
+        const int mx_grid = grid_for(num_tokens * num_kv_heads * (head_dim / 32), 256);
+        hipLaunchKernelGGL(kv_write_mx4_kernel, dim3(mx_grid), dim3(256), 0, st, (const uint16_t*)k, (const uint16_t*)v,
+                           slot_mapping, num_tokens, (uint8_t*)k_cache, (uint8_t*)v_cache, num_slots, num_kv_heads,
+                           head_dim, block_size);
     }
     return check_launch("pa_kv_write");
 }
@@ -1664,6 +1811,8 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
         return dispatch_d<PA_DTYPE_F32, PA_DTYPE_F32>(head_dim, block_size, G, a, num_seqs, st);
     if (cache_dtype == PA_DTYPE_BF16)
         return dispatch_d<PA_DTYPE_BF16, PA_DTYPE_BF16>(head_dim, block_size, G, a, num_seqs, st);
+    if (cache_dtype == PA_DTYPE_MXFP4)
+        return dispatch_d<PA_DTYPE_MXFP4, PA_DTYPE_BF16>(head_dim, block_size, G, a, num_seqs, st);
     return dispatch_d<PA_DTYPE_FP8_E4M3, PA_DTYPE_BF16>(head_dim, block_size, G, a, num_seqs, st);
 }
 
@@ -1684,11 +1833,11 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst, int32_t
                    int64_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
                    int32_t block_size, int32_t cache_dtype, void* stream) {
     pagedkv::clear_error();
-    const int eb = elem_bytes(cache_dtype);
-    if (eb == 0) return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: cache dtype %d", cache_dtype);
     if (num_pairs < 0 || num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0)
         return fail(PA_ERR_INVALID, "pa_copy_blocks: bad sizes");
-    const int64_t block_bytes = int64_t(num_kv_heads) * block_size * head_dim * eb;
+    const int64_t tb = tile_bytes(cache_dtype, block_size, head_dim);
+    if (tb == 0) return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: cache dtype %d", cache_dtype);
+    const int64_t block_bytes = int64_t(num_kv_heads) * tb;
     if (block_bytes % 16 != 0) return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: block of %lld bytes", (long long)block_bytes);
     if (num_pairs == 0) return PA_OK;
     if (!k_cache || !v_cache || !src_dst || !aligned16(k_cache) || !aligned16(v_cache))
@@ -1706,12 +1855,12 @@ int pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_
                    int64_t dst_num_blocks, int32_t num_kv_heads, int32_t head_dim,
                    int32_t block_size, int32_t cache_dtype, void* stream) {
     pagedkv::clear_error();
-    const int eb = elem_bytes(cache_dtype);
-    if (eb == 0) return fail(PA_ERR_UNSUPPORTED, "pa_swap_blocks: cache dtype %d", cache_dtype);
     if (num_pairs < 0 || src_num_blocks <= 0 || dst_num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         block_size <= 0)
         return fail(PA_ERR_INVALID, "pa_swap_blocks: bad sizes");
-    const int64_t block_bytes = int64_t(num_kv_heads) * block_size * head_dim * eb;
+    const int64_t tb = tile_bytes(cache_dtype, block_size, head_dim);
+    if (tb == 0) return fail(PA_ERR_UNSUPPORTED, "pa_swap_blocks: cache dtype %d", cache_dtype);
+    const int64_t block_bytes = int64_t(num_kv_heads) * tb;
     if (block_bytes % 16 != 0) return fail(PA_ERR_UNSUPPORTED, "pa_swap_blocks: block of %lld bytes", (long long)block_bytes);
     if (num_pairs == 0) return PA_OK;
     if (!dst_k || !dst_v || !src_k || !src_v || !src_dst || !aligned16(dst_k) || !aligned16(dst_v) ||
