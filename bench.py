@@ -22,7 +22,7 @@ launches (the layers' K/V writes are issued first).  `cpu_baseline` = the float6
 timed on a bounded sample of the same per-request work on the host.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
-    python bench.py --workload {ragged_prefix,long_context,sweep}   # other workloads' decode rates
+    python bench.py --workload {ragged_prefix,long_context,sweep,mxfp4}   # other workloads' decode rates
     python bench.py --workload swap     # preemption: swap-out / swap-in rates over the host link
     python bench.py --workload prefix_cache   # prompts through the prefix cache vs without it
     python bench.py --workload prefill  # causal paged prefill: TFLOP/s against the bf16 matrix peak
@@ -320,6 +320,9 @@ def run_workload(name, args):
         settings = [workloads.ragged_prefix(bs=16)]
     elif name == "long_context":
         settings = [workloads.long_context()]
+    elif name == "mxfp4":   # the 4-bit cache on the ragged batch and on one Llama-shaped layer
+        settings = [workloads.ragged_prefix(bs=16, fmt="mxfp4"),
+                    workloads.gqa_uniform(B=16, L=4096, fmt="mxfp4", layers=1, name="llama3_8b_layer_mxfp4")]
     else:  # block-size x KV-dtype sweep on the ragged batch
         settings = [workloads.ragged_prefix(bs=bs, fmt=fmt) for bs, fmt in workloads.sweep_settings()]
     for w in settings:
@@ -335,8 +338,11 @@ def run_workload(name, args):
             elif op[0] == "free":
                 alloc.free(op[1])
         slots = torch.from_numpy(np.concatenate(slots)).to(dev)
-        cdt = torch.uint8 if w.fmt == "fp8" else torch.bfloat16
-        kc = torch.zeros((w.num_blocks, w.Hkv, w.bs, w.d), dtype=cdt, device=dev)
+        if w.fmt == "mxfp4":
+            kc = pk.mxfp4_cache(w.num_blocks, w.Hkv, w.bs, w.d, dev)
+        else:
+            cdt = torch.uint8 if w.fmt == "fp8" else torch.bfloat16
+            kc = torch.zeros((w.num_blocks, w.Hkv, w.bs, w.d), dtype=cdt, device=dev)
         vc = torch.zeros_like(kc)
         kp = workloads.device_normal(w, "k_pre", (slots.numel(), w.Hkv, w.d))
         vp = workloads.device_normal(w, "v_pre", (slots.numel(), w.Hkv, w.d))
@@ -356,7 +362,7 @@ def run_workload(name, args):
         q = workloads.device_normal(w, "q", (w.B, w.Hq, w.d))
         out = torch.empty_like(q)
         maxL = int(lens.max())
-        nbytes = pk.pa_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, maxL, args.partition_tokens, w.bs)
+        nbytes = pk.pa_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, maxL, args.partition_tokens, w.bs, kc)
         ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
         dec = pk.PreparedDecode(out, q, kc, vc, tables, lens_d, 1.0 / math.sqrt(w.d), w.bs, max_seq_len=maxL,
                                 workspace=ws if nbytes else None, k_scale=ks, v_scale=vs,
@@ -377,10 +383,10 @@ def run_workload(name, args):
         wall = time.perf_counter() - t0
         dec_us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
         med = dec_us[len(dec_us) // 2]
-        e = 1 if w.fmt == "fp8" else 2
+        e = {"fp8": 1, "mxfp4": 17 / 32}.get(w.fmt, 2)   # mxfp4: d / 2 code bytes + d / 32 scale bytes per row
         logical = decode_bytes(lens, w.Hq, w.Hkv, w.d, w.bs, e, 2) + (2 * w.Hkv * 4 if w.fmt == "fp8" else 0)
         st = alloc.stats()
-        unique_kv = st["used_blocks"] * 2 * w.Hkv * w.bs * w.d * e
+        unique_kv = int(st["used_blocks"] * 2 * w.Hkv * w.bs * w.d * e)
         waste = int(sum(-(-int(L) // w.bs) * w.bs - int(L) for L in lens))
         reserved = int(sum(-(-int(L) // w.bs) * w.bs for L in lens))
         step_bytes = logical + kv_write_bytes(w.B, w.Hkv, w.d, 2, e)
@@ -394,7 +400,7 @@ def run_workload(name, args):
             "algorithmic_bytes": int(logical), "unique_kv_bytes": int(unique_kv),
             "batch": w.B, "num_q_heads": w.Hq, "num_kv_heads": w.Hkv, "head_dim": w.d, "block_size": w.bs,
             "kv_dtype": w.fmt, "max_seq_len": maxL, "total_tokens": int(lens.sum()),
-            "partition_tokens": pk.pa_decode_partition_tokens(w.B, w.Hkv, maxL, args.partition_tokens, w.bs),
+            "partition_tokens": pk.pa_decode_partition_tokens(w.B, w.Hkv, maxL, args.partition_tokens, w.bs, kc),
             "final_block_waste_slots": waste, "final_block_waste_pct": round(100 * waste / reserved, 3),
             "contiguous_waste_pct": round(100 * (w.B * max(8192, maxL) - int(lens.sum())) / (w.B * max(8192, maxL)), 2),
             "contiguous_reservation_tokens": max(8192, maxL),
@@ -647,7 +653,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", default="llama3_8b",
-                    choices=["llama3_8b", "ragged_prefix", "long_context", "sweep", "swap", "prefix_cache", "prefill"],
+                    choices=["llama3_8b", "ragged_prefix", "long_context", "sweep", "mxfp4", "swap", "prefix_cache",
+                             "prefill"],
                     help="llama3_8b: the benchmark; the others print per-setting measurements instead")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)

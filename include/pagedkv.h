@@ -118,8 +118,9 @@ int pa_kv_write(const void* k, const void* v, const int64_t* slot_mapping, int64
  * partitions are merged by rescaling to the largest maximum (log-sum-exp).  An explicit
  * partition_tokens > 0 is rounded up to a multiple of max(64, block_size).  0 chooses it
  * automatically (pa_decode_partition_tokens gives the value): with fewer (request, KV head)
- * pairs than the device has compute units, each request is cut into ceil(CUs / pairs) equal
- * partitions of ceil(max_seq_len / parts) tokens (one work-group per compute unit); otherwise
+ * pairs than S = the device's compute units (bf16, f32 caches) or twice that (fp8, 4-bit
+ * caches), each request is cut into ceil(S / pairs) equal partitions of
+ * ceil(max_seq_len / parts) tokens (one or two work-groups per compute unit); otherwise
  * partitions are 512 tokens.  For a given partition size the result depends only on logical
  * positions, so it is bit-identical under any physical placement of the blocks.
  *
@@ -149,12 +150,13 @@ int pa_kv_write(const void* k, const void* v, const int64_t* slot_mapping, int64
  */
 int64_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t max_seq_len, int32_t partition_tokens,
-                                  int32_t block_size);
+                                  int32_t block_size, int32_t cache_dtype);
 
-/* The partition size in tokens that pa_decode uses for these sizes on the current device
- * (partition_tokens as passed to pa_decode; 0 = automatic), or a negative status. */
+/* The partition size in tokens that pa_decode uses for these sizes and cache type on the
+ * current device (partition_tokens as passed to pa_decode; 0 = automatic), or a negative
+ * status. */
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
-                                   int32_t partition_tokens, int32_t block_size);
+                                   int32_t partition_tokens, int32_t block_size, int32_t cache_dtype);
 
 /* Zero a decode workspace (a store kernel on `stream`; no memset node is recorded, so this
  * may be captured in a graph).  workspace_bytes must be a multiple of 4. */

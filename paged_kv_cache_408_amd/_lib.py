@@ -68,8 +68,8 @@ def load(path: str = LIB_PATH):
         "pa_last_error": (ctypes.c_char_p, []),
         "pa_abi_version": (I32, []),
         "pa_kv_write": (ctypes.c_int, [P, P, P, I64, P, P, I64, I32, I32, I32, I32, I32, P, P, P]),
-        "pa_decode_workspace_bytes": (I64, [I32, I32, I32, I32, I32, I32, I32]),
-        "pa_decode_partition_tokens": (I32, [I32, I32, I32, I32, I32]),
+        "pa_decode_workspace_bytes": (I64, [I32, I32, I32, I32, I32, I32, I32, I32]),
+        "pa_decode_partition_tokens": (I32, [I32, I32, I32, I32, I32, I32]),
         "pa_decode_workspace_init": (ctypes.c_int, [P, I64, P]),
         "pa_decode": (ctypes.c_int, [P, P, P, P, P, P, F32, I32, I32, I32, I32, I32, I64, I32, I32, I32, I32,
                                      P, P, P, I64, I32, P]),
@@ -194,18 +194,27 @@ def pa_kv_write(k, v, slot_mapping, k_cache, v_cache, *, k_scale=None, v_scale=N
     _check(rc)
 
 
+def _code(cache_dtype):
+    """A cache dtype code, or the code of a cache tensor (see _cache_geom)."""
+    return cache_dtype if isinstance(cache_dtype, int) else _cache_geom(cache_dtype, "cache")[4]
+
+
 def pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_tokens=0,
-                              block_size=16) -> int:
+                              block_size=16, cache_dtype=PA_DTYPE_BF16) -> int:
+    """cache_dtype: a PA_DTYPE_* code or the cache tensor itself."""
     n = load().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
-                                         partition_tokens, block_size)
+                                         partition_tokens, block_size, _code(cache_dtype))
     if n < 0:
         _check(int(n))
     return int(n)
 
 
-def pa_decode_partition_tokens(num_seqs, num_kv_heads, max_seq_len, partition_tokens=0, block_size=16) -> int:
-    """Partition size (tokens) pa_decode uses for these sizes on the current device."""
-    n = load().pa_decode_partition_tokens(num_seqs, num_kv_heads, max_seq_len, partition_tokens, block_size)
+def pa_decode_partition_tokens(num_seqs, num_kv_heads, max_seq_len, partition_tokens=0, block_size=16,
+                               cache_dtype=PA_DTYPE_BF16) -> int:
+    """Partition size (tokens) pa_decode uses for these sizes and cache type (a PA_DTYPE_*
+    code or the cache tensor) on the current device."""
+    n = load().pa_decode_partition_tokens(num_seqs, num_kv_heads, max_seq_len, partition_tokens, block_size,
+                                          _code(cache_dtype))
     if n < 0:
         _check(int(n))
     return int(n)
@@ -270,8 +279,8 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, block_siz
             if live.size and (live.min() < 0 or live.max() >= N):
                 raise ValueError(f"block table row {b} holds an id outside [0, {N})")
     if workspace is None:
-        nbytes = pa_decode_workspace_bytes(B, Hq, Hkv, d, max_seq_len, partition_tokens, block_size)
-        key = (B, Hq, Hkv, d, int(max_seq_len), int(partition_tokens), block_size)
+        nbytes = pa_decode_workspace_bytes(B, Hq, Hkv, d, max_seq_len, partition_tokens, block_size, cdt)
+        key = (B, Hq, Hkv, d, int(max_seq_len), int(partition_tokens), block_size, cdt)
         workspace = decode_workspace(nbytes, q.device, key, stream=stream) if nbytes > 0 else None
     elif workspace is False:          # explicitly none: one partition per request
         workspace = None

@@ -332,18 +332,22 @@ int device_cu_count() {
 // work-group holds a long tail.
 constexpr int kAutoRaggedPartition = 512;
 
-int64_t resolve_partition(int64_t num_seqs, int64_t hkv, int64_t max_seq_len, int requested, int block_size) {
+int64_t resolve_partition(int64_t num_seqs, int64_t hkv, int64_t max_seq_len, int requested, int block_size,
+                          int cache_dtype) {
     const int64_t unit = partition_unit(block_size);
     int64_t pt;
     if (requested > 0) {
         pt = requested;
     } else {
+        // compressed caches (fp8, 4-bit) are bound by the per-pass work, not by the bytes, and
+        // gain from two resident work-groups per compute unit; bf16 streams best with one
+        const int64_t per_cu = (cache_dtype == PA_DTYPE_FP8_E4M3 || cache_dtype == PA_DTYPE_MXFP4) ? 2 : 1;
         const int64_t pairs = num_seqs * hkv;
-        const int64_t cus = device_cu_count();
-        if (pairs >= cus) {
+        const int64_t slots = per_cu * device_cu_count();
+        if (pairs >= slots) {
             pt = kAutoRaggedPartition;
         } else {
-            const int64_t parts = (cus + pairs - 1) / pairs;
+            const int64_t parts = (slots + pairs - 1) / pairs;
             pt = (max_seq_len + parts - 1) / parts;
         }
     }
@@ -1708,24 +1712,24 @@ int pa_kv_write(const void* k, const void* v, const int64_t* slot_mapping, int64
 
 int64_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t max_seq_len, int32_t partition_tokens,
-                                  int32_t block_size) {
+                                  int32_t block_size, int32_t cache_dtype) {
     pagedkv::clear_error();
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || (head_dim != 64 && head_dim != 128) ||
         max_seq_len < 0 || partition_tokens < 0 || block_size <= 0) {
         return fail(PA_ERR_INVALID, "pa_decode_workspace_bytes: bad sizes");
     }
-    const int64_t pt = resolve_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens, block_size);
+    const int64_t pt = resolve_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens, block_size, cache_dtype);
     const int64_t parts = max_seq_len > 0 ? (int64_t(max_seq_len) + pt - 1) / pt : 1;
     if (parts <= 1) return 0;
     return ws_layout(int64_t(num_seqs) * num_q_heads, parts, head_dim).bytes;
 }
 
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
-                                   int32_t partition_tokens, int32_t block_size) {
+                                   int32_t partition_tokens, int32_t block_size, int32_t cache_dtype) {
     pagedkv::clear_error();
     if (num_seqs < 0 || num_kv_heads <= 0 || max_seq_len < 0 || partition_tokens < 0 || block_size <= 0)
         return fail(PA_ERR_INVALID, "pa_decode_partition_tokens: bad sizes");
-    const int64_t pt = resolve_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens, block_size);
+    const int64_t pt = resolve_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens, block_size, cache_dtype);
     return pt > 0x3fffffff ? 0x3fffffff : static_cast<int32_t>(pt);
 }
 
@@ -1776,7 +1780,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     a.max_seq_len = max_seq_len;
 
     const int unit = partition_unit(block_size);
-    int64_t pt = resolve_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens, block_size);
+    int64_t pt = resolve_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens, block_size, cache_dtype);
     int64_t parts = max_seq_len > 0 ? (int64_t(max_seq_len) + pt - 1) / pt : 1;
     if (parts > 1) {
         const WsLayout lay = ws_layout(int64_t(num_seqs) * num_q_heads, parts, head_dim);

@@ -104,6 +104,12 @@ def test_workspace_bytes():
     assert pk.pa_decode_partition_tokens(3, 8, 4096, 0, 16) == 384             # 24 pairs -> 11 partitions
     assert pk.pa_decode_partition_tokens(3, 8, 4096, 500, 16) == 512           # explicit: rounded up to 64
     assert pk.pa_decode_partition_tokens(3, 8, 4096, 500, 128) == 512
+    # compressed caches: two work-groups per compute unit
+    assert pk.pa_decode_partition_tokens(16, 8, 4096, 0, 16, pk.PA_DTYPE_FP8_E4M3) == 1024
+    assert pk.pa_decode_partition_tokens(16, 8, 4096, 0, 16, pk.PA_DTYPE_MXFP4) == 1024
+    assert pk.pa_decode_partition_tokens(256, 8, 8192, 0, 16, pk.PA_DTYPE_MXFP4) == 512
+    assert pk.pa_decode_workspace_bytes(16, 32, 8, 128, 4096, 0, 16, pk.PA_DTYPE_MXFP4) > \
+        pk.pa_decode_workspace_bytes(16, 32, 8, 128, 4096, 0, 16)
     with pytest.raises(pk.PagedKVError):
         pk.pa_decode_partition_tokens(3, 8, 4096, -1, 16)
 

@@ -57,8 +57,8 @@ class Workload:
 
     @property
     def in_fmt(self) -> str:
-        """Storage of the K/V rows handed to the write (fp8 caches are fed bf16 rows)."""
-        return "bf16" if self.fmt == "fp8" else self.fmt
+        """Storage of the K/V rows handed to the write (fp8 and mxfp4 caches are fed bf16 rows)."""
+        return "bf16" if self.fmt in ("fp8", "mxfp4") else self.fmt
 
     @property
     def prefill_tokens(self) -> int:
