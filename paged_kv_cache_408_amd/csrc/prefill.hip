@@ -7,23 +7,25 @@
 // to every previous token).
 //
 // prefill_kernel: one work-group (8 wave64) per (query tile, KV head, request).  A query tile
-// is 128 rows = 128 / G new tokens x the G query heads of the KV head, 16 rows per wave.  The
-// work-group walks the request's K/V in tiles of 64 tokens, from position 0 up to the tile's
-// last query position, through a double-buffered LDS tile that each wave fills for its 8
-// token rows with global_load_lds_dwordx4 (HBM straight to LDS; 16-byte chunks of a row
-// XOR-swizzled by row so that no LDS read conflicts on banks).  Two work-groups (16 waves, 128 VGPRs each) fit a compute unit.  Per
-// 16 KV tokens each wave does what decode does for 16 heads:
-//  - scores S^T[token][row] = K_step[16 x D] . Q^T[D x 16] with v_mfma_f32_16x16x32_bf16
-//    (K read from LDS as the A operand, the wave's 16 query rows as the B operand, loaded once);
-//  - the causal mask (token position > row position -> -inf), the online softmax per row with
-//    the lazy rescale of the decode kernel, weights rounded to bf16; the denominator, the sum of
-//    the rounded weights, comes from one more product of the weights with a column of ones;
-//  - out[row][16 dims] += P . V with v_mfma_f32_16x16x32_bf16 over 32 tokens, V read
-//    token-major per dim with ds_read_b64_tr_b16 from the same LDS tile (two reads of 4 tokens
-//    form the B operand; the A operand holds the row's weights of the same 8 tokens).
-// The softmax is updated once per 64-token tile (one row maximum, one ballot); 16-token steps
-// past all of a wave's rows are skipped; tiles are loaded once per work-group for all of its
-// rows.  Rows are normalised in registers and written as bf16.
+// is 256 rows = 256 / G new tokens x the G query heads of the KV head, 32 rows per wave, so each
+// K/V tile brought into LDS serves 256 rows.  The work-group walks the request's K/V in tiles of
+// 64 tokens, from position 0 up to the tile's last query position, through a double-buffered
+// LDS ring that each wave fills for its 8 token rows with global_load_lds_dwordx4 (HBM straight
+// to LDS; 16-byte chunks of a row XOR-swizzled by row so that no LDS read conflicts on banks).
+// One work-group (2 waves per SIMD) fits a compute unit at head dim 128.  Per 64-token tile
+// each wave computes, with v_mfma_f32_32x32x16_bf16:
+//  - scores S^T[token][row] = K[32 x D] . Q^T[D x 32] for both 32-token halves (K read from
+//    LDS as the A operand, the wave's 32 query rows as the B operand, loaded once); a lane then
+//    holds 16 of the 32 scores of its own row, the other 16 sit in the lane 32 apart;
+//  - the causal mask on diagonal tiles only (token position > row position -> -inf), one
+//    online-softmax update per tile (one row maximum across the lane pair, the lazy rescale),
+//    weights rounded to bf16 by the hardware conversion; the denominator adds the rounded
+//    weights two at a time (v_dot2c_f32_bf16 with a pair of ones);
+//  - out^T[dim][row] += V^T[dim x 16] . P^T[16 x row] per 16 tokens and 32 dims: V^T comes from
+//    two ds_read_b64_tr_b16 transpose reads of 4 tokens, P^T is the lane's own weights, so the
+//    accumulators of a lane all belong to its row and take its rescale factor directly.
+// Half tiles past all of a wave's rows are skipped; tiles are loaded once per work-group for all
+// of its rows.  Rows are normalised in registers and written as bf16.
 
 #include "pa_device.h"
 #include "pa_error.h"
@@ -32,6 +34,9 @@
 using pagedkv::fail;
 
 namespace {
+
+typedef float f32x16v __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 
 struct PrefillArgs {
     void* out;
@@ -53,34 +58,44 @@ struct PrefillArgs {
 };
 
 #ifndef PA_PREFILL_WAVES
-#define PA_PREFILL_WAVES 8      // waves per work-group (4 or 8): 8 measured faster
+#define PA_PREFILL_WAVES 8
 #endif
-constexpr int kPWaves = PA_PREFILL_WAVES;
+#ifndef PA_PREFILL_STAGES
+#define PA_PREFILL_STAGES 2
+#endif
+constexpr int kPWaves = PA_PREFILL_WAVES;  // waves per work-group (4 or 8): 8 measured faster
+constexpr int kStages = PA_PREFILL_STAGES; // K/V tiles in the LDS ring (2 or 3): alike
 static_assert(kPWaves == 4 || kPWaves == 8, "4 or 8 waves per work-group");
+static_assert(kStages == 2 || kStages == 3, "2 or 3 stages");
 constexpr int kPThreads = 64 * kPWaves;
-constexpr int kPRows = 16 * kPWaves;   // query rows (token, head) per work-group
+constexpr int kWRows = 32;             // query rows (token, head) per wave
+constexpr int kPRows = kWRows * kPWaves;   // query rows per work-group
 constexpr int kKvTile = 64;            // KV tokens per LDS tile
 constexpr int kRW = kKvTile / kPWaves; // token rows of a tile each wave loads
 
 // Slot XOR of a K/V tile row in LDS: chunk c of tile row R sits at slot c ^ swz(R).  Chosen so
-// that both LDS read patterns are free of bank conflicts (64 banks of 4 bytes):
-//  - the K operand reads one chunk of 16 consecutive rows: the slots must differ among rows that
-//    share banks (D = 128: every row covers all banks once; D = 64: rows of equal parity);
-//  - the transpose reads of V take chunks {2t, 2t + 1} of 4 consecutive rows (from a multiple
-//    of 4) per 16 lanes, 8 rows per 32: those chunk pairs must be disjoint among rows that
-//    share banks.
+// that both LDS read patterns are free of bank conflicts (64 banks of 4 bytes), checked for 8-,
+// 16- and 32-lane phases:
+//  - the K operand reads one chunk of 32 consecutive rows: 16 consecutive rows must land on
+//    different banks (D = 128: every row covers all banks once, so swz is a bijection of R % 16;
+//    D = 64: rows of equal parity share banks, so a bijection of (R / 2) % 8);
+//  - the transpose reads of V take 4 chunks (32 dims) of 4 consecutive rows per 32 lanes: the
+//    chunk groups must be disjoint among rows that share banks.
+// NaN-propagating maximum (v_maximum3_f32 on gfx950: no canonicalising moves before it)
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-    if constexpr (D == 128) return ((row & 7) << 1) | ((row >> 3) & 1);
-    else return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+    if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
 template <int D, int BS, int G>
 __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs a) {
     constexpr int ROWB = D * 2;                 // bytes of one bf16 token row
     constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
-    constexpr int NQK = D / 32;                 // 16x16x32 products per 16 tokens (scores)
-    constexpr int NPV = D / 16;                 // 16-dim output tiles
+    constexpr int NQK = D / 16;                 // 32x32x16 products per 32 tokens (scores)
+    constexpr int NPV = D / 32;                 // 32-dim output tiles
     constexpr int TQ = kPRows / G;              // new tokens per work-group
     constexpr int NI = kRW * ROWB / 1024;       // DMA instructions per wave per K (or V) tile
     constexpr int RPI = 64 / CPR;               // token rows per DMA instruction
@@ -89,11 +104,11 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
     static_assert(NI >= 1 && RPI <= BS && (WPB == 1 || 2 * BS == kRW), "tile shape");
     static_assert(G == 1 || G == 4 || G == 8, "query heads per KV head");
 
-    __shared__ __align__(16) unsigned char s_kv[2][2][TB];   // [buffer][K, V][64 rows]
+    __shared__ __align__(16) unsigned char s_kv[kStages][2][TB];   // [stage][K, V][64 rows]
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int col = lane & 15, grp4 = lane >> 4;
+    const int c32 = lane & 31, hi = lane >> 5;
     const int hq = a.hkv * G;
     const int b = blockIdx.x % a.num_seqs;
     const int qt = a.qtiles - 1 - static_cast<int>(blockIdx.x / a.num_seqs);   // longest tiles first
@@ -114,18 +129,29 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
     const int ntiles = len_bad ? 0 : (kv_end + kKvTile - 1) / kKvTile;
 
     // this lane's query row (column of the score products): token t0q + r / G, head r % G
-    const int r = 16 * w + col;
+    const int r = kWRows * w + c32;
     const int my_tok = min(t0q + r / G, n - 1);
     const int my_pos = ctx + my_tok;
-    const int wave_min = ctx + min(t0q + (16 * w) / G, n - 1);
-    const int wave_max = ctx + min(t0q + (16 * w + 15) / G, n - 1);
+    const int wave_min = ctx + min(t0q + (kWRows * w) / G, n - 1);
+    const int wave_max = ctx + min(t0q + (kWRows * w + kWRows - 1) / G, n - 1);
 
+    // q row as the B operand of product j: dims 16 j + 8 hi .. +7 (the A operand, K, reads the
+    // same dims of its token row).  The scale's sign goes into q (negating bf16 values and
+    // every score is exact), so the softmax always works with a positive factor in the
+    // exponent; a zero scale becomes q = 0 (every visible token weighted equally).
+    const float sc = a.score_scale;
+    const float se = sc > 0.0f ? sc : sc < 0.0f ? -sc : 1.0f;
+    const uint32_t qflip = sc < 0.0f ? 0x80008000u : 0u;
+    const uint32_t qkeep = sc == 0.0f ? 0u : 0xffffffffu;
     const uint16_t* qbase = reinterpret_cast<const uint16_t*>(a.q);
     U4 qb[NQK];
     {
         const uint16_t* qrow = qbase + (int64_t(q0 + my_tok) * hq + int64_t(g) * G + r % G) * D;
 #pragma unroll
-        for (int j = 0; j < NQK; ++j) qb[j] = gld16(qrow + 32 * j + 8 * grp4);
+        for (int j = 0; j < NQK; ++j) {
+            const U4 v = gld16(qrow + 16 * j + 8 * hi);
+            qb[j] = U4{(v.x ^ qflip) & qkeep, (v.y ^ qflip) & qkeep, (v.z ^ qflip) & qkeep, (v.w ^ qflip) & qkeep};
+        }
     }
 
     // block ids of this wave's rows for 64 tiles (lane j: tile k0 + j); ids outside the pool
@@ -176,7 +202,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
             for (int i = 0; i < NI; ++i) dma16(kbytes + off, src_off[i], lds_addr(dk + 1024 * i));
 #pragma unroll
             for (int i = 0; i < NI; ++i) dma16(vbytes + off, src_off[i], lds_addr(dv + 1024 * i));
-        } else {   // rows 0..7 from the first block, 8..15 from the second
+        } else {   // the first BS rows from the first block, the rest from the second
             const int b1 = __builtin_amdgcn_readlane(ent_b, k & 63);
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
@@ -189,133 +215,144 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
         }
     };
 
-    float m_ref = -INFINITY;                          // row `col`, in scaled units
-    f32x4v acc[NPV];                                  // out[row 4 * grp4 + i][16 t + col]
+    float m_ref = -INFINITY;                          // this lane's row, in scaled units
+    f32x16v acc[NPV];                                 // out^T[32 t + 8 (i / 4) + 4 hi + i % 4][row]
 #pragma unroll
-    for (int t = 0; t < NPV; ++t) acc[t] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
-    f32x4v lsum = {0.0f, 0.0f, 0.0f, 0.0f};           // sum of row 4 * grp4 + i's weights (every column)
-    const bf16x8v ones = __builtin_bit_cast(bf16x8v, u32x4v{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
-    const float sc = a.score_scale;
-    const bool pos_scale = sc > 0.0f;
-    const float se = pos_scale ? sc : 1.0f;           // scale applied in the exponent
+    for (int t = 0; t < NPV; ++t) acc[t] = f32x16v{};
+    float lsum = 0.0f;                                // this lane's part of the row's denominator
+    const bf16x2v ones2 = __builtin_bit_cast(bf16x2v, 0x3f803f80u);
 
-    if (ntiles > 0) issue(0, 0);
-    for (int k = 0; k < ntiles; ++k) {
-        const int bf = k & 1;
-        wait_vmem<0>();                               // this wave's rows of tile k have landed
-        if (kKvTile * (k + 1) > L) {                  // V rows past the request: zero (may hold anything)
-            PA_LDS unsigned char* dv = (PA_LDS unsigned char*)&s_kv[bf][1][0] + kRW * w * ROWB;
-            const int pos0 = kKvTile * k + kRW * w;
+    // transpose-read addressing of the V^T operand: lane group l / 16 reads 4 token rows
+    // (4 hi + (l % 16) / 4 of a 16-token step, then 8 more) at 4 dims of a 32-dim tile
+    const int vrow = 4 * hi + ((lane & 15) >> 2);
+    const int vchunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int vbyte = 8 * (lane & 1);
+
+    // V rows of tile k past what this work-group reads: zero (they may hold anything, and a
+    // weight of 0 times a NaN would spoil a row)
+    auto zero_tail = [&](int k, int stage) {
+        if (kKvTile * (k + 1) <= kv_end) return;
+        PA_LDS unsigned char* dv = (PA_LDS unsigned char*)&s_kv[stage][1][0] + kRW * w * ROWB;
+        const int pos0 = kKvTile * k + kRW * w;
 #pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                const int p = 64 * i + lane;
-                if (pos0 + p / CPR >= L) lds_st16(dv + 16 * p, U4{0, 0, 0, 0});
-            }
+        for (int i = 0; i < NI; ++i) {
+            const int p = 64 * i + lane;
+            if (pos0 + p / CPR >= kv_end) lds_st16(dv + 16 * p, U4{0, 0, 0, 0});
         }
+    };
+
+#pragma unroll
+    for (int k = 0; k < kStages - 1; ++k)
+        if (k < ntiles) issue(k, k);
+    int bf = 0;                                       // stage of tile k
+    for (int k = 0; k < ntiles; ++k) {
+        if (kStages == 3 && k + 1 < ntiles) wait_vmem<2 * NI>();   // tile k + 1 may still be in flight
+        else wait_vmem<0>();                          // this wave's rows of tile k have landed
+        zero_tail(k, bf);
         __syncthreads();                              // tile k complete; tile k - 1 no longer read
-        if (k + 1 < ntiles) issue(k + 1, bf ^ 1);
-        const PA_LDS unsigned char* kt = (const PA_LDS unsigned char*)&s_kv[bf][0][0];
-        const PA_LDS unsigned char* vt = (const PA_LDS unsigned char*)&s_kv[bf][1][0];
+        if (k + kStages - 1 < ntiles) issue(k + kStages - 1, bf == 0 ? kStages - 1 : bf - 1);   // the stage of tile k - 1
+        const int bf_cur = bf;
+        bf = bf == kStages - 1 ? 0 : bf + 1;
+        const PA_LDS unsigned char* kt = (const PA_LDS unsigned char*)&s_kv[bf_cur][0][0];
+        const PA_LDS unsigned char* vt = (const PA_LDS unsigned char*)&s_kv[bf_cur][1][0];
         const int p_base = kKvTile * k;
         if (p_base > wave_max) continue;              // every row of this wave is before this tile
-        const int nst = min(kKvTile / 16, (wave_max - p_base) / 16 + 1);   // steps of 16 with a visible token
+        const int nsb = min(2, (wave_max - p_base) / 32 + 1);   // 32-token halves with a visible token
 
-        // scores of the tile's steps (independent chains of NQK products)
-        f32x4v s4[kKvTile / 16];
+        // scores of the tile's halves (independent chains of NQK products)
+        auto scores = [&](int sb) {
+            const int krow = 32 * sb + c32;
+            const PA_LDS unsigned char* kp = kt + krow * ROWB;
+            f32x16v acc_s = f32x16v{};
 #pragma unroll
-        for (int st = 0; st < kKvTile / 16; ++st) {
-            s4[st] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
-            if (st < nst) {
-                const int krow = 16 * st + col;
-                const PA_LDS unsigned char* kp = kt + krow * ROWB;
-#pragma unroll
-                for (int j = 0; j < NQK; ++j) {
-                    const U4 kv = lds_ld16(kp + 16 * ((4 * j + grp4) ^ swz<D>(krow)));
-                    s4[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, kv),
-                                                                     __builtin_bit_cast(bf16x8v, qb[j]), s4[st], 0, 0, 0);
-                }
+            for (int j = 0; j < NQK; ++j) {
+                const U4 kv = lds_ld16(kp + 16 * ((2 * j + hi) ^ swz<D>(krow)));
+                acc_s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v, kv),
+                                                                __builtin_bit_cast(bf16x8v, qb[j]), acc_s, 0, 0, 0);
             }
-        }
+            return acc_s;
+        };
+        f32x16v s[2];
+        s[0] = scores(0);
+        if (nsb == 2) s[1] = scores(1);
+        else s[1] = f32x16v{} - INFINITY;             // past every row of the wave
         // causal mask (tiles that reach past the wave's first row only), then one online-softmax
-        // update per tile.  With a positive scale (the usual 1 / sqrt(d)) the maximum is taken on
-        // the raw scores and the scale is folded into the exponent's fused multiply-add.
-        if (!pos_scale) {
-#pragma unroll
-            for (int st = 0; st < kKvTile / 16; ++st) s4[st] *= sc;
-        }
+        // update per tile: the maximum is taken on the raw scores and the scale is folded into
+        // the exponent's fused multiply-add
         if (p_base + kKvTile - 1 > wave_min) {
+            const int lim = my_pos - p_base - 4 * hi;     // register i of half sb is token 32 sb + 8 (i / 4) + i % 4 + 4 hi
 #pragma unroll
-            for (int st = 0; st < kKvTile / 16; ++st) {
+            for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (p_base + 16 * st + 4 * grp4 + i > my_pos) s4[st][i] = -INFINITY;
+                for (int i = 0; i < 16; ++i)
+                    if (32 * sb + 8 * (i >> 2) + (i & 3) > lim) s[sb][i] = -INFINITY;
             }
         }
-        float mx = -INFINITY;
+        float m8[8];                                  // a tree of maxima (independent chains)
 #pragma unroll
-        for (int st = 0; st < kKvTile / 16; ++st)
-            mx = fmaxf(fmaxf(mx, fmaxf(s4[st][0], s4[st][1])), fmaxf(s4[st][2], s4[st][3]));
-        mx = pair16_max(pair32_max(mx)) * se;         // the row's maximum over the tile, scaled
+        for (int i = 0; i < 8; ++i) m8[i] = vmax(vmax(s[0][2 * i], s[0][2 * i + 1]), vmax(s[1][2 * i], s[1][2 * i + 1]));
+        float mx = vmax(vmax(vmax(m8[0], m8[1]), vmax(m8[2], m8[3])), vmax(vmax(m8[4], m8[5]), vmax(m8[6], m8[7])));
+        mx = pair32_max(mx) * se;                     // the row's maximum over the tile, scaled
         if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleThreshold) != 0) {
             const float m_new = fmaxf(m_ref, mx);
             const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);   // 0 on the first tile
             m_ref = m_new;
+            lsum *= alpha;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {             // accumulator rows 4 * grp4 + i take that row's factor
-                const float ai = __int_as_float(
-                    __builtin_amdgcn_ds_bpermute(4 * (4 * grp4 + i), __float_as_int(alpha)));
-                lsum[i] *= ai;
-#pragma unroll
-                for (int t = 0; t < NPV; ++t) acc[t][i] *= ai;
-            }
+            for (int t = 0; t < NPV; ++t) acc[t] *= alpha;
         }
-        uint32_t pw[kKvTile / 16][2];                 // weights rounded to bf16, in pairs
 #pragma unroll
-        for (int st = 0; st < kKvTile / 16; ++st) {
+        for (int sb = 0; sb < 2; ++sb) {
+            if (sb >= nsb) break;
+            uint32_t pw[8];                           // weights rounded to bf16, in pairs (regs 2 e, 2 e + 1)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                bf16x2v pr;
+                pr[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][2 * e], se, -m_ref)));
+                pr[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][2 * e + 1], se, -m_ref)));
+                lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, lsum, false);
+                pw[e] = __builtin_bit_cast(uint32_t, pr);
+            }
+            // out^T += V^T . P^T over the half's two 16-token steps: the B operand's 8 values of a
+            // lane are its weights for tokens 4 hi + {0..3, 8..11} of the step (its registers
+            // 8 h .. 8 h + 7), the A operand's are the same tokens' V values at dim 32 t + lane % 32
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                bf16x2v pr;
-                pr[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s4[st][2 * h], se, -m_ref)));
-                pr[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s4[st][2 * h + 1], se, -m_ref)));
-                pw[st][h] = __builtin_bit_cast(uint32_t, pr);
-            }
-        }
-        // out[row][16 dims] += P . V over 32 tokens per product: the A operand's 8 values of a
-        // lane are its row's weights for tokens 4 grp4 .. +3 of step 2 s and of step 2 s + 1; the
-        // B operand's are the same tokens' V values, two transpose reads
-        const int vsub = 4 * grp4 + ((lane & 15) >> 2);
+                const bf16x8v pb = __builtin_bit_cast(bf16x8v, u32x4v{pw[4 * h], pw[4 * h + 1], pw[4 * h + 2], pw[4 * h + 3]});
+                const int r0 = 32 * sb + 16 * h + vrow, r1 = r0 + 8;
 #pragma unroll
-        for (int sp = 0; sp < kKvTile / 32; ++sp) {
-            if (2 * sp >= nst) break;
-            const bf16x8v pa = __builtin_bit_cast(bf16x8v, u32x4v{pw[2 * sp][0], pw[2 * sp][1], pw[2 * sp + 1][0],
-                                                                 pw[2 * sp + 1][1]});
-            lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, ones, lsum, 0, 0, 0);   // row sums of the rounded weights
-            const int r0 = 32 * sp + vsub, r1 = r0 + 16;
-#pragma unroll
-            for (int t = 0; t < NPV; ++t) {
-                const int c = 2 * t + ((lane & 3) >> 1);
-                const i16x4v v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (PA_LDS i16x4v*)(vt + r0 * ROWB + 16 * (c ^ swz<D>(r0)) + 8 * (lane & 1)));
-                const i16x4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (PA_LDS i16x4v*)(vt + r1 * ROWB + 16 * (c ^ swz<D>(r1)) + 8 * (lane & 1)));
-                const i16x8v vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8v, vv), acc[t], 0, 0, 0);
+                for (int t = 0; t < NPV; ++t) {
+                    const int c = 4 * t + vchunk;
+                    const i16x4v v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (PA_LDS i16x4v*)(vt + r0 * ROWB + 16 * (c ^ swz<D>(r0)) + vbyte));
+                    const i16x4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (PA_LDS i16x4v*)(vt + r1 * ROWB + 16 * (c ^ swz<D>(r1)) + vbyte));
+                    const i16x8v vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v, vv), pb, acc[t], 0, 0, 0);
+                }
             }
         }
     }
 
-    // normalise each row and write it (rows past the request's new tokens are not written)
+    // normalise the row and write it (rows past the request's new tokens are not written)
     const bool any_bad = __syncthreads_or(bad) || len_bad;
-    uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+    const float denom = pair32_sum(lsum);
+    const int tok = t0q + r / G;
+    if (tok >= n) return;
+    const float inv = any_bad ? __builtin_nanf("") : 1.0f / denom;
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + (int64_t(q0 + tok) * hq + int64_t(g) * G + r % G) * D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int ri = 16 * w + 4 * grp4 + i;
-        const float inv = any_bad ? __builtin_nanf("") : 1.0f / lsum[i];
-        const int tok = t0q + ri / G;
-        if (tok >= n) continue;
-        uint16_t* orow = out + (int64_t(q0 + tok) * hq + int64_t(g) * G + ri % G) * D;
+    for (int t = 0; t < NPV; ++t) {
 #pragma unroll
-        for (int t = 0; t < NPV; ++t) gst(orow + 16 * t + col, f32_to_bf16(acc[t][i] * inv));
+        for (int qd = 0; qd < 4; ++qd) {
+            bf16x2v lo, hi2;                              // round to nearest even (hardware conversion)
+            lo[0] = static_cast<__bf16>(acc[t][4 * qd] * inv);
+            lo[1] = static_cast<__bf16>(acc[t][4 * qd + 1] * inv);
+            hi2[0] = static_cast<__bf16>(acc[t][4 * qd + 2] * inv);
+            hi2[1] = static_cast<__bf16>(acc[t][4 * qd + 3] * inv);
+            gst(reinterpret_cast<u32x2v*>(orow + 32 * t + 8 * qd + 4 * hi),
+                u32x2v{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi2)});
+        }
     }
 }
 

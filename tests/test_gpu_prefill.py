@@ -144,6 +144,17 @@ def test_prefill_chunked_equals_whole():
     print(check_close(np.concatenate(parts), whole, "bf16", "chunked vs whole"), flush=True)
 
 
+@pytest.mark.parametrize("scale", [-0.3, 0.0])
+def test_prefill_nonpositive_scale(scale):
+    """A negative scale (its sign moves into q, exactly) and a zero one (every visible token
+    weighted equally) against the oracle, which applies the scale as given."""
+    c = build([37, 164, 90], [37, 64, 20], 8, 2, 128, 16, seed=23)
+    out = out_f64(run_gpu(c, scale))
+    ref = OA.prefill(c["q"], c["okc"], c["ovc"], c["tab"], c["lens"], c["qs"], np.float32(scale), c["bs"],
+                     "bf16", "bf16")
+    print(check_close(out, ref, "bf16", f"prefill scale {scale}"), flush=True)
+
+
 def test_prefill_bad_length_gives_nan_and_bad_range_writes_nothing():
     c = build([40, 40, 40], [10, 10, 10], 8, 2, 64, 16, seed=17)
     lens = c["lens"].copy()
