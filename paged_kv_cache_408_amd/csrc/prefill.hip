@@ -227,6 +227,17 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
     const int vrow = 4 * hi + ((lane & 15) >> 2);
     const int vchunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
     const int vbyte = 8 * (lane & 1);
+    // The swizzle depends on a row's low 4 bits only, so every lane's LDS offsets within a tile
+    // are a per-lane part (below) plus a constant: K row 32 sb + c32 at dims 16 j + 8 hi; V rows
+    // 32 sb + 16 h + vrow (+ 8) at dims 32 t + 4 (l % 4) + 16 ((l / 16) % 2)
+    uint32_t ko[NQK], vo0[NPV], vo1[NPV];
+#pragma unroll
+    for (int j = 0; j < NQK; ++j) ko[j] = c32 * ROWB + 16 * ((2 * j + hi) ^ swz<D>(c32));
+#pragma unroll
+    for (int t = 0; t < NPV; ++t) {
+        vo0[t] = vrow * ROWB + 16 * ((4 * t + vchunk) ^ swz<D>(vrow)) + vbyte;
+        vo1[t] = (vrow + 8) * ROWB + 16 * ((4 * t + vchunk) ^ swz<D>(vrow + 8)) + vbyte;
+    }
 
     // V rows of tile k past what this work-group reads: zero (they may hold anything, and a
     // weight of 0 times a NaN would spoil a row)
@@ -261,12 +272,11 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
 
         // scores of the tile's halves (independent chains of NQK products)
         auto scores = [&](int sb) {
-            const int krow = 32 * sb + c32;
-            const PA_LDS unsigned char* kp = kt + krow * ROWB;
+            const PA_LDS unsigned char* kp = kt + 32 * sb * ROWB;
             f32x16v acc_s = f32x16v{};
 #pragma unroll
             for (int j = 0; j < NQK; ++j) {
-                const U4 kv = lds_ld16(kp + 16 * ((2 * j + hi) ^ swz<D>(krow)));
+                const U4 kv = lds_ld16(kp + ko[j]);
                 acc_s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v, kv),
                                                                 __builtin_bit_cast(bf16x8v, qb[j]), acc_s, 0, 0, 0);
             }
@@ -319,20 +329,18 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const bf16x8v pb = __builtin_bit_cast(bf16x8v, u32x4v{pw[4 * h], pw[4 * h + 1], pw[4 * h + 2], pw[4 * h + 3]});
-                const int r0 = 32 * sb + 16 * h + vrow, r1 = r0 + 8;
+                const PA_LDS unsigned char* vs = vt + (32 * sb + 16 * h) * ROWB;
 #pragma unroll
                 for (int t = 0; t < NPV; ++t) {
-                    const int c = 4 * t + vchunk;
-                    const i16x4v v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (PA_LDS i16x4v*)(vt + r0 * ROWB + 16 * (c ^ swz<D>(r0)) + vbyte));
-                    const i16x4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (PA_LDS i16x4v*)(vt + r1 * ROWB + 16 * (c ^ swz<D>(r1)) + vbyte));
+                    const i16x4v v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4v*)(vs + vo0[t]));
+                    const i16x4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4v*)(vs + vo1[t]));
                     const i16x8v vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
                     acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v, vv), pb, acc[t], 0, 0, 0);
                 }
             }
         }
     }
+
 
     // normalise the row and write it (rows past the request's new tokens are not written)
     const bool any_bad = __syncthreads_or(bad) || len_bad;
