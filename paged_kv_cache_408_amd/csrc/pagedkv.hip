@@ -40,6 +40,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "pa_device.h"
 #include "pa_error.h"
@@ -947,9 +948,17 @@ struct MCfg<PA_DTYPE_MXFP4, D> {
 
 constexpr int kMaxListSeqs = 8192;   // batches up to this size use the compact item list
 
-// 16-byte chunk slot of bf16 chunk c in row `row` of an LDS V tile (D / 8 chunks per row).
+// 16-byte chunk slot of bf16 chunk c in row `row` of an LDS V tile (D / 8 chunks per row):
+// c XOR a per-row mask m.  m / 2 runs through every value on any 8 consecutive rows that share
+// banks, so the transpose reads (2 chunks of 4 rows per 16 lanes, 8 rows per 32) never
+// collide; m % 4 (D = 128) or m % 2 (D = 64, rows r and r + 2 share banks) differs between the
+// rows one write instruction covers, so the fp8 (2 rows x 8 chunks) and 4-bit (4 rows x 4
+// chunks) tile writes do not collide either.  Checked on the CPU for 8-, 16- and 32-lane phases.
 template <int D>
-__device__ __forceinline__ int vt_slot(int row, int c) { return c ^ (2 * (row % (D / 16))); }
+__device__ __forceinline__ int vt_slot(int row, int c) {
+    if constexpr (D == 128) return c ^ ((2 * (row & 7)) ^ ((row ^ (row >> 1)) & 1));
+    else return c ^ ((row & 7) ^ ((row >> 1) & 1));
+}
 
 // 8 fp8 codes (two dwords) -> 8 bf16 values, exact (every E4M3FN value is a bf16 number).
 __device__ __forceinline__ void e4m3x8_to_bf16(uint32_t w0, uint32_t w1, uint32_t (&o)[4]) {
@@ -1097,21 +1106,29 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
                     // block when blocks hold 8 tokens
                     const int b1 = BPP == 2 ? __builtin_amdgcn_readlane(ent_b, k & 63) : b0;
                     const int vr = lane >> 2, part = lane & 3;
-                    const int kr = BPP == 2 ? col % BS : tb % BS + col;
-                    const int vrr = BPP == 2 ? vr % BS : tb % BS + vr;
+                    // one block: uniform base (the pass's first row) + 32-bit lane offsets;
+                    // two blocks of 8 rows: rows 8..15 from the second
+                    const int kr = BPP == 2 ? col % BS : col;
+                    const int vrr = BPP == 2 ? vr % BS : vr;
+                    const uint32_t r0c = BPP == 2 ? 0u : uint32_t(tb % BS) * M::ROWB;   // codes of the first row
+                    const uint32_t r0s = BPP == 2 ? 0u : uint32_t(tb % BS) * M::SGB;    // its scales
                     const unsigned char* kt = kbytes + int64_t((BPP == 2 && col >= BS) ? b1 : b0) * blk_bytes;
                     const unsigned char* vt = vbytes + int64_t((BPP == 2 && vr >= BS) ? b1 : b0) * blk_bytes;
+                    const unsigned char* ktc = kt + r0c;
+                    const unsigned char* vtc = vt + r0c;
+                    const unsigned char* kts = kt + (BS * M::ROWB + r0s);
+                    const unsigned char* vts = vt + (BS * M::ROWB + r0s);
                     if constexpr (D == 128) {
-                        kb[0] = gld16_stream(kt + kr * M::ROWB + 16 * grp4);
-                        vb[0] = gld16_stream(vt + vrr * M::ROWB + 16 * part);
+                        kb[0] = gld16_stream(ktc + uint32_t(kr * M::ROWB + 16 * grp4));
+                        vb[0] = gld16_stream(vtc + uint32_t(vrr * M::ROWB + 16 * part));
                     } else {
-                        const uint2 k8 = gld8(kt + kr * M::ROWB + 8 * grp4);
-                        const uint2 v8 = gld8(vt + vrr * M::ROWB + 8 * part);
+                        const uint2 k8 = gld8(ktc + uint32_t(kr * M::ROWB + 8 * grp4));
+                        const uint2 v8 = gld8(vtc + uint32_t(vrr * M::ROWB + 8 * part));
                         kb[0] = U4{k8.x, k8.y, 0u, 0u};
                         vb[0] = U4{v8.x, v8.y, 0u, 0u};
                     }
-                    kb[1].x = gld_u8(kt + BS * M::ROWB + kr * M::SGB + (D == 128 ? grp4 : grp4 / 2));
-                    vb[1].x = gld_u8(vt + BS * M::ROWB + vrr * M::SGB + (D == 128 ? part : part / 2));
+                    kb[1].x = gld_u8(kts + uint32_t(kr * M::SGB + (D == 128 ? grp4 : grp4 / 2)));
+                    vb[1].x = gld_u8(vts + uint32_t(vrr * M::SGB + (D == 128 ? part : part / 2)));
                 } else if constexpr (BPP == 1) {
                     // one block: uniform base + 32-bit lane offset (+ immediate offsets)
                     const uint32_t row0b = uint32_t(tb % BS) * M::ROWB;
@@ -1140,7 +1157,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
 
             auto compute = [&](int k, U4 (&kb)[M::KLD], U4 (&vb)[M::VLD]) {
                 const int tb = t0 + (w + kWaves * k) * TPP;
-                const bool partial = tb + TPP > t1;
+                // a pass past the end of the partition masks its rows beyond t1; the others
+                // (all but the last) skip every mask
+                auto body = [&](auto partial_c) {
+                constexpr bool partial = decltype(partial_c)::value;
                 // V tile -> LDS as bf16 (rows past the end zeroed: they may hold anything)
                 if constexpr (kMx) {
                     constexpr int NW = D / 32;            // code dwords per lane (8 dims each)
@@ -1150,15 +1170,19 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
                     PA_LDS unsigned char* rowp = tile + vr * M::TROWB;
     #pragma unroll
                     for (int wi = 0; wi < NW; ++wi) {
-                        const U4 c = e2m1x8_to_bf16(u4_get(vb[0], wi), vsf);
-                        lds_st16(rowp + 16 * vt_slot<D>(vr, NW * part + wi), U4{c.x & keep, c.y & keep, c.z & keep, c.w & keep});
+                        U4 c = e2m1x8_to_bf16(u4_get(vb[0], wi), vsf);
+                        if constexpr (partial) c = U4{c.x & keep, c.y & keep, c.z & keep, c.w & keep};
+                        lds_st16(rowp + 16 * vt_slot<D>(vr, NW * part + wi), c);
                     }
                 }
     #pragma unroll
                 for (int r = 0; r < (kMx ? 0 : M::VLD); ++r) {
                     const int ci = 64 * r + lane, vr = ci / M::CPR, c = ci % M::CPR;
-                    const uint32_t keep = (partial && tb + vr >= t1) ? 0u : ~0u;
-                    const U4 v = U4{vb[r].x & keep, vb[r].y & keep, vb[r].z & keep, vb[r].w & keep};
+                    U4 v = vb[r];
+                    if constexpr (partial) {
+                        const uint32_t keep = tb + vr >= t1 ? 0u : ~0u;
+                        v = U4{v.x & keep, v.y & keep, v.z & keep, v.w & keep};
+                    }
                     PA_LDS unsigned char* rowp = tile + vr * M::TROWB;
                     if constexpr (M::E == 2) {
                         lds_st16(rowp + 16 * vt_slot<D>(vr, c), v);
@@ -1210,13 +1234,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
                         for (int t = 0; t < M::NPV; ++t) acc[t][i] *= ai;
                     }
                 }
-                uint32_t pw[4];
+                // weights rounded to bf16 by the hardware conversion (nearest even); the
+                // denominator sums the rounded weights, two at a time
+                uint32_t pw[2];
     #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pw[i] = weight_to_bf16(__builtin_amdgcn_exp2f(sv[i] - m_ref));
-                    l_run += bf16_to_f32(pw[i]);               // the denominator sums the rounded weights
+                for (int h = 0; h < 2; ++h) {
+                    bf16x2v pr;
+                    pr[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[2 * h] - m_ref));
+                    pr[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[2 * h + 1] - m_ref));
+                    l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, __builtin_bit_cast(bf16x2v, 0x3f803f80u), l_run, false);
+                    pw[h] = __builtin_bit_cast(uint32_t, pr);
                 }
-                const i16x4v pa = __builtin_bit_cast(i16x4v, make_uint2(pw[0] | (pw[1] << 16), pw[2] | (pw[3] << 16)));
+                const i16x4v pa = __builtin_bit_cast(i16x4v, make_uint2(pw[0], pw[1]));
                 // out[head][dims] += P . V, V read back token-major per dim
                 const int vrow = 4 * grp4 + ((lane & 15) >> 2);
     #pragma unroll
@@ -1226,6 +1255,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
                     const i16x4v vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4v*)src);
                     acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vt, acc[t], 0, 0, 0);
                 }
+                };
+                if (tb + TPP > t1) body(std::true_type{});
+                else body(std::false_type{});
             };
 
             {
