@@ -45,7 +45,7 @@ METRIC = "decode attention KV GB/s and % of HBM peak (GQA 32q/8kv d128, bf16)"
 HBM_PEAK_GBPS = 8000.0
 DECODE_KERNEL = "decode_mfma_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama3_8b_bf16_traffic.md")
-KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_408_amd", "csrc", f) for f in ("pagedkv.hip", "pa_device.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_408_amd", "csrc", f) for f in ("pagedkv.hip", "pa_device.h", "pa_layout.h")]
 
 
 def log(msg):

@@ -30,7 +30,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{IN
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-munsafe-fp-atomics"]
 SOURCES = ["pagedkv.hip", "prefill.hip", "allocator.cpp", "pa_error.cpp"]
-HEADERS = ["pa_error.h", "pa_device.h"]
+HEADERS = ["pa_error.h", "pa_device.h", "pa_layout.h"]
 
 
 def _digest(src: str, flags) -> str:

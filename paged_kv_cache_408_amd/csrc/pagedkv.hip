@@ -43,6 +43,7 @@
 #include <type_traits>
 
 #include "pa_device.h"
+#include "pa_layout.h"
 #include "pa_error.h"
 #include "../../include/pagedkv.h"
 
@@ -947,18 +948,6 @@ struct MCfg<PA_DTYPE_MXFP4, D> {
 };
 
 constexpr int kMaxListSeqs = 8192;   // batches up to this size use the compact item list
-
-// 16-byte chunk slot of bf16 chunk c in row `row` of an LDS V tile (D / 8 chunks per row):
-// c XOR a per-row mask m.  m / 2 runs through every value on any 8 consecutive rows that share
-// banks, so the transpose reads (2 chunks of 4 rows per 16 lanes, 8 rows per 32) never
-// collide; m % 4 (D = 128) or m % 2 (D = 64, rows r and r + 2 share banks) differs between the
-// rows one write instruction covers, so the fp8 (2 rows x 8 chunks) and 4-bit (4 rows x 4
-// chunks) tile writes do not collide either.  Checked on the CPU for 8-, 16- and 32-lane phases.
-template <int D>
-__device__ __forceinline__ int vt_slot(int row, int c) {
-    if constexpr (D == 128) return c ^ ((2 * (row & 7)) ^ ((row ^ (row >> 1)) & 1));
-    else return c ^ ((row & 7) ^ ((row >> 1) & 1));
-}
 
 // 8 fp8 codes (two dwords) -> 8 bf16 values, exact (every E4M3FN value is a bf16 number).
 __device__ __forceinline__ void e4m3x8_to_bf16(uint32_t w0, uint32_t w1, uint32_t (&o)[4]) {

@@ -28,6 +28,7 @@
 // of its rows.  Rows are normalised in registers and written as bf16.
 
 #include "pa_device.h"
+#include "pa_layout.h"
 #include "pa_error.h"
 #include "../../include/pagedkv.h"
 
@@ -73,22 +74,8 @@ constexpr int kPRows = kWRows * kPWaves;   // query rows per work-group
 constexpr int kKvTile = 64;            // KV tokens per LDS tile
 constexpr int kRW = kKvTile / kPWaves; // token rows of a tile each wave loads
 
-// Slot XOR of a K/V tile row in LDS: chunk c of tile row R sits at slot c ^ swz(R).  Chosen so
-// that both LDS read patterns are free of bank conflicts (64 banks of 4 bytes), checked for 8-,
-// 16- and 32-lane phases:
-//  - the K operand reads one chunk of 32 consecutive rows: 16 consecutive rows must land on
-//    different banks (D = 128: every row covers all banks once, so swz is a bijection of R % 16;
-//    D = 64: rows of equal parity share banks, so a bijection of (R / 2) % 8);
-//  - the transpose reads of V take 4 chunks (32 dims) of 4 consecutive rows per 32 lanes: the
-//    chunk groups must be disjoint among rows that share banks.
 // NaN-propagating maximum (v_maximum3_f32 on gfx950: no canonicalising moves before it)
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
-
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-    if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
-    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-}
 
 template <int D, int BS, int G>
 __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs a) {
@@ -178,13 +165,13 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
     };
     read_entries(0);
 
-    // DMA layout: tile row R holds its chunk c at slot c ^ swz(R); lane `lane` of the
+    // DMA layout: tile row R holds its chunk c at slot c ^ prefill_swz(R); lane `lane` of the
     // wave's instruction i fills position 64 i + lane of the wave's kRW-row slice
     uint32_t src_off[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int pos = 64 * i + lane, row = pos / CPR, slot = pos % CPR;
-        src_off[i] = uint32_t(row) * ROWB + 16u * uint32_t(slot ^ swz<D>(kRW * w + row));
+        src_off[i] = uint32_t(row) * ROWB + 16u * uint32_t(slot ^ prefill_swz<D>(kRW * w + row));
     }
     const int64_t blk_bytes = int64_t(a.hkv) * BS * ROWB;
     const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(a.k_cache) + int64_t(g) * BS * ROWB;
@@ -232,11 +219,11 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
     // 32 sb + 16 h + vrow (+ 8) at dims 32 t + 4 (l % 4) + 16 ((l / 16) % 2)
     uint32_t ko[NQK], vo0[NPV], vo1[NPV];
 #pragma unroll
-    for (int j = 0; j < NQK; ++j) ko[j] = c32 * ROWB + 16 * ((2 * j + hi) ^ swz<D>(c32));
+    for (int j = 0; j < NQK; ++j) ko[j] = c32 * ROWB + 16 * ((2 * j + hi) ^ prefill_swz<D>(c32));
 #pragma unroll
     for (int t = 0; t < NPV; ++t) {
-        vo0[t] = vrow * ROWB + 16 * ((4 * t + vchunk) ^ swz<D>(vrow)) + vbyte;
-        vo1[t] = (vrow + 8) * ROWB + 16 * ((4 * t + vchunk) ^ swz<D>(vrow + 8)) + vbyte;
+        vo0[t] = vrow * ROWB + 16 * ((4 * t + vchunk) ^ prefill_swz<D>(vrow)) + vbyte;
+        vo1[t] = (vrow + 8) * ROWB + 16 * ((4 * t + vchunk) ^ prefill_swz<D>(vrow + 8)) + vbyte;
     }
 
     // V rows of tile k past what this work-group reads: zero (they may hold anything, and a
