@@ -522,8 +522,10 @@ def run_prefill(args):
     """Causal paged prefill, Llama-3-8B shape (32 q / 8 KV heads, head_dim 128, bf16, block
     16) on seeded synthetic K/V and q in a seeded-permutation pool: 16 requests x (1024 cached
     + 1024 new tokens) (a chunk after a prefix-cache hit), 4 x 4096 new tokens with no context
-    and 1 x 16384.  Each shape is run warmup + steps times; pa_prefill is timed with HIP events
-    on the launch stream (median); flops are the algorithmic ones (visible pairs only)."""
+    and 1 x 16384; the first shape also over an fp8 cache (random codes, per-head scale 0.01)
+    and a 4-bit MXFP4 cache (random codes, block scale 2^-7).  Each case is run warmup + steps
+    times; pa_prefill is timed with HIP events on the launch stream (median); flops are the
+    algorithmic ones (visible pairs only)."""
     import numpy as np
     import torch
 
@@ -535,21 +537,40 @@ def run_prefill(args):
 
     dev = torch.device("cuda:0")
     Hq, Hkv, d, bs = 32, 8, 128, 16
-    for B, ctx, n in ((16, 1024, 1024), (4, 0, 4096), (1, 0, 16384)):
+    def cache(fmt, N, g):
+        if fmt == "bf16":
+            return (torch.randn((N, Hkv, bs, d), generator=g, device=dev) * 0.5).to(torch.bfloat16)
+        if fmt == "fp8":        # codes 0x00..0x7D and their negatives: no NaN code
+            c = torch.randint(0, 0x7E, (N, Hkv, bs, d), generator=g, device=dev, dtype=torch.int32)
+            sign = torch.randint(0, 2, (N, Hkv, bs, d), generator=g, device=dev, dtype=torch.int32) << 7
+            return (c | sign).to(torch.uint8)
+        c = pk.mxfp4_cache(N, Hkv, bs, d, dev)
+        flat = c.view(N, Hkv, -1)
+        ncode = bs * d // 2
+        flat[:, :, :ncode] = torch.randint(0, 256, (N, Hkv, ncode), generator=g, device=dev,
+                                           dtype=torch.int32).to(torch.uint8)
+        flat[:, :, ncode:] = 120
+        return c
+
+    cases = [(16, 1024, 1024, "bf16"), (4, 0, 4096, "bf16"), (1, 0, 16384, "bf16"),
+             (16, 1024, 1024, "fp8"), (16, 1024, 1024, "mxfp4")]
+    for B, ctx, n, fmt in cases:
         L = ctx + n
         nb = -(-L // bs)
         N = B * nb + 16
         g = torch.Generator(device=dev)
         g.manual_seed(408_300 + B)
-        kc = (torch.randn((N, Hkv, bs, d), generator=g, device=dev) * 0.5).to(torch.bfloat16)
-        vc = (torch.randn((N, Hkv, bs, d), generator=g, device=dev) * 0.5).to(torch.bfloat16)
+        kc, vc = cache(fmt, N, g), cache(fmt, N, g)
+        kw = {}
+        if fmt == "fp8":
+            kw = dict(k_scale=torch.full((Hkv,), 0.01, device=dev), v_scale=torch.full((Hkv,), 0.01, device=dev))
         perm = torch.from_numpy(np.random.Generator(np.random.PCG64(np.random.SeedSequence(408_301))).permutation(N)[: B * nb])
         tab = perm.reshape(B, nb).to(torch.int32).to(dev)
         lens = torch.full((B,), L, dtype=torch.int32, device=dev)
         qs = (torch.arange(B + 1, dtype=torch.int32) * n).to(dev)
         q = (torch.randn((B * n, Hq, d), generator=g, device=dev) * 0.5).to(torch.bfloat16)
         out = torch.empty_like(q)
-        call = lambda: pk.pa_prefill(out, q, kc, vc, tab, lens, qs, 1 / math.sqrt(d), bs, max_query_len=n, max_seq_len=L)
+        call = lambda: pk.pa_prefill(out, q, kc, vc, tab, lens, qs, 1 / math.sqrt(d), bs, max_query_len=n, max_seq_len=L, **kw)
         for _ in range(max(args.warmup, 1)):
             call()
         torch.cuda.synchronize()
@@ -563,7 +584,7 @@ def run_prefill(args):
         med = us[len(us) // 2]
         fl = prefill_flops([ctx] * B, [n] * B, Hq, d)
         print(json.dumps({
-            "workload": f"prefill {B} x ({ctx} cached + {n} new), 32 q / 8 kv heads, d 128, bf16, block 16",
+            "workload": f"prefill {B} x ({ctx} cached + {n} new), 32 q / 8 kv heads, d 128, {fmt} cache, block 16",
             "metric": "causal prefill TFLOP/s", "unit": "TFLOP/s", "kernel": "prefill_kernel",
             "us_median": round(med, 2), "us_min": round(us[0], 2), "algorithmic_flops": int(fl),
             "tflops": round(fl / med / 1e6, 1), "pct_of_bf16_mfma_peak": round(100 * fl / med / 1e6 / MFMA_BF16_PEAK_TFLOPS, 2),

@@ -193,8 +193,12 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  *  block_tables  device, int32 [num_seqs][max_blocks_per_seq]
  *  max_query_len host upper bound of n; max_seq_len host upper bound of L
  *
- * Supported: bf16 q and cache, head_dim {64, 128}, block_size {8, 16, 32, 128},
- * num_q_heads / num_kv_heads in {1, 4, 8}.  One kernel launch; no workspace.  A request whose
+ *  k_scale, v_scale  device, float32 [num_kv_heads]: required for an fp8 cache (K_j, V_j are
+ *                then the stored values times the head's scale, as in pa_decode), ignored
+ *                otherwise; an MXFP4 cache carries its own scales
+ *
+ * Supported: bf16 q; bf16, fp8 E4M3 or MXFP4 cache; head_dim {64, 128}, block_size {8, 16, 32,
+ * 128}, num_q_heads / num_kv_heads in {1, 4, 8}.  One kernel launch; no workspace.  A request whose
  * query range is inconsistent (decreasing, negative or past num_query_tokens) is not written;
  * one with n > L, n > max_query_len, L > max_seq_len or L > max_blocks_per_seq * block_size,
  * or whose table holds an id outside [0, num_blocks) where positions are read, gets NaN in the
@@ -204,7 +208,8 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
                float scale, int32_t block_size, int32_t num_seqs, int64_t num_query_tokens,
                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
                int32_t max_blocks_per_seq, int32_t max_query_len, int32_t max_seq_len,
-               int32_t q_dtype, int32_t cache_dtype, void* stream);
+               int32_t q_dtype, int32_t cache_dtype, const float* k_scale, const float* v_scale,
+               void* stream);
 
 /* ---------------------------------------------------------------- block copy
  *

@@ -94,7 +94,7 @@ def load(path: str = LIB_PATH):
         "pa_seq_append_tokens": (ctypes.c_int, [P, I64, P, I32, P, P, P]),
         "pa_alloc_dump_cached": (ctypes.c_int, [P, P]),
         "pa_prefill": (ctypes.c_int, [P, P, P, P, P, P, P, F32, I32, I32, I64, I32, I32, I32, I64, I32, I32, I32,
-                                      I32, I32, P]),
+                                      I32, I32, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -296,11 +296,12 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, block_siz
 
 
 def pa_prefill(out, q, k_cache, v_cache, block_tables, seq_lens, query_start, scale, block_size, *,
-               max_query_len=None, max_seq_len=None, stream=None):
+               max_query_len=None, max_seq_len=None, k_scale=None, v_scale=None, stream=None):
     """Causal attention of each request's new tokens (q rows query_start[b]..query_start[b+1]-1,
     the request's last tokens, K/V already written) over its cached tokens; see pa_prefill in
-    include/pagedkv.h.  max_query_len / max_seq_len default to the values read from the
-    device tensors (a synchronising copy)."""
+    include/pagedkv.h.  The cache may be bf16, fp8 (k_scale / v_scale: float32 [num_kv_heads])
+    or MXFP4.  max_query_len / max_seq_len default to the values read from the device tensors
+    (a synchronising copy)."""
     T, Hq, d = q.shape
     N, Hkv, bs, _, cdt = _cache_geom(k_cache, "k_cache")
     B = seq_lens.shape[0]
@@ -315,7 +316,8 @@ def pa_prefill(out, q, k_cache, v_cache, block_tables, seq_lens, query_start, sc
                            _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"),
                            _dev(query_start, "query_start"), float(scale), int(block_size), B, T, Hq, Hkv, d, N,
                            block_tables.shape[1], int(max_query_len), int(max_seq_len),
-                           _dtype_code(q, "q"), cdt, _stream(stream))
+                           _dtype_code(q, "q"), cdt, _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"),
+                           _stream(stream))
     _check(rc)
 
 

@@ -168,6 +168,15 @@ __device__ __forceinline__ uint32_t weight_to_bf16(float f) {
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// 8 fp8 codes (two dwords) -> 8 bf16 values, exact (every E4M3FN value is a bf16 number).
+__device__ __forceinline__ void e4m3x8_to_bf16(uint32_t w0, uint32_t w1, uint32_t (&o)[4]) {
+    // gfx950's scaled pair conversion with a scale of 1: one instruction per two values
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w0), 1.0f, false));
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w0), 1.0f, true));
+    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w1), 1.0f, false));
+    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w1), 1.0f, true));
+}
+
 // ------------------------------------------------------------------ MXFP4 (OCP microscaling, 4-bit)
 
 // E8M0 scale byte -> its float32 value 2^(byte - 127) (0xFF gives infinity, so the block

@@ -949,14 +949,6 @@ struct MCfg<PA_DTYPE_MXFP4, D> {
 
 constexpr int kMaxListSeqs = 8192;   // batches up to this size use the compact item list
 
-// 8 fp8 codes (two dwords) -> 8 bf16 values, exact (every E4M3FN value is a bf16 number).
-__device__ __forceinline__ void e4m3x8_to_bf16(uint32_t w0, uint32_t w1, uint32_t (&o)[4]) {
-    // gfx950's scaled pair conversion with a scale of 1: one instruction per two values
-    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w0), 1.0f, false));
-    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w0), 1.0f, true));
-    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w1), 1.0f, false));
-    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w1), 1.0f, true));
-}
 
 template <int CDT, int QDT, int D, int BS, int G>
 __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeArgs a) {

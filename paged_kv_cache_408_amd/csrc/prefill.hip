@@ -26,6 +26,8 @@
 //    accumulators of a lane all belong to its row and take its rescale factor directly.
 // Half tiles past all of a wave's rows are skipped; tiles are loaded once per work-group for all
 // of its rows.  Rows are normalised in registers and written as bf16.
+// fp8 and 4-bit caches: each wave loads its rows of the next tile into registers and writes
+// them, widened to bf16 (exactly), into the same LDS tile; the compute part is the same.
 
 #include "pa_device.h"
 #include "pa_layout.h"
@@ -47,6 +49,8 @@ struct PrefillArgs {
     const int32_t* block_tables;
     const int32_t* seq_lens;
     const int32_t* query_start;
+    const float* k_scale;       // fp8 caches: per KV head
+    const float* v_scale;
     float score_scale;          // scale * log2(e)
     int num_seqs;
     int hkv;
@@ -77,8 +81,16 @@ constexpr int kRW = kKvTile / kPWaves; // token rows of a tile each wave loads
 // NaN-propagating maximum (v_maximum3_f32 on gfx950: no canonicalising moves before it)
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
-template <int D, int BS, int G>
+template <int CDT, int D, int BS, int G>
 __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs a) {
+    // bf16 caches: tiles straight from HBM into LDS by DMA.  fp8 and 4-bit caches: each wave
+    // loads its rows of the next tile into registers one tile ahead and writes them to the
+    // same LDS tile widened to bf16 (exactly: every E4M3 value, and every E2M1 value times its
+    // block's power of two, is a bf16 number); fp8's per-head scales go into the score scale
+    // and the output.
+    constexpr bool kQ = CDT != PA_DTYPE_BF16;
+    constexpr bool kMx = CDT == PA_DTYPE_MXFP4;
+    static_assert(CDT == PA_DTYPE_BF16 || CDT == PA_DTYPE_FP8_E4M3 || CDT == PA_DTYPE_MXFP4, "cache type");
     constexpr int ROWB = D * 2;                 // bytes of one bf16 token row
     constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
     constexpr int NQK = D / 16;                 // 32x32x16 products per 32 tokens (scores)
@@ -89,6 +101,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
     constexpr int TB = kKvTile * ROWB;          // bytes of one K (or V) tile
     constexpr int WPB = BS < kRW ? 2 : 1;       // blocks behind one wave's kRW token rows
     static_assert(NI >= 1 && RPI <= BS && (WPB == 1 || 2 * BS == kRW), "tile shape");
+    static_assert(!kQ || (kRW == 8 && WPB == 1 && kStages == 2), "quantized tiles: 8 rows per wave from one block, one tile ahead");
     static_assert(G == 1 || G == 4 || G == 8, "query heads per KV head");
 
     __shared__ __align__(16) unsigned char s_kv[kStages][2][TB];   // [stage][K, V][64 rows]
@@ -126,7 +139,12 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
     // same dims of its token row).  The scale's sign goes into q (negating bf16 values and
     // every score is exact), so the softmax always works with a positive factor in the
     // exponent; a zero scale becomes q = 0 (every visible token weighted equally).
-    const float sc = a.score_scale;
+    float sc = a.score_scale;
+    float vsc = 1.0f;
+    if constexpr (CDT == PA_DTYPE_FP8_E4M3) {
+        sc *= __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gld_f32(a.k_scale + g))));
+        vsc = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gld_f32(a.v_scale + g))));
+    }
     const float se = sc > 0.0f ? sc : sc < 0.0f ? -sc : 1.0f;
     const uint32_t qflip = sc < 0.0f ? 0x80008000u : 0u;
     const uint32_t qkeep = sc == 0.0f ? 0u : 0xffffffffu;
@@ -177,7 +195,82 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
     const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(a.k_cache) + int64_t(g) * BS * ROWB;
     const unsigned char* vbytes = reinterpret_cast<const unsigned char*>(a.v_cache) + int64_t(g) * BS * ROWB;
 
+    // quantized tiles: lane l loads row l / 8 of the wave's 8 rows, dims (D / 8) (l % 8) ..
+    // + D / 8: fp8 D / 8 bytes; 4-bit D / 16 code bytes and the scale byte of their block
+    constexpr int QCB = kMx ? D / 16 : D / 8;             // cache bytes per lane (codes)
+    constexpr int64_t kQTile = kMx ? int64_t(BS) * (D / 2 + D / 32) : int64_t(BS) * D;   // (block, head) tile bytes
+    const int qrow = lane >> 3, qcf = lane & 7;
+    uint32_t qk[QCB / 4 > 0 ? QCB / 4 : 1], qv[QCB / 4 > 0 ? QCB / 4 : 1];   // pending codes (one tile ahead)
+    uint32_t qks = 0, qvs = 0;                             // pending 4-bit scale bytes
+    auto issue_q = [&](int k) {
+        if ((k & 63) == 0 && k > 0) read_entries(k);
+        const int b0 = __builtin_amdgcn_readlane(ent_a, k & 63);
+        const int rib = (kKvTile * k + kRW * w) % BS + qrow;   // row inside the block
+        const int64_t tbase = (int64_t(b0) * a.hkv + g) * kQTile;
+        const unsigned char* kt = reinterpret_cast<const unsigned char*>(a.k_cache) + tbase;
+        const unsigned char* vt = reinterpret_cast<const unsigned char*>(a.v_cache) + tbase;
+        const uint32_t co = uint32_t(rib * (kMx ? D / 2 : D) + QCB * qcf);
+        if constexpr (QCB == 16) {
+            const U4 x = gld16(kt + co), y = gld16(vt + co);
+            qk[0] = x.x; qk[1] = x.y; qk[2] = x.z; qk[3] = x.w;
+            qv[0] = y.x; qv[1] = y.y; qv[2] = y.z; qv[3] = y.w;
+        } else if constexpr (QCB == 8) {
+            const uint2 x = gld8(kt + co), y = gld8(vt + co);
+            qk[0] = x.x; qk[1] = x.y;
+            qv[0] = y.x; qv[1] = y.y;
+        } else {
+            qk[0] = *(const PA_GLOBAL uint32_t*)(kt + co);
+            qv[0] = *(const PA_GLOBAL uint32_t*)(vt + co);
+        }
+        if constexpr (kMx) {
+            const uint32_t so = uint32_t(BS * (D / 2) + rib * (D / 32) + (qcf * (D / 8)) / 32);
+            qks = gld_u8(kt + so);
+            qvs = gld_u8(vt + so);
+        }
+    };
+    // the pending rows of tile k, widened to bf16, into `stage`; rows past what this
+    // work-group reads are zero.  The two chunks a lane writes go in the order that keeps
+    // rows 2i and 2i + 1 on different banks.
+    auto store_q = [&](int k, int stage) {
+        constexpr int NC = D / 64;                          // bf16 chunks per lane
+        const int R = kRW * w + qrow;                       // tile row
+        const bool live = kKvTile * k + R < kv_end;
+        U4 ck[NC], cv[NC];
+        if constexpr (kMx) {
+            const float ksf = e8m0_to_f32(qks), vsf = e8m0_to_f32(qvs);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                ck[c] = e2m1x8_to_bf16(qk[c], ksf);
+                cv[c] = e2m1x8_to_bf16(qv[c], vsf);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                uint32_t o[4];
+                e4m3x8_to_bf16(qk[2 * c], qk[2 * c + 1], o);
+                ck[c] = U4{o[0], o[1], o[2], o[3]};
+                e4m3x8_to_bf16(qv[2 * c], qv[2 * c + 1], o);
+                cv[c] = U4{o[0], o[1], o[2], o[3]};
+            }
+        }
+        PA_LDS unsigned char* dk = (PA_LDS unsigned char*)&s_kv[stage][0][0] + R * ROWB;
+        PA_LDS unsigned char* dv = (PA_LDS unsigned char*)&s_kv[stage][1][0] + R * ROWB;
+        const int sw = prefill_swz<D>(R);
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            const int c = NC == 2 ? (i ^ (R & 1)) : i;
+            const int slot = (NC * qcf + c) ^ sw;
+            lds_st16(dk + 16 * slot, live ? ck[c] : U4{0, 0, 0, 0});
+            lds_st16(dv + 16 * slot, live ? cv[c] : U4{0, 0, 0, 0});
+        }
+    };
+
     auto issue = [&](int k, int bf) {
+        if constexpr (kQ) {
+            issue_q(k);
+            (void)bf;
+            return;
+        }
         if ((k & 63) == 0 && k > 0) read_entries(k);
         const int pos0 = kKvTile * k + kRW * w;
         const int b0 = __builtin_amdgcn_readlane(ent_a, k & 63);
@@ -244,9 +337,13 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
         if (k < ntiles) issue(k, k);
     int bf = 0;                                       // stage of tile k
     for (int k = 0; k < ntiles; ++k) {
-        if (kStages == 3 && k + 1 < ntiles) wait_vmem<2 * NI>();   // tile k + 1 may still be in flight
-        else wait_vmem<0>();                          // this wave's rows of tile k have landed
-        zero_tail(k, bf);
+        if constexpr (kQ) {
+            store_q(k, bf);                           // this wave's rows of tile k, widened
+        } else {
+            if (kStages == 3 && k + 1 < ntiles) wait_vmem<2 * NI>();   // tile k + 1 may still be in flight
+            else wait_vmem<0>();                      // this wave's rows of tile k have landed
+            zero_tail(k, bf);
+        }
         __syncthreads();                              // tile k complete; tile k - 1 no longer read
         if (k + kStages - 1 < ntiles) issue(k + kStages - 1, bf == 0 ? kStages - 1 : bf - 1);   // the stage of tile k - 1
         const int bf_cur = bf;
@@ -334,7 +431,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
     const float denom = pair32_sum(lsum);
     const int tok = t0q + r / G;
     if (tok >= n) return;
-    const float inv = any_bad ? __builtin_nanf("") : 1.0f / denom;
+    const float inv = any_bad ? __builtin_nanf("") : vsc / denom;
     uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + (int64_t(q0 + tok) * hq + int64_t(g) * G + r % G) * D;
 #pragma unroll
     for (int t = 0; t < NPV; ++t) {
@@ -351,12 +448,12 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
     }
 }
 
-template <int D, int BS>
+template <int CDT, int D, int BS>
 int launch_g(int G, const PrefillArgs& a, dim3 grid, hipStream_t st) {
     switch (G) {
-        case 1: hipLaunchKernelGGL((prefill_kernel<D, BS, 1>), grid, dim3(kPThreads), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((prefill_kernel<D, BS, 4>), grid, dim3(kPThreads), 0, st, a); break;
-        case 8: hipLaunchKernelGGL((prefill_kernel<D, BS, 8>), grid, dim3(kPThreads), 0, st, a); break;
+        case 1: hipLaunchKernelGGL((prefill_kernel<CDT, D, BS, 1>), grid, dim3(kPThreads), 0, st, a); break;
+        case 4: hipLaunchKernelGGL((prefill_kernel<CDT, D, BS, 4>), grid, dim3(kPThreads), 0, st, a); break;
+        case 8: hipLaunchKernelGGL((prefill_kernel<CDT, D, BS, 8>), grid, dim3(kPThreads), 0, st, a); break;
         default: return fail(PA_ERR_UNSUPPORTED, "pa_prefill: %d query heads per KV head not in {1, 4, 8}", G);
     }
     const hipError_t e = hipGetLastError();
@@ -364,13 +461,13 @@ int launch_g(int G, const PrefillArgs& a, dim3 grid, hipStream_t st) {
     return PA_OK;
 }
 
-template <int D>
+template <int CDT, int D>
 int launch_bs(int BS, int G, const PrefillArgs& a, dim3 grid, hipStream_t st) {
     switch (BS) {
-        case 8: return launch_g<D, 8>(G, a, grid, st);
-        case 16: return launch_g<D, 16>(G, a, grid, st);
-        case 32: return launch_g<D, 32>(G, a, grid, st);
-        case 128: return launch_g<D, 128>(G, a, grid, st);
+        case 8: return launch_g<CDT, D, 8>(G, a, grid, st);
+        case 16: return launch_g<CDT, D, 16>(G, a, grid, st);
+        case 32: return launch_g<CDT, D, 32>(G, a, grid, st);
+        case 128: return launch_g<CDT, D, 128>(G, a, grid, st);
         default: return fail(PA_ERR_UNSUPPORTED, "pa_prefill: block_size %d not in {8, 16, 32, 128}", BS);
     }
 }
@@ -384,11 +481,15 @@ extern "C" int pa_prefill(void* out, const void* q, const void* k_cache, const v
                           float scale, int32_t block_size, int32_t num_seqs, int64_t num_query_tokens,
                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
                           int32_t max_blocks_per_seq, int32_t max_query_len, int32_t max_seq_len,
-                          int32_t q_dtype, int32_t cache_dtype, void* stream) {
+                          int32_t q_dtype, int32_t cache_dtype, const float* k_scale, const float* v_scale,
+                          void* stream) {
     pagedkv::clear_error();
-    if (q_dtype != PA_DTYPE_BF16 || cache_dtype != PA_DTYPE_BF16)
-        return fail(PA_ERR_UNSUPPORTED, "pa_prefill: (q dtype %d, cache dtype %d) not supported (bf16, bf16 only)",
+    if (q_dtype != PA_DTYPE_BF16 ||
+        (cache_dtype != PA_DTYPE_BF16 && cache_dtype != PA_DTYPE_FP8_E4M3 && cache_dtype != PA_DTYPE_MXFP4))
+        return fail(PA_ERR_UNSUPPORTED, "pa_prefill: (q dtype %d, cache dtype %d) not supported (bf16 q; bf16, fp8 or 4-bit cache)",
                     q_dtype, cache_dtype);
+    if (cache_dtype == PA_DTYPE_FP8_E4M3 && (!k_scale || !v_scale))
+        return fail(PA_ERR_INVALID, "pa_prefill: fp8 cache needs k_scale and v_scale");
     if (num_seqs < 0 || num_query_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
         max_blocks_per_seq < 0 || max_query_len < 0 || max_seq_len < 0)
         return fail(PA_ERR_INVALID, "pa_prefill: negative or zero size");
@@ -401,6 +502,8 @@ extern "C" int pa_prefill(void* out, const void* q, const void* k_cache, const v
         return fail(PA_ERR_INVALID, "pa_prefill: NULL pointer");
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return fail(PA_ERR_INVALID, "pa_prefill: out, q and caches must be 16-byte aligned");
+    if (cache_dtype != PA_DTYPE_BF16 && block_size < 8)
+        return fail(PA_ERR_UNSUPPORTED, "pa_prefill: block_size %d below 8", block_size);
     if (int64_t(max_blocks_per_seq) * block_size < max_seq_len)
         return fail(PA_ERR_INVALID, "pa_prefill: max_blocks_per_seq * block_size < max_seq_len");
     if (max_query_len > max_seq_len) return fail(PA_ERR_INVALID, "pa_prefill: max_query_len > max_seq_len");
@@ -423,6 +526,8 @@ extern "C" int pa_prefill(void* out, const void* q, const void* k_cache, const v
     a.block_tables = block_tables;
     a.seq_lens = seq_lens;
     a.query_start = query_start;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
     a.score_scale = scale * kLog2e;
     a.num_seqs = num_seqs;
     a.hkv = num_kv_heads;
@@ -434,6 +539,15 @@ extern "C" int pa_prefill(void* out, const void* q, const void* k_cache, const v
     a.num_query_tokens = num_query_tokens;
     const dim3 grid(static_cast<unsigned>(qtiles * num_seqs), static_cast<unsigned>(num_kv_heads));
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (head_dim == 64) return launch_bs<64>(block_size, G, a, grid, st);
-    return launch_bs<128>(block_size, G, a, grid, st);
+    switch (cache_dtype) {
+        case PA_DTYPE_FP8_E4M3:
+            return head_dim == 64 ? launch_bs<PA_DTYPE_FP8_E4M3, 64>(block_size, G, a, grid, st)
+                                  : launch_bs<PA_DTYPE_FP8_E4M3, 128>(block_size, G, a, grid, st);
+        case PA_DTYPE_MXFP4:
+            return head_dim == 64 ? launch_bs<PA_DTYPE_MXFP4, 64>(block_size, G, a, grid, st)
+                                  : launch_bs<PA_DTYPE_MXFP4, 128>(block_size, G, a, grid, st);
+        default:
+            return head_dim == 64 ? launch_bs<PA_DTYPE_BF16, 64>(block_size, G, a, grid, st)
+                                  : launch_bs<PA_DTYPE_BF16, 128>(block_size, G, a, grid, st);
+    }
 }

@@ -28,10 +28,11 @@ def _announce(request):
     yield
 
 
-def build(lens, n_new, Hq, Hkv, d, bs, seed, prefix=0, n_sharers=0, spare=3):
+def build(lens, n_new, Hq, Hkv, d, bs, seed, prefix=0, n_sharers=0, spare=3, fmt="bf16"):
     """Requests 0..n_sharers-1 hold a `prefix`-token shared prefix (written once by a holder,
     forked, released) before their own tokens; every request ends with n_new[b] new tokens
-    among its lens[b].  Returns the library side and the oracle side."""
+    among its lens[b].  fmt: the cache format (bf16, fp8 with per-head scales amax / 448, or
+    mxfp4); unused slots hold NaN patterns.  Returns the library side and the oracle side."""
     rng = np.random.default_rng(seed)
     B = len(lens)
     holder = B
@@ -63,35 +64,60 @@ def build(lens, n_new, Hq, Hkv, d, bs, seed, prefix=0, n_sharers=0, spare=3):
     T = len(slots)
     k = workloads.normal_storage(rng, (T, Hkv, d), 0.5, "bf16")
     v = workloads.normal_storage(rng, (T, Hkv, d), 0.5, "bf16")
-    okc = np.full((N, Hkv, bs, d), SENTINEL["bf16"], NP_DT["bf16"])
-    ovc = okc.copy()
-    OA.kv_write(k, v, slots, okc, ovc, bs, "bf16")
-    kc, vc = to_dev(np.full_like(okc, SENTINEL["bf16"]), "bf16"), to_dev(np.full_like(okc, SENTINEL["bf16"]), "bf16")
-    pk.pa_kv_write(to_dev(k, "bf16"), to_dev(v, "bf16"), torch.from_numpy(slots).to(DEV), kc, vc)
-    torch.cuda.synchronize()
-    assert np.array_equal(bits(to_host(kc, "bf16")), bits(okc)) and np.array_equal(bits(to_host(vc, "bf16")), bits(ovc))
+    ks = vs = None
+    if fmt == "mxfp4":
+        okc = np.full((N, Hkv, bs * pk.mx_row_bytes(d)), 0xFF, np.uint8)   # NaN blocks
+        ovc = okc.copy()
+        OA.kv_write(k, v, slots, okc, ovc, bs, "mxfp4")
+        kc, vc = pk.mxfp4_cache(N, Hkv, bs, d, DEV), pk.mxfp4_cache(N, Hkv, bs, d, DEV)
+        kc.fill_(0xFF)
+        vc.fill_(0xFF)
+        pk.pa_kv_write(to_dev(k, "bf16"), to_dev(v, "bf16"), torch.from_numpy(slots).to(DEV), kc, vc)
+        torch.cuda.synchronize()
+        assert np.array_equal(kc.cpu().numpy().reshape(okc.shape), okc)
+        assert np.array_equal(vc.cpu().numpy().reshape(ovc.shape), ovc)
+    else:
+        if fmt == "fp8":   # per-head scales amax / 448 over the head's values
+            amax = lambda x: np.abs(OA.codecs.storage_to_f64(x, "bf16")).max(axis=(0, 2))
+            ks, vs = np.float32(amax(k) / 448.0), np.float32(amax(v) / 448.0)
+        okc = np.full((N, Hkv, bs, d), SENTINEL[fmt], NP_DT[fmt])
+        ovc = okc.copy()
+        OA.kv_write(k, v, slots, okc, ovc, bs, fmt, ks, vs)
+        kc, vc = to_dev(np.full_like(okc, SENTINEL[fmt]), fmt), to_dev(np.full_like(okc, SENTINEL[fmt]), fmt)
+        kw = dict(k_scale=torch.from_numpy(ks).to(DEV), v_scale=torch.from_numpy(vs).to(DEV)) if fmt == "fp8" else {}
+        pk.pa_kv_write(to_dev(k, "bf16"), to_dev(v, "bf16"), torch.from_numpy(slots).to(DEV), kc, vc, **kw)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(to_host(kc, fmt)), bits(okc)) and np.array_equal(bits(to_host(vc, fmt)), bits(ovc))
     mb = max(1, max(-(-L // bs) for L in lens))
     tab, L_ = ga.block_tables(list(range(B)), mb)
     otab, oL = oa.block_table(range(B), mb)
     assert tab.tolist() == otab and L_.tolist() == oL
     qs = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)
     q = workloads.normal_storage(rng, (int(qs[-1]), Hq, d), 0.5, "bf16")
-    return dict(kc=kc, vc=vc, okc=okc, ovc=ovc, tab=tab, lens=L_, qs=qs, q=q, B=B, Hq=Hq, d=d, bs=bs)
+    return dict(kc=kc, vc=vc, okc=okc, ovc=ovc, tab=tab, lens=L_, qs=qs, q=q, B=B, Hq=Hq, d=d, bs=bs, fmt=fmt,
+                ks=ks, vs=vs)
 
 
 def run_gpu(c, scale):
     out = torch.full((c["q"].shape[0], c["Hq"], c["d"]), float("nan"), dtype=torch.bfloat16, device=DEV)
+    kw = {}
+    if c.get("fmt") == "fp8":
+        kw = dict(k_scale=torch.from_numpy(c["ks"]).to(DEV), v_scale=torch.from_numpy(c["vs"]).to(DEV))
     pk.pa_prefill(out, to_dev(c["q"], "bf16"), c["kc"], c["vc"], torch.from_numpy(c["tab"]).to(DEV),
-                  torch.from_numpy(c["lens"]).to(DEV), torch.from_numpy(c["qs"]).to(DEV), scale, c["bs"])
+                  torch.from_numpy(c["lens"]).to(DEV), torch.from_numpy(c["qs"]).to(DEV), scale, c["bs"], **kw)
     torch.cuda.synchronize()
     return out
+
+
+def oracle(c, scale):
+    return OA.prefill(c["q"], c["okc"], c["ovc"], c["tab"], c["lens"], c["qs"], np.float32(scale), c["bs"],
+                      c.get("fmt", "bf16"), "bf16", c.get("ks"), c.get("vs"))
 
 
 def check_case(c, what):
     scale = 1 / math.sqrt(c["d"])
     out = run_gpu(c, scale)
-    ref = OA.prefill(c["q"], c["okc"], c["ovc"], c["tab"], c["lens"], c["qs"], np.float32(scale), c["bs"],
-                     "bf16", "bf16")
+    ref = oracle(c, scale)
     got = out_f64(out)
     assert np.isfinite(got).all()
     print(check_close(got, ref, "bf16", what), flush=True)
@@ -108,6 +134,34 @@ def test_prefill_ragged_contexts(d, bs, G):
     n_new = [37, 64, 1, 150, 1, 0, 65]
     c = build(lens, n_new, Hkv * G, Hkv, d, bs, seed=100 + d + bs + G)
     check_case(c, f"prefill d{d} bs{bs} G{G}")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("d,bs,G", [(128, 16, 4), (64, 8, 1), (128, 128, 8), (64, 32, 4), (128, 8, 1)])
+def test_prefill_quantized_cache(fmt, d, bs, G):
+    """fp8 (per-head scales) and 4-bit caches: the tiles are widened to bf16 exactly in LDS;
+    the same ragged shapes as the bf16 test, NaN patterns in every unused slot."""
+    Hkv = 2
+    lens = [37, 164, 6, 450, 1, 90, 129]
+    n_new = [37, 64, 1, 150, 1, 0, 65]
+    c = build(lens, n_new, Hkv * G, Hkv, d, bs, seed=300 + d + bs + G, fmt=fmt)
+    check_case(c, f"prefill {fmt} d{d} bs{bs} G{G}")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_prefill_quantized_shared_prefix_and_decode(fmt):
+    """A shared prefix over a quantized cache; one new token per request equals pa_decode."""
+    lens = [256 + x for x in (5, 70, 1, 33)] + [77, 300]
+    c = build(lens, [5, 40, 1, 33, 77, 12], 32, 8, 128, 16, seed=31, prefix=256, n_sharers=4, fmt=fmt)
+    check_case(c, f"prefill {fmt} shared prefix")
+    c1 = build([1, 17, 300, 1024], [1] * 4, 32, 8, 128, 16, seed=37, fmt=fmt)
+    out = check_case(c1, f"prefill {fmt} n=1")
+    dec = torch.empty_like(out)
+    kw = dict(k_scale=torch.from_numpy(c1["ks"]).to(DEV), v_scale=torch.from_numpy(c1["vs"]).to(DEV)) if fmt == "fp8" else {}
+    pk.pa_decode(dec, to_dev(c1["q"], "bf16"), c1["kc"], c1["vc"], torch.from_numpy(c1["tab"]).to(DEV),
+                 torch.from_numpy(c1["lens"]).to(DEV), 1 / math.sqrt(128), 16, max_seq_len=1024, **kw)
+    torch.cuda.synchronize()
+    print(check_close(out_f64(dec), out_f64(out), "bf16", f"{fmt} decode vs prefill"), flush=True)
 
 
 def test_prefill_shared_prefix():
@@ -150,9 +204,7 @@ def test_prefill_nonpositive_scale(scale):
     weighted equally) against the oracle, which applies the scale as given."""
     c = build([37, 164, 90], [37, 64, 20], 8, 2, 128, 16, seed=23)
     out = out_f64(run_gpu(c, scale))
-    ref = OA.prefill(c["q"], c["okc"], c["ovc"], c["tab"], c["lens"], c["qs"], np.float32(scale), c["bs"],
-                     "bf16", "bf16")
-    print(check_close(out, ref, "bf16", f"prefill scale {scale}"), flush=True)
+    print(check_close(out, oracle(c, scale), "bf16", f"prefill scale {scale}"), flush=True)
 
 
 def test_prefill_bad_length_gives_nan_and_bad_range_writes_nothing():
