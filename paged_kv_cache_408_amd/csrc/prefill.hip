@@ -256,12 +256,22 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
         PA_LDS unsigned char* dk = (PA_LDS unsigned char*)&s_kv[stage][0][0] + R * ROWB;
         PA_LDS unsigned char* dv = (PA_LDS unsigned char*)&s_kv[stage][1][0] + R * ROWB;
         const int sw = prefill_swz<D>(R);
+        const bool swap = NC == 2 && (R & 1);             // odd rows write their second chunk first
+        auto sel = [&](const U4& x, const U4& y) {       // x, or y on a swapping lane (no indexing by lane)
+            return U4{swap ? y.x : x.x, swap ? y.y : x.y, swap ? y.z : x.z, swap ? y.w : x.w};
+        };
+        auto keep = [&](const U4& x) { return live ? x : U4{0, 0, 0, 0}; };
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
-            const int c = NC == 2 ? (i ^ (R & 1)) : i;
+            const int c = NC == 2 ? (swap ? 1 - i : i) : i;
             const int slot = (NC * qcf + c) ^ sw;
-            lds_st16(dk + 16 * slot, live ? ck[c] : U4{0, 0, 0, 0});
-            lds_st16(dv + 16 * slot, live ? cv[c] : U4{0, 0, 0, 0});
+            if constexpr (NC == 2) {
+                lds_st16(dk + 16 * slot, keep(i == 0 ? sel(ck[0], ck[1]) : sel(ck[1], ck[0])));
+                lds_st16(dv + 16 * slot, keep(i == 0 ? sel(cv[0], cv[1]) : sel(cv[1], cv[0])));
+            } else {
+                lds_st16(dk + 16 * slot, keep(ck[0]));
+                lds_st16(dv + 16 * slot, keep(cv[0]));
+            }
         }
     };
 

@@ -101,3 +101,14 @@ def test_prefill_kv_tile(tables, D):
                         c = 4 * t + 2 * ((l >> 4) & 1) + ((l & 3) >> 1)
                         addrs.append(row * rowb + 16 * slot(row, c) + 8 * (l & 1))
                     assert conflicts(addrs, 8, (16, 32)) == [], ("V read", sb, h, rd, t)
+    # fp8 / 4-bit tiles widened into LDS: lane l of wave w writes row 8 w + l / 8, NC = D / 64
+    # chunks NC (l % 8) + c; with NC = 2 an odd row writes its second chunk first
+    nc = D // 64
+    for w in range(8):
+        for i in range(nc):
+            addrs = []
+            for l in range(64):
+                row, qcf = 8 * w + l // 8, l % 8
+                c = (1 - i if row & 1 else i) if nc == 2 else i
+                addrs.append(row * rowb + 16 * slot(row, nc * qcf + c))
+            assert conflicts(addrs, 16, (8, 16)) == [], ("widened write", w, i)
