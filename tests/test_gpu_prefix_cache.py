@@ -129,3 +129,69 @@ def test_prefix_cache_matches_oracle_and_uncached(make):
     ref_out = OA.decode(q_bits[rows], okc, ovc, np.array(otab)[rows], np.array(olens)[rows],
                         np.float32(1 / math.sqrt(w.d)), w.bs, "bf16", "bf16")
     print(check_close(out_f64(out)[rows], ref_out, "bf16", w.name), flush=True)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
+def test_prefix_cache_then_prefill(fmt):
+    """The serving path of a prompt: the prefix cache covers its leading blocks, only the other
+    tokens' K/V are written, and pa_prefill attends each uncovered token over the whole prompt
+    (cached blocks included).  Compared with the oracle's allocator, writes and prefill, and
+    with a prefill of every token of every prompt run without the cache."""
+    w = workloads.prompt_workload(n_req=10, systems=(96, 40), suffix_max=70, finished_every=0, seed_index=11)
+    Hq, Hkv, d, bs = w.Hq, w.Hkv, w.d, w.bs
+
+    def cache():
+        if fmt == "mxfp4":
+            c = pk.mxfp4_cache(w.num_blocks, Hkv, bs, d, DEV)
+            c.fill_(0xFF)                                  # NaN blocks in every unused slot
+            return c
+        return to_dev(np.full((w.num_blocks, Hkv, bs, d), SENTINEL["bf16"], NP_DT["bf16"]), "bf16")
+
+    def ocache():
+        if fmt == "mxfp4":
+            return np.full((w.num_blocks, Hkv, bs * pk.mx_row_bytes(d)), 0xFF, np.uint8)
+        return np.full((w.num_blocks, Hkv, bs, d), SENTINEL["bf16"], NP_DT["bf16"])
+
+    def serve(cached):
+        al, kc, vc = pk.Allocator(w.num_blocks, bs, w.free_order), cache(), cache()
+        oal, okc, ovc = OAlloc(w.num_blocks, bs, w.free_order), ocache(), ocache()
+        n_new = []
+        for i, toks in enumerate(w.prompts):
+            if cached:
+                n_cached, slots = al.add_prompt(i, toks)
+                on_cached, oslots = oal.add_prompt(i, toks)
+            else:
+                al.add(i)
+                oal.add(i)
+                slots, _ = al.append(i, len(toks))
+                oslots, _ = oal.append(i, len(toks))
+                n_cached = on_cached = 0
+            assert n_cached == on_cached and [int(s) for s in slots] == list(oslots)
+            k, v = workloads.prefix_kv(toks, Hkv, d, w.std, w.seed_index)
+            if len(slots):
+                pk.pa_kv_write(to_dev(k[n_cached:], "bf16"), to_dev(v[n_cached:], "bf16"),
+                               torch.from_numpy(np.asarray(slots, np.int64)).to(DEV), kc, vc)
+                OA.kv_write(k[n_cached:], v[n_cached:], np.asarray(oslots, np.int64), okc, ovc, bs, fmt)
+            n_new.append(len(toks) - n_cached)
+        mb = max(-(-len(p) // bs) for p in w.prompts)
+        tab, lens = al.block_tables(list(range(len(w.prompts))), mb)
+        otab, olens = oal.block_table(range(len(w.prompts)), mb)
+        assert tab.tolist() == otab and lens.tolist() == olens
+        qs = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)
+        # each prompt token's query, a function of its prefix like its K/V
+        q = np.concatenate([workloads.prefix_kv(p, Hq, d, w.std, w.seed_index + 1)[0][len(p) - n:]
+                            for p, n in zip(w.prompts, n_new)])
+        out = torch.full((int(qs[-1]), Hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+        pk.pa_prefill(out, to_dev(q, "bf16"), kc, vc, torch.from_numpy(tab).to(DEV), torch.from_numpy(lens).to(DEV),
+                      torch.from_numpy(qs).to(DEV), 1 / math.sqrt(d), bs)
+        torch.cuda.synchronize()
+        ref = OA.prefill(q, okc, ovc, np.array(otab), np.array(olens), qs, np.float32(1 / math.sqrt(d)), bs, fmt, "bf16")
+        return out_f64(out), ref, n_new, qs
+
+    got, ref, n_new, qs = serve(cached=True)
+    assert sum(len(p) - n for p, n in zip(w.prompts, n_new)) > 0, "the cache served no token"
+    print(check_close(got, ref, "bf16", f"prefix cache + prefill ({fmt})"), flush=True)
+    full, _, _, fqs = serve(cached=False)
+    # the uncovered tokens are each prompt's last n: the same rows of the full prefill
+    rows = np.concatenate([np.arange(fqs[i + 1] - n, fqs[i + 1]) for i, n in enumerate(n_new)])
+    print(check_close(got, full[rows], "bf16", f"prefix cache + prefill vs full prefill ({fmt})"), flush=True)
