@@ -21,7 +21,7 @@ measured with HIP events on the launch stream around each step's 32 back-to-back
 launches (the layers' K/V writes are issued first).  `cpu_baseline` = the float64 oracle
 timed on a bounded sample of the same per-request work on the host.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--graph]   # --graph: replay each step from HIP graphs
     python bench.py --workload {ragged_prefix,long_context,sweep,mxfp4}   # other workloads' decode rates
     python bench.py --workload swap     # preemption: swap-out / swap-in rates over the host link
     python bench.py --workload prefix_cache   # prompts through the prefix cache vs without it
@@ -208,13 +208,26 @@ def run(args):
     log(f"split-K partitions of {part_used} tokens (requested {args.partition_tokens}; 0 = automatic)")
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     pk.pa_decode_workspace_init(ws)
-    dec = [pk.PreparedDecode(outs[l], q[l], kc[l], vc[l], tables_d, lens_d, scale, bs, max_seq_len=max_seq,
-                             workspace=ws, partition_tokens=args.partition_tokens) for l in range(layers)]
-    wr = [pk.PreparedKVWrite(kn[l], vn[l], slot_d, kc[l], vc[l]) for l in range(layers)]
+    def prepared(stream):
+        d_ = [pk.PreparedDecode(outs[l], q[l], kc[l], vc[l], tables_d, lens_d, scale, bs, max_seq_len=max_seq,
+                                workspace=ws, partition_tokens=args.partition_tokens, stream=stream)
+              for l in range(layers)]
+        w_ = [pk.PreparedKVWrite(kn[l], vn[l], slot_d, kc[l], vc[l], stream=stream) for l in range(layers)]
+        return d_, w_
+
+    dec, wr = prepared(None)             # launches on the current stream
     seq_ids = list(range(B))
     ones = [1] * B
 
-    def step(i, events=None):
+    def write_all():                     # each layer's new K/V first ...
+        for l in range(layers):
+            wr[l]()
+
+    def decode_all():                    # ... then the 32 decode launches back to back
+        for l in range(layers):
+            dec[l]()
+
+    def step(i, events=None, launch=(write_all, decode_all)):
         s, cow = alloc.batch_append(seq_ids, ones)
         alloc.block_tables(seq_ids, max_blocks, pin_tab[i].numpy(), pin_len[i].numpy())
         pin_slot[i].numpy()[:] = s
@@ -225,12 +238,10 @@ def run(args):
             pairs = torch.tensor(cow, dtype=torch.int64).to(dev, non_blocking=False)
             for l in range(layers):
                 pk.pa_copy_blocks(kc[l], vc[l], pairs)
-        for l in range(layers):          # each layer's new K/V first ...
-            wr[l]()
+        launch[0]()
         if events is not None:
             events[0].record()
-        for l in range(layers):          # ... then the 32 decode launches back to back
-            dec[l]()
+        launch[1]()
         if events is not None:
             events[1].record()
         return pin_len[i].numpy().copy()
@@ -238,18 +249,48 @@ def run(args):
     for i in range(warm):
         step(i)
     torch.cuda.synchronize()
-    log(f"warmup done ({warm} steps); timing {steps} steps")
+    launch = (write_all, decode_all)
+    if args.graph:
+        # the 32 writes and the 32 decodes of a step as two HIP graphs, replayed every step on
+        # the same buffers (the step's tables, lengths and slots are copied into them first):
+        # one launch per graph instead of 64 host calls.  The library's launches on the
+        # capture stream are what the graphs hold; nothing in them allocates or clears memory.
+        # (Measured: each decode kernel takes longer inside the graph than launched on its own,
+        # 52 against 45 us, so host launches are the default.)
+        cap = torch.cuda.Stream()
+        dec_c, wr_c = prepared(cap)
+        g_write, g_decode = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_write, stream=cap, capture_error_mode="thread_local"):
+            for l in range(layers):
+                wr_c[l]()
+        with torch.cuda.graph(g_decode, stream=cap, capture_error_mode="thread_local"):
+            for l in range(layers):
+                dec_c[l]()
+        torch.cuda.synchronize()
+        launch = (g_write.replay, g_decode.replay)
+    log(f"warmup done ({warm} steps); timing {steps} steps ({'HIP graphs' if args.graph else 'host launches'})")
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     lens_per_step = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        lens_per_step.append(step(warm + i, evs[i]))
+        lens_per_step.append(step(warm + i, evs[i], launch))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
     log(f"timed {steps} steps in {wall * 1e3:.2f} ms")
+    if args.graph:
+        # the graphs' last outputs against eager launches on the same inputs: bit for bit
+        # (decode is deterministic; the write of the same rows again changes nothing)
+        got = [outs[l].clone() for l in (0, layers - 1)]
+        write_all()
+        decode_all()
+        torch.cuda.synchronize()
+        for g_out, l in zip(got, (0, layers - 1)):
+            if not torch.equal(g_out.view(torch.int16), outs[l].view(torch.int16)):
+                raise RuntimeError(f"graph replay of layer {l} differs from an eager decode")
+        log("graph outputs of the last step equal eager launches (layers 0 and 31)")
 
     # HIP events on the launch stream around each step's 32 back-to-back decode launches
     dec_ms = [e0.elapsed_time(e1) / layers for (e0, e1) in evs for _ in range(layers)]
@@ -282,6 +323,7 @@ def run(args):
             "block_size": bs, "seq_len_start": int(lens_per_step[0][0]), "seq_len_end": int(lens_per_step[-1][0]),
             "partition_tokens": part_used,
             "kv_cache_gb": round(2 * layers * kc[0].numel() * 2 / 1e9, 3),
+            "launch": "two HIP graphs per step" if args.graph else "one host launch per kernel",
         },
         "roofline": {
             "bound": "hbm",
@@ -682,6 +724,8 @@ def main():
     ap.add_argument("--partition-tokens", type=int, default=0, help="split-K partition size; 0 = automatic")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="default workload: replay each step's writes and decodes from two HIP graphs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run pa_copy_blocks over 1 GiB of blocks (write-counter calibration)")
     ap.add_argument("--calibrate-read", action="store_true",

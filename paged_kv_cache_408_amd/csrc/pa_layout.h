@@ -1,28 +1,58 @@
 // LDS layouts of the K/V tiles, shared by the kernels and by the host-side layout check
-// (tests/lds_layout_dump.cpp).  LDS has 64 banks of 4 bytes; a 16-byte chunk of a tile row
-// is placed at a slot that depends on the row, so that the lanes of one LDS instruction
-// touch different banks.
+// (tests/lds_layout_dump.cpp).  A 16-byte chunk of a tile row is placed at a slot that depends
+// on the row (and, for the decode V tile, on the chunk), so that the lanes of one LDS
+// instruction that are served together touch different banks.  On gfx950, as measured with
+// the LDS bank-conflict counter:
+//   - 8-byte reads (ds_read_b64, ds_read_b64_tr_b16): lanes 0-31, then 32-63; 64 banks of 4
+//     bytes, so two lanes collide when their addresses are equal modulo 256 bytes but their
+//     words differ;
+//   - 16-byte reads (ds_read_b128): 16 lanes at a time, within each 32-lane half the lane
+//     quads whose index (lane / 4) % 8 has even bit parity, then those with odd parity; 64 banks;
+//   - 16-byte writes (ds_write_b128): 8 consecutive lanes at a time; two lanes collide when
+//     their chunks are equal modulo 128 bytes.
 #pragma once
 
 #include <hip/hip_runtime.h>
 
-// Decode: slot of bf16 chunk c (16 bytes = 8 dims) in row `row` of a wave's V tile (D / 8
-// chunks per row): c XOR a per-row mask m.  m / 2 runs through every value on any 8
-// consecutive rows that share banks, so the transpose reads (2 chunks of 4 rows per 16 lanes,
-// 8 rows per 32) never collide; m % 4 (D = 128) or m % 2 (D = 64, where rows r and r + 2 share
-// banks) differs between the rows one write instruction covers, so the fp8 tile writes (2 rows
-// x 8 chunks) and the 4-bit ones (4 rows x 4 chunks) do not collide either.
+// Decode, fp8 and 4-bit caches: slot of bf16 chunk c (16 bytes = 8 dims) in row `row` of a
+// wave's widened V tile (D / 8 chunks per row).
+//  - D = 128 (256-byte rows, each row on every bank): c with bit 0 flipped by bit 3, XOR a
+//    row mask m.  m / 2 takes 8 different values on 8 consecutive rows, so the transpose
+//    reads (2 chunks of 8 rows per 32 lanes) never collide.  The writes of 8 lanes cover
+//    chunks c and c + 8 of a row together (the fp8 widening writes chunks 0, 2, .., 14 of one
+//    row; the 4-bit one chunks w, w + 4, w + 8, w + 12 of two rows): the bit-3 flip puts
+//    those on different 16-byte positions modulo 128 bytes, and m % 8 of rows 2i and 2i + 1
+//    differs by 3, which keeps the two rows' sets of positions apart.
+//  - D = 64 (128-byte rows: rows r and r + 2 share banks): c XOR m, m / 2 different over the
+//    rows that share banks in one transpose read; rows 2i, 2i + 1 differ in m % 2 so the
+//    writes (two rows of 4 lanes each) take complementary halves of the positions.
 template <int D>
 __host__ __device__ constexpr int vt_slot(int row, int c) {
-    return D == 128 ? c ^ ((2 * (row & 7)) ^ ((row ^ (row >> 1)) & 1)) : c ^ ((row & 7) ^ ((row >> 1) & 1));
+    return D == 128 ? c ^ ((c >> 3) & 1) ^ ((2 * (row & 7)) ^ ((row ^ (row >> 1)) & 1))
+                    : c ^ ((row & 7) ^ ((row >> 1) & 1));
+}
+
+// Decode, bf16 cache: the K/V stage of 16 rows filled by direct-to-LDS loads.  Chunk c of row
+// `row` sits at slot c XOR m(row) (an involution: the same call maps a slot back to the chunk
+// it holds, which is how the loads pick their source).  The K operand reads one chunk of the
+// 16 rows per 16-lane phase (lane l: row l % 16, chunk 4 j + l / 16) and the transpose reads
+// of V take chunks 2 t, 2 t + 1 of 8 rows per 32 lanes.
+//  - D = 128: m = 2 (row % 8), XOR 9 on rows 8..15.  m / 2 is different on rows 0..7 and on
+//    rows 8..15 (transpose reads); the masks of rows {0..3, 12..15} are exactly 0..7, a set
+//    closed under XOR 1, which is what the two 16-lane read phases need (each takes chunk
+//    4 j on half of those rows and chunk 4 j + 1 on the others).
+//  - D = 64: m = row % 8.
+template <int D>
+__host__ __device__ constexpr int dma_slot(int row, int c) {
+    return D == 128 ? c ^ ((2 * (row & 7)) ^ (9 * ((row >> 3) & 1))) : c ^ (row & 7);
 }
 
 // Prefill: chunk c of K/V tile row R (D / 8 chunks per row) sits at slot c ^ prefill_swz(R).
-// The K operand reads one chunk of 32 consecutive rows: 16 consecutive rows must land on
-// different banks (D = 128: every row covers all banks once, so a bijection of R % 16; D = 64:
-// rows of equal parity share banks, so a bijection of (R / 2) % 8).  The transpose reads of V
-// take 4 chunks (32 dims) of 4 consecutive rows per 32 lanes: those chunk groups must be
-// disjoint among rows that share banks.
+// The K operand reads one chunk of 32 consecutive rows: the 16 rows of one read phase must
+// land on different banks (D = 128: every row covers all banks once, so a bijection of
+// R % 16; D = 64: rows of equal parity share banks, so a bijection of (R / 2) % 8).  The
+// transpose reads of V take 4 chunks (32 dims) of 4 consecutive rows per 32 lanes: those
+// chunk groups must be disjoint among rows that share banks.
 template <int D>
 __host__ __device__ constexpr int prefill_swz(int row) {
     return D == 128 ? ((row & 3) << 2) | ((row >> 2) & 3) : (((row >> 1) & 1) << 2) | ((row >> 2) & 3);

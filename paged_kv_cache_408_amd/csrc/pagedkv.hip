@@ -1267,7 +1267,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
             }
         } else {
         // ---- K/V through an LDS ring of kStages stages per wave, filled by DMA loads.
-        // A tile's 16-byte chunk position p (row p / CPR) holds data chunk (p % CPR) ^ (row % CPR)
+        // A tile's 16-byte chunk position p (row p / CPR) holds data chunk stage_slot(row, p % CPR)
         // of its row, so that the K reads (16 rows at one chunk) and the V transpose reads spread
         // over the banks.  Lane `lane` of DMA instruction i fills position 64 i + lane.
         constexpr int CPR = M::CPR;
@@ -1275,11 +1275,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
         constexpr int NIP = 2 * NI;                       // per pass (K and V)
         constexpr int RPI = 64 / CPR;                     // rows per DMA instruction
         static_assert(KT % 1024 == 0 && NI >= 1, "tile of whole KiB");
+        // bf16 stages use dma_slot (a conflict-free layout for both operand reads); the fp8
+        // stage keeps chunk p % CPR XOR row % CPR of its 128-byte rows
+        auto stage_slot = [](int row, int c) { return M::E == 2 ? dma_slot<D>(row, c) : c ^ (row % CPR); };
         uint32_t src_off[NI];                             // source byte offset inside the 16 rows
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int pos = 64 * i + lane, row = pos / CPR, slot = pos % CPR;
-            src_off[i] = uint32_t(row) * M::ROWB + 16u * uint32_t(slot ^ (row % CPR));
+            src_off[i] = uint32_t(row) * M::ROWB + 16u * uint32_t(stage_slot(row, slot));
         }
         PA_LDS unsigned char* ring = tile;                // stage s: K at ring + 2 s KT, V at + KT
         PA_LDS unsigned char* vtile = tile + kStages * 2 * KT;   // fp8: bf16 V tile
@@ -1350,8 +1353,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
                     e4m3x8_to_bf16(v.x, v.y, lo);
                     e4m3x8_to_bf16(v.z, v.w, hi);
                     PA_LDS unsigned char* rowp = vtile + row * M::TROWB;
-                    lds_st16(rowp + 16 * ((2 * c) ^ (row % (D / 8))), U4{lo[0], lo[1], lo[2], lo[3]});
-                    lds_st16(rowp + 16 * ((2 * c + 1) ^ (row % (D / 8))), U4{hi[0], hi[1], hi[2], hi[3]});
+                    lds_st16(rowp + 16 * dma_slot<D>(row, 2 * c), U4{lo[0], lo[1], lo[2], lo[3]});
+                    lds_st16(rowp + 16 * dma_slot<D>(row, 2 * c + 1), U4{hi[0], hi[1], hi[2], hi[3]});
                 }
             }
             // scores: K rows as the A operand read from the stage
@@ -1361,9 +1364,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
             for (int j = 0; j < M::NQK; ++j) {
                 U4 kv;
                 if constexpr (M::E == 2) {
-                    kv = lds_ld16(krow + 16 * ((4 * j + grp4) ^ (col % CPR)));
+                    kv = lds_ld16(krow + 16 * stage_slot(col, 4 * j + grp4));
                 } else {
-                    const U4 src = lds_ld16(krow + 16 * ((4 * (j >> 1) + grp4) ^ (col % CPR)));
+                    const U4 src = lds_ld16(krow + 16 * stage_slot(col, 4 * (j >> 1) + grp4));
                     uint32_t o[4];
                     if (j & 1) e4m3x8_to_bf16(src.z, src.w, o); else e4m3x8_to_bf16(src.x, src.y, o);
                     kv = U4{o[0], o[1], o[2], o[3]};
@@ -1401,7 +1404,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
 #pragma unroll
             for (int t = 0; t < M::NPV; ++t) {
                 const int c = 2 * t + ((lane & 3) >> 1);
-                PA_LDS unsigned char* src = vt + vrow * M::TROWB + 16 * (c ^ (vrow % (D / 8))) + 8 * (lane & 1);
+                PA_LDS unsigned char* src = vt + vrow * M::TROWB + 16 * dma_slot<D>(vrow, c) + 8 * (lane & 1);
                 const i16x4v vtr = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4v*)src);
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vtr, acc[t], 0, 0, 0);
             }

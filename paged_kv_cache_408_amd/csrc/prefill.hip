@@ -229,8 +229,10 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
         }
     };
     // the pending rows of tile k, widened to bf16, into `stage`; rows past what this
-    // work-group reads are zero.  The two chunks a lane writes go in the order that keeps
-    // rows 2i and 2i + 1 on different banks.
+    // work-group reads are zero.  The 8 lanes of a row are one phase of a 16-byte LDS write,
+    // which collides on chunks equal modulo 128 bytes: lanes 4..7 of a row write their two
+    // chunks in the other order from lanes 0..3 (on odd rows the other way round), so the 8 chunks
+    // written together are 8 different positions modulo 128 bytes.
     auto store_q = [&](int k, int stage) {
         constexpr int NC = D / 64;                          // bf16 chunks per lane
         const int R = kRW * w + qrow;                       // tile row
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
         PA_LDS unsigned char* dk = (PA_LDS unsigned char*)&s_kv[stage][0][0] + R * ROWB;
         PA_LDS unsigned char* dv = (PA_LDS unsigned char*)&s_kv[stage][1][0] + R * ROWB;
         const int sw = prefill_swz<D>(R);
-        const bool swap = NC == 2 && (R & 1);             // odd rows write their second chunk first
+        const bool swap = NC == 2 && ((R ^ (qcf >> 2)) & 1);   // this lane writes its second chunk first
         auto sel = [&](const U4& x, const U4& y) {       // x, or y on a swapping lane (no indexing by lane)
             return U4{swap ? y.x : x.x, swap ? y.y : x.y, swap ? y.z : x.z, swap ? y.w : x.w};
         };
