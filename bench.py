@@ -345,8 +345,9 @@ def run(args):
 
 def run_workload(name, args):
     """One decode step of a non-default workload, timed: the step token's pa_kv_write, then
-    pa_decode, repeated on the same state.  Prints one JSON line per setting (these are
-    measurements for the record, not the benchmark line)."""
+    pa_decode, repeated on the same state (step_gbps from the wall time); then pa_decode alone,
+    8 back-to-back launches between HIP events, for the kernel's time.  Prints one JSON line
+    per setting (these are measurements for the record, not the benchmark line)."""
     import numpy as np
     import torch
 
@@ -423,7 +424,18 @@ def run_workload(name, args):
             e1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        dec_us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+        single_us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+        # the kernel's own time: events around back-to-back launches on the same state (as the
+        # headline times its 32 layers); events around one launch also hold its dispatch
+        rep = 8
+        evb = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for e0, e1 in evb:
+            e0.record()
+            for _ in range(rep):
+                dec()
+            e1.record()
+        torch.cuda.synchronize()
+        dec_us = sorted(e0.elapsed_time(e1) * 1e3 / rep for e0, e1 in evb)
         med = dec_us[len(dec_us) // 2]
         e = {"fp8": 1, "mxfp4": 17 / 32}.get(w.fmt, 2)   # mxfp4: d / 2 code bytes + d / 32 scale bytes per row
         logical = decode_bytes(lens, w.Hq, w.Hkv, w.d, w.bs, e, 2) + (2 * w.Hkv * 4 if w.fmt == "fp8" else 0)
@@ -435,6 +447,8 @@ def run_workload(name, args):
         print(json.dumps({
             "workload": w.name, "metric": "decode attention KV GB/s", "unit": "GB/s",
             "decode_us_median": round(med, 3), "decode_us_min": round(dec_us[0], 3),
+            "decode_timing": "HIP events around %d back-to-back launches, median over %d" % (rep, args.steps),
+            "decode_us_single_launch_median": round(single_us[len(single_us) // 2], 3),
             "logical_gbps": round(logical / med / 1e3, 1),
             "unique_kv_gbps": round(unique_kv / med / 1e3, 1),
             "pct_of_hbm_peak_logical": round(100 * logical / med / 1e3 / HBM_PEAK_GBPS, 2),
