@@ -71,6 +71,13 @@ namespace {
 #endif
 constexpr int kWaves = PA_DECODE_WAVES;
 constexpr int kThreads = 64 * kWaves;
+// Waves per work-group of the matrix-core decode when it walks the compact item list (ragged
+// batches).  Items there are short (a request's last partition, often a few hundred tokens),
+// so each item's start -- the table read, then the first K/V loads -- is latency, not
+// bandwidth.  Two-wave work-groups keep twice as many items in flight per compute unit as
+// four-wave ones (4 work-groups instead of 2 at 256 VGPRs); the uniform grid, whose items are
+// long, keeps kWaves.
+constexpr int kListWaves = 2;
 constexpr int kDepth = PA_DECODE_DEPTH;
 constexpr bool kNonTemporal = PA_DECODE_NT != 0;
 constexpr int kStagesBf16 = PA_DECODE_STAGES;
@@ -78,6 +85,7 @@ constexpr int kStagesFp8 = PA_DECODE_STAGES_FP8;
 static_assert(kStagesBf16 == 0 || (kStagesBf16 >= 2 && kStagesBf16 <= 6), "LDS ring of 2 to 6 stages");
 static_assert(kStagesFp8 == 0 || (kStagesFp8 >= 2 && kStagesFp8 <= 6), "LDS ring of 2 to 6 stages");
 static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves per work-group");
+static_assert(kListWaves == 2 || kListWaves == 4, "2 or 4 waves per work-group on the item list");
 static_assert(kDepth >= 2 && kDepth <= 4, "2 to 4 passes in flight");
 constexpr int kMergeGroup = 16;   // partitions merged together at the first merge level
 
@@ -409,17 +417,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_view(const float* bas
 // (a bad block id) makes the result NaN.  Writes `out` (rounded) or, when out == nullptr, one
 // partial row per head to (m_dst, l_dst, acc_dst) with the given head stride, by
 // agent-scope stores.
-template <int QDT, int D, int G>
+template <int QDT, int D, int G, int NT>
 __device__ __forceinline__ void merge_rows(const float* m_src, const float* l_src, const float* acc_src, int64_t row0,
                            int64_t head_stride, int count, typename Elem<QDT>::T* out, float* m_dst, float* l_dst,
                            float* acc_dst, int64_t dst_head_stride) {
     constexpr int NC = G * D / 4;               // float4 columns
-    constexpr int NS = kThreads / NC > 0 ? kThreads / NC : 1;   // row slices
-    static_assert(NC <= kThreads, "one column per thread");
+    constexpr int NS = NT / NC > 0 ? NT / NC : 1;   // row slices (1 when columns outnumber threads)
+    constexpr int NCB = NC > NT ? NC / NT : 1;  // column batches per thread
+    static_assert(NC <= NT || NC % NT == 0, "whole column batches");
     __shared__ float s_mm[NS][NC], s_ll[NS][NC];
     __shared__ float4 s_num[NS][NC];
     const int t = threadIdx.x;
-    const int col = t % NC, slice = t / NC;
+    for (int cb = 0; cb < NCB; ++cb) {
+    const int col = NC > NT ? cb * NT + t : t % NC, slice = NC > NT ? 0 : t / NC;
     const int h = col / (D / 4), c4 = col % (D / 4);
     const bool active = slice < NS;
     float M = -INFINITY, den = 0.0f;
@@ -488,6 +498,7 @@ __device__ __forceinline__ void merge_rows(const float* m_src, const float* l_sr
             store_agent(l_dst + int64_t(h) * dst_head_stride, dt);
         }
     }
+    }   // column batches
 }
 
 // End of one partition of one (request, KV head): merges the waves' states held in LDS
@@ -502,7 +513,7 @@ __device__ __forceinline__ void merge_rows(const float* m_src, const float* l_sr
 // agent-scope loads.  This avoids agent-scope fences, whose L2 write-back/invalidate would
 // serialise the work-groups of an XCD.  Counters are left at zero.  Work-group uniform; ends
 // with a barrier, so the caller may reuse the LDS arrays afterwards.
-template <int QDT, int D, int G>
+template <int QDT, int D, int G, int NW>
 __device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int g, int part, int nparts, float vsc, bool any_bad,
                                  const float* s_m, const float* s_l, const float* s_acc, int acc_wave_stride) {
     using QT = typename Elem<QDT>::T;
@@ -510,14 +521,14 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int
     const int hq = a.hkv * G;
     QT* out = reinterpret_cast<QT*>(a.out) + (int64_t(b) * hq + int64_t(g) * G) * D;
     const bool single = nparts == 1;
-    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < G * D; idx += 64 * NW) {
         const int h = idx / D, dim = idx - h * D;
         float M = s_m[h];
 #pragma unroll
-        for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, s_m[ww * G + h]);
+        for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, s_m[ww * G + h]);
         float num = 0.0f, den = 0.0f;
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) {
+        for (int ww = 0; ww < NW; ++ww) {
             const float f = __builtin_amdgcn_exp2f(s_m[ww * G + h] - M);   // 0 for an idle wave
             num = fmaf(f, s_acc[ww * acc_wave_stride + h * D + dim], num);
             den = fmaf(f, s_l[ww * G + h], den);
@@ -562,13 +573,13 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int
     const int64_t rows1 = (int64_t(b) * hq + int64_t(g) * G) * a.max_parts;    // head h: + h * max_parts
     const int first = grp * kMergeGroup, count = min(kMergeGroup, nparts - first);
     if (ngroups == 1) {
-        merge_rows<QDT, D, G>(a.ws_m, a.ws_l, a.ws_acc, rows1 + first, a.max_parts, count, out, nullptr, nullptr,
+        merge_rows<QDT, D, G, 64 * NW>(a.ws_m, a.ws_l, a.ws_acc, rows1 + first, a.max_parts, count, out, nullptr, nullptr,
                               nullptr, 0);
         __syncthreads();
         return;
     }
     const int64_t rows2 = (int64_t(b) * hq + int64_t(g) * G) * a.max_groups;
-    merge_rows<QDT, D, G>(a.ws_m, a.ws_l, a.ws_acc, rows1 + first, a.max_parts, count, nullptr, a.ws_m2 + rows2 + grp,
+    merge_rows<QDT, D, G, 64 * NW>(a.ws_m, a.ws_l, a.ws_acc, rows1 + first, a.max_parts, count, nullptr, a.ws_m2 + rows2 + grp,
                           a.ws_l2 + rows2 + grp, a.ws_acc2 + (rows2 + grp) * D, a.max_groups);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -582,7 +593,7 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int
     const bool merge2 = s_last;
     __syncthreads();
     if (!merge2) return;
-    merge_rows<QDT, D, G>(a.ws_m2, a.ws_l2, a.ws_acc2, rows2, a.max_groups, ngroups, out, nullptr, nullptr, nullptr, 0);
+    merge_rows<QDT, D, G, 64 * NW>(a.ws_m2, a.ws_l2, a.ws_acc2, rows2, a.max_groups, ngroups, out, nullptr, nullptr, nullptr, 0);
     __syncthreads();
 }
 
@@ -883,7 +894,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeArgs 
         }
     }
     const bool any_bad = __syncthreads_or(bad);
-    finish_partition<QDT, D, G>(a, b, g, part, nparts, vsc, any_bad, &s_m[0][0], &s_l[0][0], &s_acc[0][0][0],
+    finish_partition<QDT, D, G, kWaves>(a, b, g, part, nparts, vsc, any_bad, &s_m[0][0], &s_l[0][0], &s_acc[0][0][0],
                                 G * D);
 }
 
@@ -950,9 +961,10 @@ struct MCfg<PA_DTYPE_MXFP4, D> {
 constexpr int kMaxListSeqs = 8192;   // batches up to this size use the compact item list
 
 
-template <int CDT, int QDT, int D, int BS, int G>
-__global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeArgs a) {
+template <int CDT, int QDT, int D, int BS, int G, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void decode_mfma_kernel(const DecodeArgs a) {
     using M = MCfg<CDT, D>;
+    constexpr int NT = 64 * NW;                           // threads per work-group
     using CT = typename Elem<CDT>::T;
     using QT = typename Elem<QDT>::T;
     constexpr int TPP = 16;                               // tokens per pass
@@ -971,10 +983,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
 
     // per-wave V tile (bf16, swizzled); after a partition's passes the same bytes hold the
     // wave's accumulator slice acc[G][D] (float) for the merge across waves
-    __shared__ __align__(16) unsigned char s_tile[kWaves][WAVE_LDS];
-    __shared__ float s_m[kWaves][G];
-    __shared__ float s_l[kWaves][G];
-    extern __shared__ int s_pref[];                       // compact item list: B + 1 prefix sums
+    __shared__ __align__(16) unsigned char s_tile[NW][WAVE_LDS];
+    __shared__ float s_m[NW][G];
+    __shared__ float s_l[NW][G];
+    extern __shared__ int s_pref[];                       // compact item list: B + 1 prefix sums,
+    int* const s_len = s_pref + a.num_seqs + 1;           // then the B request lengths
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, uniform per wave
@@ -994,12 +1007,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
         const int t0 = part * a.part_tokens;
         const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
 
-        // block ids of this wave's passes, 64 at a time (lane j: pass w + kWaves * (k0 + j)),
+        // block ids of this wave's passes, 64 at a time (lane j: pass w + NW * (k0 + j)),
         // read before the length is known; `check_entries` flags ids outside the pool inside
         // the live range and replaces every such id by 0
         int ent_a = 0, ent_b = 0;
         auto read_entries = [&](int k0) {
-            const int e = (t0 + (w + kWaves * (k0 + lane)) * TPP) / BS;
+            const int e = (t0 + (w + NW * (k0 + lane)) * TPP) / BS;
             ent_a = a.max_blocks > 0 ? gld_i32(table + min(e, a.max_blocks - 1)) : -1;
             if constexpr (BPP == 2) ent_b = a.max_blocks > 0 ? gld_i32(table + min(e + 1, a.max_blocks - 1)) : -1;
         };
@@ -1026,14 +1039,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
         if (L == 0) {   // empty request (zeros) or invalid length (NaN); single partition
             QT* out = reinterpret_cast<QT*>(a.out) + (int64_t(b) * hq + int64_t(g) * G) * D;
             const float fill = len_bad ? __builtin_nanf("") : 0.0f;
-            for (int i = threadIdx.x; i < G * D; i += kThreads) gst(out + i, f32_to_bf16(fill));
+            for (int i = threadIdx.x; i < G * D; i += NT) gst(out + i, f32_to_bf16(fill));
             __syncthreads();
             return;
         }
 
         const int t1 = min(L, t0 + a.part_tokens);
         const int npass = (t1 - t0 + TPP - 1) / TPP;
-        const int nk = npass > w ? (npass - w + kWaves - 1) / kWaves : 0;
+        const int nk = npass > w ? (npass - w + NW - 1) / NW : 0;
         float sc = a.score_scale;
         float vsc = 1.0f;
         if constexpr (CDT == PA_DTYPE_FP8_E4M3) {
@@ -1050,7 +1063,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
                 ent_a = 0;
             }
             if constexpr (BPP == 2) {
-                const int e = (t0 + (w + kWaves * kk) * TPP) / BS;
+                const int e = (t0 + (w + NW * kk) * TPP) / BS;
                 if (ent_b < 0 || ent_b >= a.num_blocks) {
                     if (live && (e + 1) * BS < t1) bad = true;
                     ent_b = 0;
@@ -1080,7 +1093,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
                     read_entries(k);
                     check_entries(k);
                 }
-                const int tb = t0 + (w + kWaves * k) * TPP;
+                const int tb = t0 + (w + NW * k) * TPP;
                 const int b0 = __builtin_amdgcn_readlane(ent_a, k & 63);
                 if constexpr (kMx) {
                     // K row `col`, V row lane / 4 (quarter lane % 4); rows 8..15 in the second
@@ -1137,23 +1150,23 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
             };
 
             auto compute = [&](int k, U4 (&kb)[M::KLD], U4 (&vb)[M::VLD]) {
-                const int tb = t0 + (w + kWaves * k) * TPP;
+                const int tb = t0 + (w + NW * k) * TPP;
                 // a pass past the end of the partition masks its rows beyond t1; the others
                 // (all but the last) skip every mask
                 auto body = [&](auto partial_c) {
                 constexpr bool partial = decltype(partial_c)::value;
                 // V tile -> LDS as bf16 (rows past the end zeroed: they may hold anything)
                 if constexpr (kMx) {
-                    constexpr int NW = D / 32;            // code dwords per lane (8 dims each)
+                    constexpr int NCD = D / 32;           // code dwords per lane (8 dims each)
                     const int vr = lane >> 2, part = lane & 3;
                     const uint32_t keep = (partial && tb + vr >= t1) ? 0u : ~0u;
                     const float vsf = e8m0_to_f32(vb[1].x);
                     PA_LDS unsigned char* rowp = tile + vr * M::TROWB;
     #pragma unroll
-                    for (int wi = 0; wi < NW; ++wi) {
+                    for (int wi = 0; wi < NCD; ++wi) {
                         U4 c = e2m1x8_to_bf16(u4_get(vb[0], wi), vsf);
                         if constexpr (partial) c = U4{c.x & keep, c.y & keep, c.z & keep, c.w & keep};
-                        lds_st16(rowp + 16 * vt_slot<D>(vr, NW * part + wi), c);
+                        lds_st16(rowp + 16 * vt_slot<D>(vr, NCD * part + wi), c);
                     }
                 }
     #pragma unroll
@@ -1293,7 +1306,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
                 read_entries(k);
                 check_entries(k);
             }
-            const int tb = t0 + (w + kWaves * k) * TPP;
+            const int tb = t0 + (w + NW * k) * TPP;
             const int b0 = __builtin_amdgcn_readlane(ent_a, k & 63);
             PA_LDS unsigned char* dk = stage_k(st);
             PA_LDS unsigned char* dv = dk + KT;
@@ -1326,7 +1339,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
         };
 
         auto compute_dma = [&](int k, int st) {
-            const int tb = t0 + (w + kWaves * k) * TPP;
+            const int tb = t0 + (w + NW * k) * TPP;
             const bool partial = tb + TPP > t1;
             PA_LDS unsigned char* dk = stage_k(st);
             PA_LDS unsigned char* dv = dk + KT;
@@ -1447,21 +1460,26 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
             }
         }
         const bool any_bad = __syncthreads_or(bad);
-        finish_partition<QDT, D, G>(a, b, g, part, nparts, vsc, any_bad, &s_m[0][0], &s_l[0][0],
+        finish_partition<QDT, D, G, NW>(a, b, g, part, nparts, vsc, any_bad, &s_m[0][0], &s_l[0][0],
                                     reinterpret_cast<const float*>(&s_tile[0][0]), int(sizeof(s_tile[0]) / 4));
     };
 
     // ---- work items: the compact list (prefix sums of each request's full partitions, all but
-    // its last, in LDS), or one item per work-group of the (partition, KV head, request) grid
+    // its last, and the request lengths, in LDS), or one item per work-group of the (partition,
+    // KV head, request) grid
     int F = 0;
     int64_t total = 1;
     if (a.list) {
         const int B = a.num_seqs;
-        const int per = (B + kThreads - 1) / kThreads;
+        const int per = (B + NT - 1) / NT;
         const int i0 = min(B, int(threadIdx.x) * per), i1 = min(B, i0 + per);
         int local = 0;
-        for (int i = i0; i < i1; ++i) local += nparts_of(gld_i32(a.seq_lens + i)) - 1;
-        __shared__ int s_wsum[kWaves];
+        for (int i = i0; i < i1; ++i) {
+            const int Li = gld_i32(a.seq_lens + i);
+            s_len[i] = Li;
+            local += nparts_of(Li) - 1;
+        }
+        __shared__ int s_wsum[NW];
         int incl = local;                                 // work-group exclusive scan of `local`
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -1474,9 +1492,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
         for (int ww = 0; ww < w; ++ww) run += s_wsum[ww];
         for (int i = i0; i < i1; ++i) {
             s_pref[i] = run;
-            run += nparts_of(gld_i32(a.seq_lens + i)) - 1;
+            run += nparts_of(s_len[i]) - 1;
         }
-        if (threadIdx.x == kThreads - 1) s_pref[B] = run;
+        if (threadIdx.x == NT - 1) s_pref[B] = run;
         __syncthreads();
         F = __builtin_amdgcn_readfirstlane(s_pref[B]);
         total = int64_t(F + B) * a.hkv;
@@ -1496,7 +1514,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeAr
                 part = u - s_pref[lo];
             } else {
                 b = u - F;
-                part = nparts_of(gld_i32(a.seq_lens + b)) - 1;
+                part = nparts_of(s_len[b]) - 1;
             }
         } else {
             b = blockIdx.z;
@@ -1597,15 +1615,18 @@ WsLayout ws_layout(int64_t seqs_x_heads, int64_t parts, int d) {
     return w;
 }
 
-// Resident work-groups per compute unit of a decode kernel at a given dynamic LDS size
-// (cached per kernel instance for the last size asked).
-template <typename K>
-int resident_per_cu(K kernel, int dyn_lds) {
+// Resident work-groups per compute unit of the matrix-core decode kernel instance
+// <CDT, QDT, D, BS, G, NW> at a given dynamic LDS size (cached per instance for the last size
+// asked: every instance has the same function type, so the cache is keyed by the template
+// arguments, not by the type).
+template <int CDT, int QDT, int D, int BS, int G, int NW>
+int resident_per_cu(int dyn_lds) {
     static std::atomic<int64_t> cache{-1};
     const int64_t c = cache.load(std::memory_order_relaxed);
     if (c >= 0 && int(c >> 32) == dyn_lds) return int(c & 0xffffffff);
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kThreads, dyn_lds) != hipSuccess || n <= 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<CDT, QDT, D, BS, G, NW>, 64 * NW,
+                                                     dyn_lds) != hipSuccess || n <= 0) {
         (void)hipGetLastError();
         n = 1;
     }
@@ -1619,19 +1640,23 @@ int launch_decode(DecodeArgs a, int B, hipStream_t st) {
         dim3 grid(a.max_parts, a.hkv, B);
         hipLaunchKernelGGL((decode_valu_kernel<CDT, QDT, D, BS, G>), grid, dim3(kThreads), 0, st, a);
     } else {
-        auto kernel = decode_mfma_kernel<CDT, QDT, D, BS, G>;
-        // The (partition, KV head, request) grid is used when all of it is resident at once
-        // (uniform batches: no work-group waits for a slot, none of them is empty); otherwise,
-        // up to kMaxListSeqs requests, the compact item list on about one work-group per slot.
+        // The (partition, KV head, request) grid of kWaves-wave work-groups is used when all
+        // of it is resident at once (uniform batches: no work-group waits for a slot, none of
+        // them is empty); otherwise, up to kMaxListSeqs requests, the compact item list on
+        // about one kListWaves-wave work-group per slot.
         const int64_t grid_items = int64_t(B) * a.max_parts * a.hkv;
-        const int lds = (B + 1) * 4;
-        const int64_t slots = B <= kMaxListSeqs ? int64_t(device_cu_count()) * resident_per_cu(kernel, lds) : 0;
-        if (B <= kMaxListSeqs && grid_items > slots) {
+        const int lds = (2 * B + 1) * 4;
+        const int64_t cus = device_cu_count();
+        const int64_t grid_slots = B <= kMaxListSeqs ? cus * resident_per_cu<CDT, QDT, D, BS, G, kWaves>(0) : 0;
+        if (B <= kMaxListSeqs && grid_items > grid_slots) {
             a.list = 1;
-            hipLaunchKernelGGL(kernel, dim3(static_cast<int>(slots)), dim3(kThreads), lds, st, a);
+            const int64_t slots = cus * resident_per_cu<CDT, QDT, D, BS, G, kListWaves>(lds);
+            hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, D, BS, G, kListWaves>), dim3(static_cast<int>(slots)),
+                               dim3(64 * kListWaves), lds, st, a);
         } else {
             a.list = 0;
-            hipLaunchKernelGGL(kernel, dim3(a.max_parts, a.hkv, B), dim3(kThreads), 0, st, a);
+            hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, D, BS, G, kWaves>), dim3(a.max_parts, a.hkv, B),
+                               dim3(kThreads), 0, st, a);
         }
     }
     return check_launch("pa_decode");
