@@ -93,6 +93,17 @@ def test_mxfp4_write_and_decode(d, bs, G):
     decode_case(c, f"mxfp4 d{d} bs{bs} G{G}")
 
 
+@pytest.mark.parametrize("d,bs,G", [(128, 16, 8), (128, 8, 4), (128, 128, 1), (64, 16, 4), (64, 8, 8)])
+def test_mxfp4_item_list(d, bs, G):
+    """A batch with more (request, KV head, partition) items than the uniform grid keeps
+    resident (100 requests x 4 KV heads x up to 16 partitions of 64 tokens), so the two-wave
+    work-groups walk the compact item list; G = 8 at d 128 takes the merge's column batches."""
+    lens = [1, 17, 300, 1000, 64] * 20
+    assert len(lens) * 4 * -(-1000 // max(64, bs)) > 2048
+    c = build(lens, 4 * G, 4, d, bs, seed=3 * d + bs + G)
+    decode_case(c, f"mxfp4 list d{d} bs{bs} G{G}", partition_tokens=64)
+
+
 def test_mxfp4_write_special_values():
     """Zeros, magnitudes near the bottom and top of bf16, negative zeros and exact ties."""
     build([40, 9], 8, 2, 128, 16, seed=3, special=True)

@@ -179,6 +179,31 @@ def test_supported_set(fmt, d, bs, G):
     run_pair(w, partition_tokens=128)
 
 
+@pytest.mark.parametrize("fmt,d,bs,G", [
+    (f, d, bs, G) for f in ("bf16", "fp8") for d in (64, 128) for bs in (8, 16, 32, 128) for G in (1, 4, 8)
+])
+def test_supported_set_item_list(fmt, d, bs, G):
+    """The same set on a batch with more (request, KV head, partition) items than the uniform
+    grid keeps resident (96 requests x 4 KV heads x up to 13 partitions of 64 tokens, or 7 of
+    128 at block 128: at least 2688 items), so the two-wave work-groups walk the compact item
+    list.  At G = 8 and d = 128 the partition merge has more float4 columns (256) than such a
+    work-group has threads (128) and takes them in two batches."""
+    Hkv = 4
+    lens = np.array([1, bs - 1 if bs > 1 else 1, bs, bs + 1, 300, 777] * 16)
+    B = len(lens)
+    n = int(sum(-(-int(L) // bs) for L in lens)) + 3
+    ops = []
+    for b, L in enumerate(lens):
+        ops += [("add", b)] + ([("append", b, int(L) - 1)] if L > 1 else [])
+    w = workloads.Workload(f"list_{fmt}_d{d}_bs{bs}_G{G}", B=B, Hq=Hkv * G, Hkv=Hkv, d=d, bs=bs, fmt=fmt,
+                           q_fmt="bf16", std=0.5, seq_lens=lens, num_blocks=n,
+                           free_order=np.random.default_rng(7 * bs + G + d).permutation(n).astype(np.int32),
+                           ops=ops, seed_index=61)
+    ptok = max(64, bs)
+    assert B * Hkv * -(-int(lens.max()) // ptok) > 2048   # beyond any resident grid (8 per CU x 256)
+    run_pair(w, partition_tokens=64)
+
+
 # --------------------------------------------------------------------------- structure
 
 def _permuted_copy(g, perm_seed):
