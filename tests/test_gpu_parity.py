@@ -204,6 +204,24 @@ def test_supported_set_item_list(fmt, d, bs, G):
     run_pair(w, partition_tokens=64)
 
 
+@pytest.mark.parametrize("B", [8192, 8193])
+def test_largest_item_list_batch(B):
+    """8192 requests, the largest batch the compact item list takes (its prefix sums and
+    lengths fill 64 KiB of LDS per work-group), and one more, which falls back to the
+    (partition, KV head, request) grid; short random lengths, 64-token partitions."""
+    Hkv, G, d, bs = 1, 4, 128, 16
+    lens = np.random.default_rng(B).integers(1, 97, size=B)
+    n = int(sum(-(-int(L) // bs) for L in lens)) + 3
+    ops = []
+    for b, L in enumerate(lens):
+        ops += [("add", b)] + ([("append", b, int(L) - 1)] if L > 1 else [])
+    w = workloads.Workload(f"batch_{B}", B=B, Hq=Hkv * G, Hkv=Hkv, d=d, bs=bs, fmt="bf16", q_fmt="bf16", std=0.5,
+                           seq_lens=lens, num_blocks=n,
+                           free_order=np.random.default_rng(B + 1).permutation(n).astype(np.int32),
+                           ops=ops, seed_index=62)
+    run_pair(w, partition_tokens=64)
+
+
 # --------------------------------------------------------------------------- structure
 
 def _permuted_copy(g, perm_seed):
