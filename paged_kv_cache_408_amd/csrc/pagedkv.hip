@@ -410,26 +410,49 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_view(const float* bas
                                              static_cast<int>(bytes > 0x7fffffff ? 0x7fffffff : bytes), 0x00020000);
 }
 
+// Column layout shared by finish_partition and merge_rows: the G x D outputs of a (request, KV
+// head) as NC float4 columns (head h = col / (D / 4), dims 4 (col % (D / 4)) .. + 3).  Thread t
+// of an NT-thread work-group takes column t % NC (row slice t / NC) or, when the columns
+// outnumber the threads, columns cb NT + t for its NCB column batches cb.
+template <int D, int G, int NT>
+struct MergeCols {
+    static constexpr int NC = G * D / 4;                 // float4 columns
+    static constexpr int NS = NT / NC > 0 ? NT / NC : 1; // row slices (1 when columns outnumber threads)
+    static constexpr int NCB = NC > NT ? NC / NT : 1;    // column batches per thread
+    static_assert(NC <= NT || NC % NT == 0, "whole column batches");
+    __device__ static int col(int t, int cb) { return NC > NT ? cb * NT + t : t % NC; }
+    __device__ static int slice(int t) { return NC > NT ? 0 : t / NC; }
+};
+
+// A work-group's own partial row, per column batch of the thread: the same floats it would have
+// written to the workspace (max, sum, accumulator slice).
+template <int NCB>
+struct OwnRow {
+    float m[NCB], l[NCB];
+    float4 acc[NCB];
+};
+
 // Log-sum-exp merge of `count` consecutive partial rows (m, l, acc[D]) of each of the G heads
-// of one (request, KV head): head h's rows are row0 + h * head_stride + [0, count).  The block's threads take float4
-// columns of the G x D outputs and split the rows among themselves; each keeps an online
-// (max, sum, accumulator) state, and the slices are combined in LDS.  A NaN max in any row
-// (a bad block id) makes the result NaN.  Writes `out` (rounded) or, when out == nullptr, one
-// partial row per head to (m_dst, l_dst, acc_dst) with the given head stride, by
-// agent-scope stores.
+// of one (request, KV head): head h's rows are row0 + h * head_stride + [0, count).  The block's
+// threads take float4 columns of the G x D outputs (MergeCols) and split the rows among
+// themselves; each keeps an online (max, sum, accumulator) state, and the slices are combined
+// in LDS.  Row own_r (if >= 0) is not read from memory: its values are the calling
+// work-group's own, passed in registers, and are merged at the same place in the same order,
+// so the result is the same bits either way.  A NaN max in any row (a bad block id) makes the
+// result NaN.  Writes `out` (rounded) or, when out == nullptr, one partial row per head to
+// (m_dst, l_dst, acc_dst) with the given head stride, by agent-scope stores.
 template <int QDT, int D, int G, int NT>
 __device__ __forceinline__ void merge_rows(const float* m_src, const float* l_src, const float* acc_src, int64_t row0,
                            int64_t head_stride, int count, typename Elem<QDT>::T* out, float* m_dst, float* l_dst,
-                           float* acc_dst, int64_t dst_head_stride) {
-    constexpr int NC = G * D / 4;               // float4 columns
-    constexpr int NS = NT / NC > 0 ? NT / NC : 1;   // row slices (1 when columns outnumber threads)
-    constexpr int NCB = NC > NT ? NC / NT : 1;  // column batches per thread
-    static_assert(NC <= NT || NC % NT == 0, "whole column batches");
+                           float* acc_dst, int64_t dst_head_stride, int own_r,
+                           const OwnRow<MergeCols<D, G, NT>::NCB>& own) {
+    using MC = MergeCols<D, G, NT>;
+    constexpr int NC = MC::NC, NS = MC::NS, NCB = MC::NCB;
     __shared__ float s_mm[NS][NC], s_ll[NS][NC];
     __shared__ float4 s_num[NS][NC];
     const int t = threadIdx.x;
     for (int cb = 0; cb < NCB; ++cb) {
-    const int col = NC > NT ? cb * NT + t : t % NC, slice = NC > NT ? 0 : t / NC;
+    const int col = MC::col(t, cb), slice = MC::slice(t);
     const int h = col / (D / 4), c4 = col % (D / 4);
     const bool active = slice < NS;
     float M = -INFINITY, den = 0.0f;
@@ -439,9 +462,18 @@ __device__ __forceinline__ void merge_rows(const float* m_src, const float* l_sr
         const int64_t rh = row0 + int64_t(h) * head_stride;     // rows rh .. rh + count - 1
         const auto racc = coherent_view(acc_src + rh * D, int64_t(count) * D);
         for (int r = slice; r < count; r += NS) {
-            const float mr = load_agent(m_src + rh + r);
-            const float lr = load_agent(l_src + rh + r);
-            const auto v = __builtin_amdgcn_raw_buffer_load_b128(racc, (r * D + c4 * 4) * 4, 0, 16);
+            float mr, lr;
+            float4 v;
+            if (r == own_r) {
+                mr = own.m[cb];
+                lr = own.l[cb];
+                v = own.acc[cb];
+            } else {
+                mr = load_agent(m_src + rh + r);
+                lr = load_agent(l_src + rh + r);
+                const auto vi = __builtin_amdgcn_raw_buffer_load_b128(racc, (r * D + c4 * 4) * 4, 0, 16);
+                v = make_float4(__int_as_float(vi[0]), __int_as_float(vi[1]), __int_as_float(vi[2]), __int_as_float(vi[3]));
+            }
             nan_seen |= __builtin_isnan(mr);
             if (mr > M) {   // new maximum: rescale the state (exp2(-inf) = 0 on the first row)
                 const float f = __builtin_amdgcn_exp2f(M - mr);
@@ -451,10 +483,10 @@ __device__ __forceinline__ void merge_rows(const float* m_src, const float* l_sr
             }
             const float wgt = __builtin_amdgcn_exp2f(mr - M);
             den = fmaf(wgt, lr, den);
-            num.x = fmaf(wgt, __int_as_float(v[0]), num.x);
-            num.y = fmaf(wgt, __int_as_float(v[1]), num.y);
-            num.z = fmaf(wgt, __int_as_float(v[2]), num.z);
-            num.w = fmaf(wgt, __int_as_float(v[3]), num.w);
+            num.x = fmaf(wgt, v.x, num.x);
+            num.y = fmaf(wgt, v.y, num.y);
+            num.z = fmaf(wgt, v.z, num.z);
+            num.w = fmaf(wgt, v.w, num.w);
         }
         if (nan_seen) M = __builtin_nanf("");
         s_mm[slice][col] = M;
@@ -503,97 +535,154 @@ __device__ __forceinline__ void merge_rows(const float* m_src, const float* l_sr
 
 // End of one partition of one (request, KV head): merges the waves' states held in LDS
 // (m[w][h], l[w][h] and acc[w][h][d] at acc + w * acc_wave_stride; scores in log2 units, acc
-// unnormalised), then writes
-// `out` when the request has a single partition, or the partition's partial row followed by
-// the log-sum-exp merge of the request's partitions by the last work-group to finish, in up
-// to two levels: the last of each group of kMergeGroup partitions merges that group; with
-// more than one group, the last group-merger then merges the groups.  Partials are written
-// with agent-scope stores (coherent across the XCDs' L2s); draining the store counter makes
-// them visible at agent scope before a ticket is taken, and mergers read them with
-// agent-scope loads.  This avoids agent-scope fences, whose L2 write-back/invalidate would
-// serialise the work-groups of an XCD.  Counters are left at zero.  Work-group uniform; ends
-// with a barrier, so the caller may reuse the LDS arrays afterwards.
-template <int QDT, int D, int G, int NW>
+// unnormalised) into this work-group's own partial (max, sum, accumulator), in registers in
+// the merge's column layout, then writes `out` when the request has a single partition, or
+// else takes part in the log-sum-exp merge of the request's partitions, in up to two levels:
+// the last of each group of kMergeGroup partitions merges that group; with more than one
+// group, the last group-merger then merges the groups.
+// A work-group learns that it is its group's last in one of two ways:
+//  - the group's ticket, read (agent scope) while the waves' states are merged, already counts
+//    every other member: it merges at once, with its own row from registers, and writes no
+//    partial and takes no ticket (every other member has taken its ticket and will not touch
+//    the counter again, so it resets it);
+//  - otherwise it writes its partial row with agent-scope stores (coherent across the XCDs'
+//    L2s), drains the store counter so that they are visible at agent scope, and takes a
+//    ticket; the member that draws the last one merges, reading the others' rows with
+//    agent-scope loads.
+// Both paths merge the same rows in the same order with the same values, so the output does not
+// depend on which one ran.  The first is taken only where EARLY is set (bf16 caches: measured
+// 1% faster on the Llama-shaped layer and 2% on the ragged batch; fp8 caches 5% slower on the
+// ragged batch, whose many short items mostly end up on the second path and then pay the
+// ticket read too).  No work-group waits for another, and no agent-scope fence (whose L2
+// write-back/invalidate would serialise the work-groups of an XCD) is used.  Counters are left
+// at zero.  Work-group uniform; ends with a barrier, so the caller may reuse the LDS arrays
+// afterwards.
+template <int QDT, int D, int G, int NW, bool EARLY>
 __device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int g, int part, int nparts, float vsc, bool any_bad,
                                  const float* s_m, const float* s_l, const float* s_acc, int acc_wave_stride) {
     using QT = typename Elem<QDT>::T;
+    constexpr int NT = 64 * NW;
+    using MC = MergeCols<D, G, NT>;
+    constexpr int NC = MC::NC, NCB = MC::NCB;
     __shared__ int s_last;
     const int hq = a.hkv * G;
     QT* out = reinterpret_cast<QT*>(a.out) + (int64_t(b) * hq + int64_t(g) * G) * D;
     const bool single = nparts == 1;
-    for (int idx = threadIdx.x; idx < G * D; idx += 64 * NW) {
-        const int h = idx / D, dim = idx - h * D;
+    const int ngroups = (nparts + kMergeGroup - 1) / kMergeGroup;
+    const int grp = part / kMergeGroup;
+    const int first = grp * kMergeGroup, count = min(kMergeGroup, nparts - first);
+    const int64_t bg = int64_t(b) * a.hkv + g;
+    int* ctr = a.ws_ctr + bg * a.max_groups + grp;
+    int seen = 0;
+    if (EARLY && !single && threadIdx.x == 0) seen = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    const int t = threadIdx.x;
+    OwnRow<NCB> own;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int col = MC::col(t, cb);
+        const int h = col / (D / 4), c4 = col % (D / 4);
         float M = s_m[h];
 #pragma unroll
         for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, s_m[ww * G + h]);
-        float num = 0.0f, den = 0.0f;
+        float den = 0.0f;
+        float num[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) {
             const float f = __builtin_amdgcn_exp2f(s_m[ww * G + h] - M);   // 0 for an idle wave
-            num = fmaf(f, s_acc[ww * acc_wave_stride + h * D + dim], num);
+            const float* src = s_acc + ww * acc_wave_stride + h * D + 4 * c4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) num[e] = fmaf(f, src[e], num[e]);
             den = fmaf(f, s_l[ww * G + h], den);
         }
         if (any_bad) {
-            num = __builtin_nanf("");
+#pragma unroll
+            for (int e = 0; e < 4; ++e) num[e] = __builtin_nanf("");
             den = __builtin_nanf("");
             M = __builtin_nanf("");
         }
         if (single) {
-            const float o = num / den * vsc;
-            if constexpr (QDT == PA_DTYPE_BF16) gst(out + idx, f32_to_bf16(o)); else gst(out + idx, o);
-        } else {
-            const int64_t row = (int64_t(b) * hq + int64_t(g) * G + h) * a.max_parts + part;
-            store_agent(a.ws_acc + row * D + dim, num * vsc);
-            if (dim == 0) {
-                store_agent(a.ws_m + row, M);
-                store_agent(a.ws_l + row, den);
+            if (NC > NT || t < NC) {   // one thread per column
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float o = num[e] / den * vsc;
+                    if constexpr (QDT == PA_DTYPE_BF16) gst(out + h * D + 4 * c4 + e, f32_to_bf16(o));
+                    else gst(out + h * D + 4 * c4 + e, o);
+                }
             }
+        } else {
+            own.m[cb] = M;
+            own.l[cb] = den;
+            own.acc[cb] = make_float4(num[0] * vsc, num[1] * vsc, num[2] * vsc, num[3] * vsc);
         }
     }
     if (single) {
         __syncthreads();
         return;
     }
-    const int ngroups = (nparts + kMergeGroup - 1) / kMergeGroup;
-    const int grp = part / kMergeGroup;
-    const int64_t bg = int64_t(b) * a.hkv + g;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int* ctr = a.ws_ctr + bg * a.max_groups + grp;
-        const int members = min(kMergeGroup, nparts - grp * kMergeGroup);
-        const int ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = ticket == members - 1;
-        if (s_last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool early = false;
+    if constexpr (EARLY) {
+        if (threadIdx.x == 0) s_last = seen == count - 1;
+        __syncthreads();
+        early = s_last;
+        __syncthreads();             // s_last is rewritten below
     }
-    __syncthreads();
-    const bool merge1 = s_last;
-    __syncthreads();                 // s_last is rewritten below
-    if (!merge1) return;
+    if (early) {
+        if (threadIdx.x == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        if (NC > NT || t < NC) {     // one thread per column writes the partial row
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                const int col = MC::col(t, cb);
+                const int h = col / (D / 4), c4 = col % (D / 4);
+                const int64_t row = (int64_t(b) * hq + int64_t(g) * G + h) * a.max_parts + part;
+                float* dst = a.ws_acc + row * D + 4 * c4;
+                store_agent(dst + 0, own.acc[cb].x);
+                store_agent(dst + 1, own.acc[cb].y);
+                store_agent(dst + 2, own.acc[cb].z);
+                store_agent(dst + 3, own.acc[cb].w);
+                if (c4 == 0) {
+                    store_agent(a.ws_m + row, own.m[cb]);
+                    store_agent(a.ws_l + row, own.l[cb]);
+                }
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const int ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = ticket == count - 1;
+            if (s_last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        const bool merge1 = s_last;
+        __syncthreads();             // s_last is rewritten below
+        if (!merge1) return;
+    }
     const int64_t rows1 = (int64_t(b) * hq + int64_t(g) * G) * a.max_parts;    // head h: + h * max_parts
-    const int first = grp * kMergeGroup, count = min(kMergeGroup, nparts - first);
     if (ngroups == 1) {
-        merge_rows<QDT, D, G, 64 * NW>(a.ws_m, a.ws_l, a.ws_acc, rows1 + first, a.max_parts, count, out, nullptr, nullptr,
-                              nullptr, 0);
+        merge_rows<QDT, D, G, NT>(a.ws_m, a.ws_l, a.ws_acc, rows1 + first, a.max_parts, count, out, nullptr, nullptr,
+                                  nullptr, 0, part - first, own);
         __syncthreads();
         return;
     }
     const int64_t rows2 = (int64_t(b) * hq + int64_t(g) * G) * a.max_groups;
-    merge_rows<QDT, D, G, 64 * NW>(a.ws_m, a.ws_l, a.ws_acc, rows1 + first, a.max_parts, count, nullptr, a.ws_m2 + rows2 + grp,
-                          a.ws_l2 + rows2 + grp, a.ws_acc2 + (rows2 + grp) * D, a.max_groups);
+    merge_rows<QDT, D, G, NT>(a.ws_m, a.ws_l, a.ws_acc, rows1 + first, a.max_parts, count, nullptr, a.ws_m2 + rows2 + grp,
+                              a.ws_l2 + rows2 + grp, a.ws_acc2 + (rows2 + grp) * D, a.max_groups, part - first, own);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
-        int* ctr = a.ws_ctr + int64_t(a.max_groups) * a.hkv * a.num_seqs + bg;
-        const int ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int* ctr2 = a.ws_ctr + int64_t(a.max_groups) * a.hkv * a.num_seqs + bg;
+        const int ticket = __hip_atomic_fetch_add(ctr2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = ticket == ngroups - 1;
-        if (s_last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (s_last) __hip_atomic_store(ctr2, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     const bool merge2 = s_last;
     __syncthreads();
     if (!merge2) return;
-    merge_rows<QDT, D, G, 64 * NW>(a.ws_m2, a.ws_l2, a.ws_acc2, rows2, a.max_groups, ngroups, out, nullptr, nullptr, nullptr, 0);
+    merge_rows<QDT, D, G, NT>(a.ws_m2, a.ws_l2, a.ws_acc2, rows2, a.max_groups, ngroups, out, nullptr, nullptr, nullptr, 0,
+                              -1, own);
     __syncthreads();
 }
 
@@ -894,7 +983,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeArgs 
         }
     }
     const bool any_bad = __syncthreads_or(bad);
-    finish_partition<QDT, D, G, kWaves>(a, b, g, part, nparts, vsc, any_bad, &s_m[0][0], &s_l[0][0], &s_acc[0][0][0],
+    finish_partition<QDT, D, G, kWaves, false>(a, b, g, part, nparts, vsc, any_bad, &s_m[0][0], &s_l[0][0], &s_acc[0][0][0],
                                 G * D);
 }
 
@@ -1460,7 +1549,7 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_mfma_kernel(const DecodeArg
             }
         }
         const bool any_bad = __syncthreads_or(bad);
-        finish_partition<QDT, D, G, NW>(a, b, g, part, nparts, vsc, any_bad, &s_m[0][0], &s_l[0][0],
+        finish_partition<QDT, D, G, NW, CDT == PA_DTYPE_BF16>(a, b, g, part, nparts, vsc, any_bad, &s_m[0][0], &s_l[0][0],
                                     reinterpret_cast<const float*>(&s_tile[0][0]), int(sizeof(s_tile[0]) / 4));
     };
 

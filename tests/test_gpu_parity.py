@@ -137,6 +137,21 @@ def test_long_context_scaled():
     run_pair(workloads.long_context(B=2, L=20000, seed_index=41, name="long_ctx_20k"), partition_tokens=512)
 
 
+@pytest.mark.parametrize("ptok", [0, 512])
+def test_merge_paths_bit_identical(ptok):
+    """A partition's work-group merges its group either at once (the group's ticket already
+    counted every other member when it finished) or after taking the last ticket, depending on
+    timing; both must give the same bits.  20 launches of a bf16 batch with 16 equal partitions
+    per request (one merge group, automatic size) or 40 of 512 tokens (three groups, two merge
+    levels): every output equals the first bit for bit, and the first matches the oracle."""
+    w = workloads.long_context(B=2, L=20000, seed_index=43, name=f"merge_paths_{ptok}")
+    g, o, got, ref = run_pair(w, partition_tokens=ptok)
+    first = g.decode()
+    for _ in range(20):
+        again = g.decode()
+        assert torch.equal(again.view(torch.int16), first.view(torch.int16)), "merge result depends on the path"
+
+
 def test_long_context_scaled_auto():
     """The same layer with automatic partitions: 16 (request, KV head) pairs, so each request
     is cut into 16 equal partitions and merged in one group."""
