@@ -630,21 +630,36 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int
     if (early) {
         if (threadIdx.x == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
-        if (NC > NT || t < NC) {     // one thread per column writes the partial row
+        // the partial row, written by consecutive lanes to consecutive floats (whole 64-byte
+        // segments per store): staged through the waves' state area, which no thread reads
+        // once every thread has passed this barrier
+        __syncthreads();
+        float* stage = const_cast<float*>(s_acc);
+        __shared__ float s_om[G], s_ol[G];
+        if (NC > NT || t < NC) {
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
                 const int col = MC::col(t, cb);
                 const int h = col / (D / 4), c4 = col % (D / 4);
-                const int64_t row = (int64_t(b) * hq + int64_t(g) * G + h) * a.max_parts + part;
-                float* dst = a.ws_acc + row * D + 4 * c4;
-                store_agent(dst + 0, own.acc[cb].x);
-                store_agent(dst + 1, own.acc[cb].y);
-                store_agent(dst + 2, own.acc[cb].z);
-                store_agent(dst + 3, own.acc[cb].w);
+                float* p = stage + h * D + 4 * c4;
+                p[0] = own.acc[cb].x;
+                p[1] = own.acc[cb].y;
+                p[2] = own.acc[cb].z;
+                p[3] = own.acc[cb].w;
                 if (c4 == 0) {
-                    store_agent(a.ws_m + row, own.m[cb]);
-                    store_agent(a.ws_l + row, own.l[cb]);
+                    s_om[h] = own.m[cb];
+                    s_ol[h] = own.l[cb];
                 }
+            }
+        }
+        __syncthreads();
+        for (int idx = t; idx < G * D; idx += NT) {
+            const int h = idx / D, dim = idx - h * D;
+            const int64_t row = (int64_t(b) * hq + int64_t(g) * G + h) * a.max_parts + part;
+            store_agent(a.ws_acc + row * D + dim, stage[idx]);
+            if (dim == 0) {
+                store_agent(a.ws_m + row, s_om[h]);
+                store_agent(a.ws_l + row, s_ol[h]);
             }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
