@@ -551,9 +551,9 @@ __device__ __forceinline__ void merge_rows(const float* m_src, const float* l_sr
 //    agent-scope loads.
 // Both paths merge the same rows in the same order with the same values, so the output does not
 // depend on which one ran.  The first is taken only where EARLY is set (bf16 caches: measured
-// 1% faster on the Llama-shaped layer and 2% on the ragged batch; fp8 caches 5% slower on the
-// ragged batch, whose many short items mostly end up on the second path and then pay the
-// ticket read too).  No work-group waits for another, and no agent-scope fence (whose L2
+// 1% faster on the Llama-shaped layer and 2% on the ragged batch; with it, fp8 caches were 5%
+// slower on the ragged batch, whose many short items mostly end up on the second path and then
+// pay the ticket read too, and 4-bit caches 3-7% slower on both workloads).  No work-group waits for another, and no agent-scope fence (whose L2
 // write-back/invalidate would serialise the work-groups of an XCD) is used.  Counters are left
 // at zero.  Work-group uniform; ends with a barrier, so the caller may reuse the LDS arrays
 // afterwards.
