@@ -535,7 +535,7 @@ __device__ __forceinline__ void merge_rows(const float* m_src, const float* l_sr
 
 // End of one partition of one (request, KV head): merges the waves' states held in LDS
 // (m[w][h], l[w][h] and acc[w][h][d] at acc + w * acc_wave_stride; scores in log2 units, acc
-// unnormalised) into this work-group's own partial (max, sum, accumulator), in registers in
+// unnormalised; the acc area is then reused to stage the partial row) into this work-group's own partial (max, sum, accumulator), in registers in
 // the merge's column layout, then writes `out` when the request has a single partition, or
 // else takes part in the log-sum-exp merge of the request's partitions, in up to two levels:
 // the last of each group of kMergeGroup partitions merges that group; with more than one
@@ -559,7 +559,7 @@ __device__ __forceinline__ void merge_rows(const float* m_src, const float* l_sr
 // afterwards.
 template <int QDT, int D, int G, int NW, bool EARLY>
 __device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int g, int part, int nparts, float vsc, bool any_bad,
-                                 const float* s_m, const float* s_l, const float* s_acc, int acc_wave_stride) {
+                                 const float* s_m, const float* s_l, float* s_acc, int acc_wave_stride) {
     using QT = typename Elem<QDT>::T;
     constexpr int NT = 64 * NW;
     using MC = MergeCols<D, G, NT>;
@@ -634,7 +634,7 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int
         // segments per store): staged through the waves' state area, which no thread reads
         // once every thread has passed this barrier
         __syncthreads();
-        float* stage = const_cast<float*>(s_acc);
+        float* stage = s_acc;
         __shared__ float s_om[G], s_ol[G];
         if (NC > NT || t < NC) {
 #pragma unroll
@@ -1565,7 +1565,7 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_mfma_kernel(const DecodeArg
         }
         const bool any_bad = __syncthreads_or(bad);
         finish_partition<QDT, D, G, NW, CDT == PA_DTYPE_BF16>(a, b, g, part, nparts, vsc, any_bad, &s_m[0][0], &s_l[0][0],
-                                    reinterpret_cast<const float*>(&s_tile[0][0]), int(sizeof(s_tile[0]) / 4));
+                                    reinterpret_cast<float*>(&s_tile[0][0]), int(sizeof(s_tile[0]) / 4));
     };
 
     // ---- work items: the compact list (prefix sums of each request's full partitions, all but
