@@ -25,7 +25,7 @@ Modules:
 * ``allocator``  -- the block allocator model (FIFO free list, refcounts, fork, COW).
 * ``attention``  -- slot-mapped scatter, block-table gather, exact softmax(q.K^T*scale).V,
                     the split-K / log-sum-exp variant and a pure-Python brute force.
-* ``measures``   -- cache-size formula, contiguous and paged waste, algorithmic bytes.
+* ``measures``   -- cache footprint, slots held and filled (reserved or paged), algorithmic bytes.
 
 Every function is pinned by ``tests/test_oracle_*.py`` to something other than itself
 (the pages' worked examples, closed forms, invariants, library routines, brute force).

@@ -3,8 +3,8 @@
 What the pages fix:
 
 * The cache is split into fixed-size blocks of ``block_size`` token slots; a request's
-  tokens go into whatever blocks are free, and a per-request block table maps logical
-  block j to a physical block, like an OS page table ("KV Cache Optimization and
+  a request's tokens may sit in any free blocks, and a per-request block table maps logical
+  block j to a physical block, as an operating system's page table maps pages ("KV Cache Optimization and
   PagedAttention", prose on paging; "PagedAttention: Optimizing KV Cache Utilization in
   Large Language Models", "The Mechanics of PagedAttention").
 * Blocks are granted on demand: a request holds one block and gets the next when that one

@@ -13,7 +13,7 @@ the softmax of q.K^T / sqrt(d_k).  Readings where that section is silent or loos
 * It omits V.  The output is the weighted sum of the value vectors, o = A.V.
 * Decode has query length 1; the new token's K/V are written before the attention, so
   ``seq_lens[b]`` counts the cached tokens including the new one and the query sees
-  logical positions 0..L_b-1 (each new token attends to every previous token: "KV Cache
+  logical positions 0..L_b-1 (a new token's attention covers all earlier tokens: "KV Cache
   Optimization and PagedAttention", first paragraph; "KV Cache Management", "Why Does This
   Exist?").  No other mask.
 * ``scale`` is taken as given (1/sqrt(d) in the workloads), widened to float64.
@@ -76,10 +76,15 @@ def kv_write(k, v, slot_mapping, k_cache, v_cache, block_size: int, fmt: str,
 
 
 def copy_blocks(k_cache, v_cache, pairs) -> None:
-    """Whole-block copies src -> dst (the copy-on-write step), in place."""
+    """Whole-block copies src -> dst (the copy-on-write step: "KV Cache Optimization and
+    PagedAttention", prose on shared prefix blocks), in place, K and V, every head, row and
+    dim.  A pair naming a block outside the pool is skipped, as the library's contract for
+    its block copy states."""
+    n = k_cache.shape[0]
     for src, dst in pairs:
-        k_cache[dst] = k_cache[src]
-        v_cache[dst] = v_cache[src]
+        if 0 <= src < n and 0 <= dst < n:
+            k_cache[dst] = k_cache[src]
+            v_cache[dst] = v_cache[src]
 
 
 def mx_tile_view(cache, block_size: int, d: int):
@@ -154,7 +159,7 @@ def prefill(q, k_cache, v_cache, block_tables, seq_lens, query_start, scale: flo
 
     The pages' step before decode: a prompt's K/V are computed once and stored ("KV Cache
     Management", "Why Does This Exist?": the first 1,000 tokens' keys and values are saved
-    as they are calculated), and every token attends to every token before it ("KV Cache
+    as they are calculated), and a token's attention covers all tokens before it ("KV Cache
     Optimization and PagedAttention", first paragraph).  Readings: the new tokens' K/V are
     written into the cache first (as for decode), so request b's L_b = seq_lens[b] cached
     tokens include its n_b = query_start[b+1] - query_start[b] new ones, which are its last

@@ -110,11 +110,6 @@ def e4m3_quantize(x_f64: np.ndarray, scale) -> np.ndarray:
     return e4m3_encode(q)
 
 
-def e4m3_dequantize(codes: np.ndarray, scale: float) -> np.ndarray:
-    """Exact float64 value of codes times the float32 scale."""
-    return e4m3_bits_to_f64(codes) * np.asarray(scale, dtype=np.float32).astype(np.float64)
-
-
 # ----------------------------------------------------------------------------- 4-bit: OCP MXFP4
 #
 # The pages allow a cache "down to 8-bit or 4-bit" and fix no 4-bit format.  The reading taken

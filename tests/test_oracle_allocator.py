@@ -52,13 +52,13 @@ def test_first_token_takes_one_block_next_block_when_full():
     assert s == [2 * 16] and a.stats()["used"] == 2
 
 
-def test_waste_stat_is_sum_of_paged_waste():
+def test_waste_stat_is_sum_of_unused_slots():
     a = Allocator(100, 16)
     lens = [1, 16, 17, 200, 31]
     for i, L in enumerate(lens):
         a.add(i)
         a.append(i, L)
-    assert a.stats()["waste_slots"] == sum(M.paged_waste(L, 16) for L in lens)
+    assert a.stats()["waste_slots"] == sum(M.unused_slots(L, block_size=16) for L in lens)
     assert a.stats()["waste_slots"] == 15 + 0 + 15 + 8 + 1
 
 

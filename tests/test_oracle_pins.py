@@ -40,40 +40,128 @@ def test_pages_worked_examples():
     seen = set()
     for name, args, want in _golden():
         seen.add(name)
-        if name == "kv_cache_gb_1dp":
-            gb = M.kv_cache_bytes(*args) / 1e9
+        if name == "footprint_gb_1dp":
+            gb = M.footprint_bytes(*args) / 1e9
             assert f"{gb:.1f}" == f"{want:.1f}"
-        elif name == "contiguous_waste":
-            assert M.contiguous_waste(*args) == want
-        elif name == "paged_waste":
-            assert M.paged_waste(*args) == want
-        elif name == "paged_waste_bound":
+        elif name == "reserved_unused":
+            tokens, reserve = args
+            assert M.unused_slots(tokens, reserve=reserve) == want
+        elif name == "blocks_unused":
+            tokens, bs = args
+            assert M.unused_slots(tokens, block_size=bs) == want
+        elif name == "blocks_unused_max":
             bs = args[0]
-            assert max(M.paged_waste(L, bs) for L in range(1, 5000)) == want
+            assert max(M.unused_slots(L, block_size=bs) for L in range(1, 5000)) == want
         elif name == "default_block_size":
             assert want == 16
         else:
             raise AssertionError(f"unknown golden entry {name}")
-    assert {"kv_cache_gb_1dp", "contiguous_waste", "paged_waste", "paged_waste_bound"} <= seen
+    assert {"footprint_gb_1dp", "reserved_unused", "blocks_unused", "blocks_unused_max"} <= seen
 
 
-def test_kv_cache_bytes_exact_and_decode_bytes_agree():
+def test_footprint_exact_and_decode_bytes_agree():
     """The listing's product is 2*32*8*128*4096*16*2; the per-layer KV term of the
     algorithmic byte model times 32 layers must equal it."""
-    assert M.kv_cache_bytes(32, 8, 128, 4096, 16, 2) == 8_589_934_592
+    assert M.footprint_bytes(32, 8, 128, 4096, 16, 2) == 8_589_934_592
     per_layer = M.decode_bytes([4096] * 16, 32, 8, 128, 16, kv_bytes=2, q_bytes=2, out_bytes=2)
     kv = 2 * 8 * 4096 * 128 * 2 * 16
     assert per_layer == kv + 16 * 32 * 128 * 4 + 16 * 256 * 4 + 16 * 4
-    assert 32 * kv == M.kv_cache_bytes(32, 8, 128, 4096, 16, 2)
+    assert 32 * kv == M.footprint_bytes(32, 8, 128, 4096, 16, 2)
+
+
+def test_footprint_counts_each_vector_once():
+    """Each factor enters once: doubling any one of layers, heads, dims, tokens, requests or
+    bytes doubles the footprint, and one layer of one head for one token of one request holds
+    one K and one V vector."""
+    base = (3, 5, 7, 11, 13, 2)
+    f0 = M.footprint_bytes(*base)
+    for i in range(6):
+        args = list(base)
+        args[i] *= 2
+        assert M.footprint_bytes(*args) == 2 * f0
+    assert M.footprint_bytes(1, 1, 128, 1, 1, 2) == 2 * 128 * 2
 
 
 @pytest.mark.parametrize("bs", [8, 16, 32, 128])
-def test_paged_waste_bound_bruteforce(bs):
-    """Paged waste never exceeds block-1 and is zero exactly on block multiples."""
+def test_paged_unused_bound_bruteforce(bs):
+    """Paged waste never exceeds block-1 and is zero exactly on block multiples; held slots
+    are the fewest whole blocks that cover the request (brute force over block counts)."""
     for L in range(1, 20001):
-        w = M.paged_waste(L, bs)
+        held, filled = M.slot_budget(L, block_size=bs)
+        assert filled == L and held % bs == 0
+        assert held >= L and held - bs < L
+        w = M.unused_slots(L, block_size=bs)
         assert 0 <= w <= bs - 1
         assert (w == 0) == (L % bs == 0)
+
+
+def test_slot_budget_rejects_ambiguous_or_short_placements():
+    with pytest.raises(ValueError):
+        M.slot_budget(10)
+    with pytest.raises(ValueError):
+        M.slot_budget(10, reserve=16, block_size=16)
+    with pytest.raises(ValueError):
+        M.slot_budget(20, reserve=16)
+
+
+def test_copy_blocks_hand_worked():
+    """The copy-on-write copy, by hand: two (src, dst) pairs move whole blocks, K and V both,
+    from src to dst (not the other way), every head, row and dim; other blocks are untouched;
+    a pair naming a block outside the pool is skipped (the library's stated contract for
+    pa_copy_blocks)."""
+    N, H, bs, d = 5, 2, 3, 2
+    k = np.arange(N * H * bs * d, dtype=np.float32).reshape(N, H, bs, d)
+    v = -k - 1
+    k0, v0 = k.copy(), v.copy()
+    A.copy_blocks(k, v, [(0, 3), (4, 1), (2, 5), (-1, 2)])
+    # block 3 now holds block 0's K and V; block 1 holds block 4's
+    assert k[3, 1, 2, 1] == 0 * 12 + 1 * 6 + 2 * 2 + 1 == k0[0, 1, 2, 1]
+    assert v[3, 0, 0, 0] == -1.0
+    assert k[1, 0, 1, 0] == 4 * 12 + 0 * 6 + 1 * 2 + 0 == 50
+    assert v[1, 1, 2, 1] == -(4 * 12 + 1 * 6 + 2 * 2 + 1) - 1 == -60
+    assert np.array_equal(k[3], k0[0]) and np.array_equal(v[3], v0[0])
+    assert np.array_equal(k[1], k0[4]) and np.array_equal(v[1], v0[4])
+    # sources and every other block unchanged; the out-of-range pairs wrote nothing
+    for blk in (0, 2, 4):
+        assert np.array_equal(k[blk], k0[blk]) and np.array_equal(v[blk], v0[blk])
+
+
+def test_copy_on_write_keeps_every_sequence_readable():
+    """Copy-on-write through the oracle's allocator, write and copy: a parent and a forked
+    child share a partly filled block; appending to the child moves it to a fresh block, whose
+    (old, new) pair copy_blocks copies before the write.  Read through their tables, both
+    sequences then hold exactly their own rows (the parent's prefix in both, each one's own
+    new row in its own position), and the shared block still holds only the parent's rows."""
+    rng = np.random.default_rng(3)
+    N, H, bs, d = 8, 2, 4, 3
+    al = Allocator(N, bs, list(rng.permutation(N)))
+    k = np.full((N, H, bs, d), np.nan, np.float32)
+    v = np.full_like(k, np.nan)
+    al.add(0)
+    rows_k = rng.standard_normal((6, H, d)).astype(np.float32)
+    rows_v = rng.standard_normal((6, H, d)).astype(np.float32)
+    slots, cow = al.append(0, 6)
+    assert not cow
+    A.kv_write(rows_k, rows_v, np.array(slots), k, v, bs, "f32")
+    al.fork(0, 1)
+    child_k = rng.standard_normal((1, H, d)).astype(np.float32)
+    child_v = rng.standard_normal((1, H, d)).astype(np.float32)
+    s_child, cow = al.append(1, 1)
+    assert len(cow) == 1
+    A.copy_blocks(k, v, cow)
+    A.kv_write(child_k, child_v, np.array(s_child), k, v, bs, "f32")
+    tab, lens = al.block_table([0, 1], 4)
+    for h in range(H):
+        pk = A.gather(k, tab[0], lens[0], h, bs, "f32")
+        ck = A.gather(k, tab[1], lens[1], h, bs, "f32")
+        cv = A.gather(v, tab[1], lens[1], h, bs, "f32")
+        assert np.array_equal(pk, rows_k[:, h].astype(np.float64))
+        assert np.array_equal(ck[:6], rows_k[:, h].astype(np.float64))
+        assert np.array_equal(ck[6], child_k[0, h].astype(np.float64))
+        assert np.array_equal(cv[6], child_v[0, h].astype(np.float64))
+    src, dst = cow[0]
+    assert tab[0][1] == src and tab[1][1] == dst
+    assert np.isnan(k[src, :, 2:]).all()       # the shared block's unfilled rows stay unwritten
 
 
 # --------------------------------------------------------------------------- helpers
