@@ -10,8 +10,10 @@ unit).
 One step is one pass of the whole hot path over the batch:
   1. host allocator: append one token to each request (slots; copy-on-write pairs, if any,
      are copied with pa_copy_blocks in every layer),
-  2. block-table export to pinned host memory and an async copy to the device,
-  3. for each of the 32 layers: pa_kv_write of the 16 new tokens' K/V, then pa_decode.
+  2. block-table export: the table rows, lengths and the new tokens' slots staged in one
+     pinned host buffer and moved to the device by one pa_upload kernel on the launch stream,
+  3. pa_kv_write of the 16 new tokens' K/V for each of the 32 layers, then the 32 layers'
+     pa_decode launches back to back.
 Requests grow by one token per step, as in generation.
 
 Reported (one JSON line): `value` = algorithmic bytes of the whole step (every request's
@@ -19,7 +21,9 @@ cached K/V once per KV head, q, out, table entries, lengths; plus the write's ro
 slots) / wall time per step.  `roofline` = pa_decode (a single kernel launch per layer)
 measured with HIP events on the launch stream around each step's 32 back-to-back decode
 launches (the layers' K/V writes are issued first).  `cpu_baseline` = the float64 oracle
-timed on a bounded sample of the same per-request work on the host.
+timed on a bounded sample of the same per-request work on the host.  Each run also prints,
+on stderr, where a step's time goes: host microseconds per phase and HIP-event microseconds
+of the upload, the writes, the decodes and the device's idle time between steps.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--graph]   # --graph: replay each step from HIP graphs
     python bench.py --workload {ragged_prefix,long_context,sweep,mxfp4}   # other workloads' decode rates
@@ -29,6 +33,8 @@ timed on a bounded sample of the same per-request work on the host.
 """
 
 import argparse
+import contextlib
+import gc
 import hashlib
 import json
 import math
@@ -50,6 +56,26 @@ KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_408_amd", "csrc", f) for f 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+@contextlib.contextmanager
+def gc_held():
+    """Python's cyclic garbage collector held off over a timed region, as timeit does.  A full
+    collection walks every tracked object (about 170k once torch is imported: 40-55 ms), and
+    when one lands inside the region the device idles for that long: a fresh box's first run,
+    which also compiles this repository's modules to bytecode, shifted one into the timed steps
+    (one step's allocator call took 37.7 ms).  Objects that exist before the region are
+    frozen, so a collection after it stays cheap."""
+    gc.collect()
+    gc.freeze()
+    was_enabled = gc.isenabled()
+    gc.disable()
+    try:
+        yield
+    finally:
+        if was_enabled:
+            gc.enable()
+        gc.unfreeze()
 
 
 # ----------------------------------------------------------------------------- byte model
@@ -143,6 +169,38 @@ def cpu_baseline(seconds: float):
 
 # ----------------------------------------------------------------------------- GPU step
 
+def report_phases(host_marks, evs, t0, t1, layers):
+    """Where a timed step's time goes, on stderr: host microseconds per phase (allocator,
+    staging the tables and slots, enqueueing the upload, the writes and the decodes) and
+    HIP-event microseconds on the launch stream (upload, writes, decodes, and the gap between
+    one step's last decode and the next step's upload).  A gap means the device waited for the
+    host; host enqueue times beyond the device's show where."""
+    import statistics as st
+
+    def us(x):
+        return f"{st.mean(x):8.1f} {st.median(x):8.1f} {max(x):8.1f}"
+
+    n = len(host_marks)
+    ph = [[(m[k + 1] - m[k]) * 1e6 for m in host_marks] for k in range(5)]
+    names = ["allocator", "stage tables", "upload enqueue", f"{layers} writes enqueue", f"{layers} decodes enqueue"]
+    log(f"phase (us)               mean   median      max   over {n} timed steps")
+    for nm, x in zip(names, ph):
+        log(f"  host {nm:<18s}{us(x)}")
+    g_up = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
+    g_wr = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
+    g_de = [e[2].elapsed_time(e[3]) * 1e3 for e in evs]
+    gap = [evs[i][3].elapsed_time(evs[i + 1][0]) * 1e3 for i in range(len(evs) - 1)] or [0.0]
+    log(f"  gpu  upload            {us(g_up)}")
+    log(f"  gpu  {layers} writes         {us(g_wr)}")
+    log(f"  gpu  {layers} decodes        {us(g_de)}")
+    log(f"  gpu  idle between steps{us(gap)}")
+    busy = sum(g_up) + sum(g_wr) + sum(g_de)
+    log(f"  device busy {busy / 1e3:.3f} ms of {(t1 - t0) * 1e3:.3f} ms wall ({100 * busy / 1e3 / ((t1 - t0) * 1e3):.1f}%); "
+        f"host enqueue per step {st.mean([m[5] - m[0] for m in host_marks]) * 1e6:.1f} us; "
+        f"last step enqueued at {(host_marks[-1][5] - t0) * 1e3:.3f} ms of the wall (near the wall: host-bound)")
+
+
+
 def run(args):
     import numpy as np
     import torch
@@ -195,14 +253,23 @@ def run(args):
     torch.cuda.synchronize()
     log(f"caches ready: {2 * layers * kc[0].numel() * 2 / 1e9:.2f} GB")
 
-    # per-step device inputs, refreshed from pinned host buffers (one buffer per step, so no
-    # host write can race an async copy still in flight)
-    tables_d = torch.empty((B, max_blocks), dtype=torch.int32, device=dev)
-    lens_d = torch.empty((B,), dtype=torch.int32, device=dev)
-    slot_d = torch.empty((B,), dtype=torch.int64, device=dev)
-    pin_tab = [torch.empty((B, max_blocks), dtype=torch.int32).pin_memory() for _ in range(grow)]
-    pin_len = [torch.empty((B,), dtype=torch.int32).pin_memory() for _ in range(grow)]
-    pin_slot = [torch.empty((B,), dtype=torch.int64).pin_memory() for _ in range(grow)]
+    # per-step device inputs: the step's table rows, lengths and new-token slots packed into one
+    # pinned host buffer per step (no host write can race a copy still in flight) and moved by
+    # one pa_upload kernel on the launch stream (no copy engine, no cross-queue wait)
+    up16 = lambda x: (x + 15) // 16 * 16
+    tab_bytes = B * max_blocks * 4
+    len_off = up16(tab_bytes)
+    slot_off = up16(len_off + 4 * B)
+    pack = up16(slot_off + 8 * B)
+    meta_d = torch.zeros(pack, dtype=torch.uint8, device=dev)
+    tables_d = meta_d[:tab_bytes].view(torch.int32).view(B, max_blocks)
+    lens_d = meta_d[len_off:len_off + 4 * B].view(torch.int32)
+    slot_d = meta_d[slot_off:slot_off + 8 * B].view(torch.int64)
+    staging = torch.zeros((grow, pack), dtype=torch.uint8).pin_memory()
+    stage_np = staging.numpy()
+    stage_tab = [stage_np[i, :tab_bytes].view(np.int32).reshape(B, max_blocks) for i in range(grow)]
+    stage_len = [stage_np[i, len_off:len_off + 4 * B].view(np.int32) for i in range(grow)]
+    stage_slot = [stage_np[i, slot_off:slot_off + 8 * B].view(np.int64) for i in range(grow)]
     nbytes = pk.pa_decode_workspace_bytes(B, Hq, Hkv, d, max_seq, args.partition_tokens, bs)
     part_used = pk.pa_decode_partition_tokens(B, Hkv, max_seq, args.partition_tokens, bs)
     log(f"split-K partitions of {part_used} tokens (requested {args.partition_tokens}; 0 = automatic)")
@@ -227,24 +294,38 @@ def run(args):
         for l in range(layers):
             dec[l]()
 
+    # per step: host timestamps [start, allocator done, tables and slots staged, upload enqueued,
+    # writes enqueued, decodes enqueued] and, when timing, HIP events on the launch stream
+    # [before the upload, after it, after the writes, after the decodes]
+    host_marks = []
+
     def step(i, events=None, launch=(write_all, decode_all)):
+        h0 = time.perf_counter()
         s, cow = alloc.batch_append(seq_ids, ones)
-        alloc.block_tables(seq_ids, max_blocks, pin_tab[i].numpy(), pin_len[i].numpy())
-        pin_slot[i].numpy()[:] = s
-        tables_d.copy_(pin_tab[i], non_blocking=True)
-        lens_d.copy_(pin_len[i], non_blocking=True)
-        slot_d.copy_(pin_slot[i], non_blocking=True)
+        h1 = time.perf_counter()
+        alloc.block_tables(seq_ids, max_blocks, stage_tab[i], stage_len[i])
+        stage_slot[i][:] = s
+        h2 = time.perf_counter()
+        if events is not None:
+            events[0].record()
+        pk.pa_upload(meta_d, staging[i])
         if cow:
             pairs = torch.tensor(cow, dtype=torch.int64).to(dev, non_blocking=False)
             for l in range(layers):
                 pk.pa_copy_blocks(kc[l], vc[l], pairs)
-        launch[0]()
-        if events is not None:
-            events[0].record()
-        launch[1]()
         if events is not None:
             events[1].record()
-        return pin_len[i].numpy().copy()
+        h3 = time.perf_counter()
+        launch[0]()
+        if events is not None:
+            events[2].record()
+        h4 = time.perf_counter()
+        launch[1]()
+        if events is not None:
+            events[3].record()
+        h5 = time.perf_counter()
+        host_marks.append((h0, h1, h2, h3, h4, h5))
+        return stage_len[i].copy()
 
     for i in range(warm):
         step(i)
@@ -252,11 +333,9 @@ def run(args):
     launch = (write_all, decode_all)
     if args.graph:
         # the 32 writes and the 32 decodes of a step as two HIP graphs, replayed every step on
-        # the same buffers (the step's tables, lengths and slots are copied into them first):
+        # the same buffers (the step's tables, lengths and slots are uploaded into them first):
         # one launch per graph instead of 64 host calls.  The library's launches on the
         # capture stream are what the graphs hold; nothing in them allocates or clears memory.
-        # (Measured: each decode kernel takes longer inside the graph than launched on its own,
-        # 52 against 45 us, so host launches are the default.)
         cap = torch.cuda.Stream()
         dec_c, wr_c = prepared(cap)
         g_write, g_decode = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
@@ -270,16 +349,19 @@ def run(args):
         launch = (g_write.replay, g_decode.replay)
     log(f"warmup done ({warm} steps); timing {steps} steps ({'HIP graphs' if args.graph else 'host launches'})")
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(steps)]
     lens_per_step = []
+    host_marks.clear()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        lens_per_step.append(step(warm + i, evs[i], launch))
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with gc_held():
+        t0 = time.perf_counter()
+        for i in range(steps):
+            lens_per_step.append(step(warm + i, evs[i], launch))
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     wall = t1 - t0
     log(f"timed {steps} steps in {wall * 1e3:.2f} ms")
+    report_phases(host_marks, evs, t0, t1, layers)
     if args.graph:
         # the graphs' last outputs against eager launches on the same inputs: bit for bit
         # (decode is deterministic; the write of the same rows again changes nothing)
@@ -293,7 +375,7 @@ def run(args):
         log("graph outputs of the last step equal eager launches (layers 0 and 31)")
 
     # HIP events on the launch stream around each step's 32 back-to-back decode launches
-    dec_ms = [e0.elapsed_time(e1) / layers for (e0, e1) in evs for _ in range(layers)]
+    dec_ms = [e[2].elapsed_time(e[3]) / layers for e in evs for _ in range(layers)]
     dec_bytes = [decode_bytes(L, Hq, Hkv, d, bs, 2, 2) for L in lens_per_step for _ in range(layers)]
     step_bytes = sum(dec_bytes) + steps * layers * kv_write_bytes(B, Hkv, d, 2, 2)
     value = step_bytes / wall / 1e9
@@ -416,14 +498,15 @@ def run_workload(name, args):
             dec()
         torch.cuda.synchronize()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-        t0 = time.perf_counter()
-        for e0, e1 in evs:
-            wr()
-            e0.record()
-            dec()
-            e1.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+        with gc_held():
+            t0 = time.perf_counter()
+            for e0, e1 in evs:
+                wr()
+                e0.record()
+                dec()
+                e1.record()
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
         single_us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
         # the kernel's own time: events around back-to-back launches on the same state (as the
         # headline times its 32 layers); events around one launch also hold its dispatch

@@ -4,8 +4,8 @@
  * The method (web pages, cited by title and section):
  *  - "KV Cache Optimization and PagedAttention" (cracklab.in): each token's K and V are
  *    stored once and reused by every later token; the cache is split into small
- *    fixed-size blocks held in whatever physical blocks are free, with a per-request block
- *    table mapping logical to physical blocks like an OS page table; requests with a common
+ *    fixed-size blocks held in any free physical blocks, with a per-request block
+ *    table mapping logical to physical blocks as an operating system's page table maps pages; requests with a common
  *    prefix can point at the same physical blocks (copy-on-write).
  *  - "PagedAttention: Optimizing KV Cache Utilization in Large Language Models"
  *    (fromzero2ai.dev): "The Mechanics of PagedAttention" (logical blocks, physical
@@ -136,12 +136,16 @@ int pa_kv_write(const void* k, const void* v, const int64_t* slot_mapping, int64
  *                slow for long contexts).  It holds the partitions' partial results and merge
  *                ticket counters: the last work-group of each group of 16 partitions of a
  *                request and KV head merges that group, and with more than one group the last
- *                group-merger merges the groups, all in the same launch.  Zero the workspace
- *                (pa_decode_workspace_init) before its first use and whenever it is reused
- *                with different (num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
- *                partition_tokens, block_size); consecutive calls with the same sizes leave
- *                the counters at zero and need no re-zeroing.  Calls that share a workspace
- *                must not run concurrently (order them on one stream).
+ *                group-merger merges the groups, all in the same launch.  The ticket counters
+ *                sit at the start of the workspace, in a region whose place and size depend
+ *                only on (num_seqs, num_q_heads, max_seq_len), and every call leaves them at
+ *                zero.  Zero the workspace (pa_decode_workspace_init) before its first use and
+ *                whenever it is reused with a different (num_seqs, num_q_heads, max_seq_len);
+ *                calls that differ only in num_kv_heads, head_dim, block_size,
+ *                partition_tokens, cache_dtype or the device's compute units (all of which
+ *                change the partition count and the partial rows' layout, never the ticket
+ *                region) need no re-zeroing.  Calls that share a workspace must not run
+ *                concurrently (order them on one stream).
  *
  * Device-side faults are turned into loud results instead of out-of-bounds accesses: a
  * request whose L exceeds max_seq_len or max_blocks_per_seq * block_size, or whose table
@@ -174,7 +178,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  *
  * Attention of several new tokens per request through the block table, causal: the step
  * before decode, where a prompt's (or a chunk of it) keys and values are computed once and
- * stored ("KV Cache Management", "Why Does This Exist?") and every token attends to every
+ * stored ("KV Cache Management", "Why Does This Exist?") and a token's attention covers every
  * token before it ("KV Cache Optimization and PagedAttention", first paragraph).  The new
  * tokens' K/V are written first (pa_kv_write), so for request b with L = seq_lens[b] cached
  * tokens and n = query_start[b+1] - query_start[b] new ones (its last n tokens), new token i
@@ -224,12 +228,30 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst, int32_t
                    int64_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
                    int32_t block_size, int32_t cache_dtype, void* stream);
 
+/* ---------------------------------------------------------------- block-table upload
+ *
+ * The host -> device leg of the block-table export: the tables live in the host allocator
+ * ("KV Cache Optimization and PagedAttention", prose on paging: each request's table maps its
+ * logical blocks to physical ones), and every decode step hands the changed rows, lengths and
+ * new tokens' slots to the device before the step's writes and decodes.
+ *     dst[0 .. bytes) = src[0 .. bytes)
+ * by one kernel on `stream`, so the copy is ordered with the stream's kernels on one queue, with
+ * no copy engine and no cross-queue wait.  The kernel reads src with system-scope loads, which
+ * bypass the device caches: it sees what the host wrote to pinned memory before the call.
+ *  dst, src  16-byte aligned; each range must lie inside one HIP allocation, device memory or
+ *            pinned host memory allocated by HIP (checked before the launch; pageable host
+ *            memory gives PA_ERR_INVALID).  The ranges must not overlap.
+ *  bytes     a multiple of 16, below 2^31.
+ * The caller keeps src unchanged until the stream has passed the call (e.g. one pinned buffer
+ * per step in flight). */
+int pa_upload(void* dst, const void* src, int64_t bytes, void* stream);
+
 /* ---------------------------------------------------------------- host block allocator
  *
  * CPU-only bookkeeping of the block pool; never touches the device.  One handle is used
  * by one thread at a time.  Rules:
  *  - a free FIFO queue (initial order given, identity if NULL); grants pop the head,
- *    releases push to the tail ("whatever blocks are free");
+ *    releases push to the tail (the pages let any free block be granted; FIFO is this library's choice);
  *  - blocks are granted on demand: appending token n of a sequence takes a new block when
  *    n % block_size == 0 ("The Solution: PagedAttention (vLLM)");
  *  - slot of token n = block * block_size + n % block_size;

@@ -26,7 +26,7 @@ EXPORTED = [
     "pa_batch_append", "pa_seq_fork", "pa_seq_free", "pa_block_tables", "pa_alloc_stats",
     "pa_alloc_dump", "pa_alloc_set_host_blocks", "pa_swap_out", "pa_swap_in", "pa_seq_is_swapped",
     "pa_alloc_dump_host", "pa_swap_blocks", "pa_seq_add_prompt", "pa_seq_append_tokens", "pa_alloc_dump_cached",
-    "pa_prefill",
+    "pa_prefill", "pa_upload",
 ]
 
 
@@ -90,6 +90,7 @@ def load(path: str = LIB_PATH):
         "pa_seq_is_swapped": (ctypes.c_int, [P, I64]),
         "pa_alloc_dump_host": (ctypes.c_int, [P, P, P, P]),
         "pa_swap_blocks": (ctypes.c_int, [P, P, P, P, P, I32, I64, I64, I32, I32, I32, I32, P]),
+        "pa_upload": (ctypes.c_int, [P, P, I64, P]),
         "pa_seq_add_prompt": (ctypes.c_int, [P, I64, P, I32, P, P]),
         "pa_seq_append_tokens": (ctypes.c_int, [P, I64, P, I32, P, P, P]),
         "pa_alloc_dump_cached": (ctypes.c_int, [P, P]),
@@ -318,6 +319,20 @@ def pa_prefill(out, q, k_cache, v_cache, block_tables, seq_lens, query_start, sc
                            block_tables.shape[1], int(max_query_len), int(max_seq_len),
                            _dtype_code(q, "q"), cdt, _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"),
                            _stream(stream))
+    _check(rc)
+
+
+def pa_upload(dst, src, *, stream=None):
+    """Copy src (a pinned host tensor or a device tensor) into the device tensor dst, byte for
+    byte, with one kernel on the stream (see pa_upload in include/pagedkv.h): a step's packed
+    block-table rows, lengths and slots, with no copy engine involved.  src must stay unchanged
+    until the stream has passed the call."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError(f"pa_upload: {nbytes} source bytes into a {dst.numel() * dst.element_size()}-byte destination")
+    if not src.is_contiguous() or not (src.is_cuda or src.is_pinned()):
+        raise ValueError("pa_upload: src must be a contiguous pinned host or device tensor")
+    rc = load().pa_upload(_dev(dst, "dst"), ctypes.c_void_p(src.data_ptr()), nbytes, _stream(stream))
     _check(rc)
 
 

@@ -31,12 +31,16 @@
 //  copy_blocks_kernel    whole-block copies: copy-on-write inside a pool, and swapping blocks
 //                        between the device pool and a pinned host pool (read and written
 //                        over the host link by the kernel itself).
+//  upload_kernel         a step's block-table rows, lengths and slots from pinned host memory
+//                        to the device, read at system scope on the stream of the kernels that
+//                        use them.
 //
 // Reduction order depends only on logical token positions (never on physical block ids),
 // so results are bit-identical under any placement of the blocks.
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -292,6 +296,19 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* dk, uint8_t* 
     }
 }
 
+// Host -> device copy of a step's block-table rows, lengths and slots (pa_upload): 16-byte
+// loads at system scope (sc0 sc1), which bypass the device caches and so see what the host
+// wrote to pinned memory before the launch; plain stores.  One kernel on the caller's stream
+// keeps the copy on the queue of the kernels that read the result.
+__global__ __launch_bounds__(256) void upload_kernel(uint8_t* __restrict__ dst, const uint8_t* src, int n16) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src), 0, n16 * 16, 0x00020000);
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n16; i += gridDim.x * 256) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, i * 16, 0, 17);   // sc0 | sc1
+        *(PA_GLOBAL u32x4v*)(dst + int64_t(i) * 16) = u32x4v{v[0], v[1], v[2], v[3]};
+    }
+}
+
 // ------------------------------------------------------------------ decode: layout
 
 template <int CDT, int D, int BS, int G>
@@ -374,7 +391,8 @@ struct DecodeArgs {
     const int32_t* seq_lens;
     const float* k_scale;
     const float* v_scale;
-    int* ws_ctr;           // merge tickets (level 1: per group of partitions; level 2), zero between calls
+    int* ws_ctr;           // merge tickets, ctr_stride per (request, KV head): one per group of partitions
+                           // (level 1), the last one for the groups (level 2); zero between calls
     float* ws_m;           // level-1 partials: one row per (request, q head, partition)
     float* ws_l;
     float* ws_acc;
@@ -390,7 +408,8 @@ struct DecodeArgs {
     int max_seq_len;
     int part_tokens;
     int max_parts;
-    int max_groups;        // ceil(max_parts / kMergeGroup)
+    int ctr_stride;        // tickets (and level-2 rows) per (request, KV head): a bound on the merge groups
+                           // of any partition size, plus one
 };
 
 // ------------------------------------------------------------------ decode: partitions and merge
@@ -572,7 +591,7 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int
     const int grp = part / kMergeGroup;
     const int first = grp * kMergeGroup, count = min(kMergeGroup, nparts - first);
     const int64_t bg = int64_t(b) * a.hkv + g;
-    int* ctr = a.ws_ctr + bg * a.max_groups + grp;
+    int* ctr = a.ws_ctr + bg * a.ctr_stride + grp;
     int seen = 0;
     if (EARLY && !single && threadIdx.x == 0) seen = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
@@ -681,13 +700,13 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int
         __syncthreads();
         return;
     }
-    const int64_t rows2 = (int64_t(b) * hq + int64_t(g) * G) * a.max_groups;
+    const int64_t rows2 = (int64_t(b) * hq + int64_t(g) * G) * a.ctr_stride;
     merge_rows<QDT, D, G, NT>(a.ws_m, a.ws_l, a.ws_acc, rows1 + first, a.max_parts, count, nullptr, a.ws_m2 + rows2 + grp,
-                              a.ws_l2 + rows2 + grp, a.ws_acc2 + (rows2 + grp) * D, a.max_groups, part - first, own);
+                              a.ws_l2 + rows2 + grp, a.ws_acc2 + (rows2 + grp) * D, a.ctr_stride, part - first, own);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
-        int* ctr2 = a.ws_ctr + int64_t(a.max_groups) * a.hkv * a.num_seqs + bg;
+        int* ctr2 = a.ws_ctr + bg * a.ctr_stride + (a.ctr_stride - 1);
         const int ticket = __hip_atomic_fetch_add(ctr2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = ticket == ngroups - 1;
         if (s_last) __hip_atomic_store(ctr2, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -696,7 +715,7 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int
     const bool merge2 = s_last;
     __syncthreads();
     if (!merge2) return;
-    merge_rows<QDT, D, G, NT>(a.ws_m2, a.ws_l2, a.ws_acc2, rows2, a.max_groups, ngroups, out, nullptr, nullptr, nullptr, 0,
+    merge_rows<QDT, D, G, NT>(a.ws_m2, a.ws_l2, a.ws_acc2, rows2, a.ctr_stride, ngroups, out, nullptr, nullptr, nullptr, 0,
                               -1, own);
     __syncthreads();
 }
@@ -1694,22 +1713,29 @@ int grid_for(int64_t work, int per_block) {
 }
 
 // Workspace (each region 256-byte aligned):
-//   [tickets: requests x q heads x groups int32 (level 1)][tickets: requests x q heads (level 2)]
+//   [tickets: requests x q heads x stride int32]   stride = ticket_groups + 1 per (request, KV
+//                                                   head): level-1 tickets, then the level-2 one
 //   [m1, l1: rows1][acc1: rows1 x d]   rows1 = requests x q heads x partitions
-//   [m2, l2: rows2][acc2: rows2 x d]   rows2 = requests x q heads x groups (only with > 1 group)
-// (q heads bound the KV heads the tickets are indexed by.)
+//   [m2, l2: rows2][acc2: rows2 x d]   rows2 = requests x q heads x stride (only with > 1 group)
+// (q heads bound the KV heads the tickets are indexed by.)  ticket_groups bounds the merge
+// groups of every partition size (partitions hold at least 64 tokens), so the tickets' place
+// and size depend only on (requests, q heads, max_seq_len).  Every launch leaves its tickets at
+// zero, so a workspace reused with another partition size, block size, cache type, head dim or
+// device finds zeros where its tickets are, never a stale partial row.
 struct WsLayout {
     int64_t ctr_off, m_off, l_off, acc_off, m2_off, l2_off, acc2_off, bytes;
-    int groups;
+    int groups, stride;
 };
 
-WsLayout ws_layout(int64_t seqs_x_heads, int64_t parts, int d) {
+WsLayout ws_layout(int64_t seqs_x_heads, int64_t max_seq_len, int64_t parts, int d) {
     auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
     WsLayout w;
     w.groups = static_cast<int>((parts + kMergeGroup - 1) / kMergeGroup);
-    const int64_t rows1 = seqs_x_heads * parts, rows2 = w.groups > 1 ? seqs_x_heads * w.groups : 0;
+    const int64_t max_parts_any = (std::max<int64_t>(max_seq_len, 1) + 63) / 64;
+    w.stride = static_cast<int>((max_parts_any + kMergeGroup - 1) / kMergeGroup) + 1;
+    const int64_t rows1 = seqs_x_heads * parts, rows2 = w.groups > 1 ? seqs_x_heads * w.stride : 0;
     w.ctr_off = 0;
-    w.m_off = up(seqs_x_heads * (w.groups + 1) * 4);
+    w.m_off = up(seqs_x_heads * w.stride * 4);
     w.l_off = w.m_off + up(rows1 * 4);
     w.acc_off = w.l_off + up(rows1 * 4);
     w.m2_off = w.acc_off + up(rows1 * int64_t(d) * 4);
@@ -1866,7 +1892,7 @@ int64_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
     const int64_t pt = resolve_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens, block_size, cache_dtype);
     const int64_t parts = max_seq_len > 0 ? (int64_t(max_seq_len) + pt - 1) / pt : 1;
     if (parts <= 1) return 0;
-    return ws_layout(int64_t(num_seqs) * num_q_heads, parts, head_dim).bytes;
+    return ws_layout(int64_t(num_seqs) * num_q_heads, max_seq_len, parts, head_dim).bytes;
 }
 
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
@@ -1928,7 +1954,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     int64_t pt = resolve_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens, block_size, cache_dtype);
     int64_t parts = max_seq_len > 0 ? (int64_t(max_seq_len) + pt - 1) / pt : 1;
     if (parts > 1) {
-        const WsLayout lay = ws_layout(int64_t(num_seqs) * num_q_heads, parts, head_dim);
+        const WsLayout lay = ws_layout(int64_t(num_seqs) * num_q_heads, max_seq_len, parts, head_dim);
         if (!workspace) {
             // no workspace: one partition per request
             pt = (max_seq_len + unit - 1) / unit * unit;
@@ -1939,7 +1965,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
         } else {
             char* base = static_cast<char*>(workspace);
             a.ws_ctr = reinterpret_cast<int*>(base + lay.ctr_off);
-            a.max_groups = lay.groups;
+            a.ctr_stride = lay.stride;
             a.ws_m2 = reinterpret_cast<float*>(base + lay.m2_off);
             a.ws_l2 = reinterpret_cast<float*>(base + lay.l2_off);
             a.ws_acc2 = reinterpret_cast<float*>(base + lay.acc2_off);
@@ -1997,6 +2023,25 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst, int32_t
                        static_cast<const uint8_t*>(k_cache), static_cast<const uint8_t*>(v_cache), src_dst,
                        num_pairs, num_blocks, num_blocks, block_bytes);
     return check_launch("pa_copy_blocks");
+}
+
+int pa_upload(void* dst, const void* src, int64_t bytes, void* stream) {
+    pagedkv::clear_error();
+    if (bytes < 0 || bytes % 16 != 0 || bytes >= (int64_t(1) << 31))
+        return fail(PA_ERR_INVALID, "pa_upload: %lld bytes (a multiple of 16 below 2^31)", (long long)bytes);
+    if (bytes == 0) return PA_OK;
+    if (!dst || !src || !aligned16(dst) || !aligned16(src))
+        return fail(PA_ERR_INVALID, "pa_upload: NULL or misaligned pointer");
+    const uintptr_t d0 = reinterpret_cast<uintptr_t>(dst), s0 = reinterpret_cast<uintptr_t>(src);
+    if (d0 < s0 + static_cast<uintptr_t>(bytes) && s0 < d0 + static_cast<uintptr_t>(bytes))
+        return fail(PA_ERR_INVALID, "pa_upload: source and destination overlap");
+    const void *dv, *sv;
+    if (int rc = device_view(dst, bytes, "pa_upload", "dst", &dv)) return rc;
+    if (int rc = device_view(src, bytes, "pa_upload", "src", &sv)) return rc;
+    const int n16 = static_cast<int>(bytes / 16);
+    hipLaunchKernelGGL(upload_kernel, dim3(grid_for(n16, 256)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<uint8_t*>(const_cast<void*>(dv)), static_cast<const uint8_t*>(sv), n16);
+    return check_launch("pa_upload");
 }
 
 int pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,

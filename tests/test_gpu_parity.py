@@ -152,6 +152,36 @@ def test_merge_paths_bit_identical(ptok):
         assert torch.equal(again.view(torch.int16), first.view(torch.int16)), "merge result depends on the path"
 
 
+def test_workspace_shared_across_cache_types():
+    """One workspace serves an fp8 call, a bf16 call and the fp8 call again with no re-zeroing
+    in between (3 requests x 8 KV heads, group 1, 4096 tokens, automatic partitions: 22 for the
+    fp8 cache, two merge groups, and 11 for bf16, one group).  The ticket counters sit in a
+    region fixed by (requests, q heads, max_seq_len), so the bf16 call's partial rows cannot
+    land where the fp8 call reads its level-2 tickets: every output matches the oracle and the
+    two fp8 calls are bit-identical."""
+    B, H, L = 3, 8, 4096
+    sides = {}
+    for fmt in ("fp8", "bf16"):
+        w = workloads.gqa_uniform(B=B, L=L, Hq=H, Hkv=H, fmt=fmt, layers=1, seed_index=44, name=f"ws_share_{fmt}")
+        vals = workloads.host_values(w)
+        sides[fmt] = (w, GpuSide(w, vals), OracleSide(w, vals))
+    n_fp8 = pk.pa_decode_workspace_bytes(B, H, H, 128, L, 0, 16, pk.PA_DTYPE_FP8_E4M3)
+    n_bf16 = pk.pa_decode_workspace_bytes(B, H, H, 128, L, 0, 16, pk.PA_DTYPE_BF16)
+    assert pk.pa_decode_partition_tokens(B, H, L, 0, 16, pk.PA_DTYPE_FP8_E4M3) * 16 < L   # > 16 partitions
+    assert pk.pa_decode_partition_tokens(B, H, L, 0, 16, pk.PA_DTYPE_BF16) * 16 >= L      # one group
+    ws = torch.zeros(max(n_fp8, n_bf16), dtype=torch.uint8, device=DEV)
+    outs = []
+    for fmt in ("fp8", "bf16", "fp8"):
+        w, g, o = sides[fmt]
+        out = torch.empty_like(g.q)
+        pk.pa_decode(out, g.q, g.kc, g.vc, g.tables, g.lens, g.scale, w.bs, max_seq_len=L, k_scale=g.ks,
+                     v_scale=g.vs, workspace=ws)
+        torch.cuda.synchronize()
+        print(check_close(out_f64(out), o.decode(), w.q_fmt, f"{w.name} on a shared workspace"), flush=True)
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
+
+
 def test_long_context_scaled_auto():
     """The same layer with automatic partitions: 16 (request, KV head) pairs, so each request
     is cut into 16 equal partitions and merged in one group."""
@@ -412,7 +442,7 @@ def test_copy_blocks_bitexact():
     pairs = [(3, 10), (0, 19), (7, 2), (100, 5), (4, 4)]
     pk.pa_copy_blocks(kc, vc, torch.tensor(pairs, dtype=torch.int64, device=DEV))
     ok, ov = k.copy(), v.copy()
-    OA.copy_blocks(ok, ov, [p for p in pairs if p[0] < N and p[1] < N])
+    OA.copy_blocks(ok, ov, pairs)            # the pair naming block 100 is skipped on both sides
     assert np.array_equal(to_host(kc, "bf16"), ok) and np.array_equal(to_host(vc, "bf16"), ov)
 
 
