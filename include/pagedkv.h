@@ -174,6 +174,33 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               const float* k_scale, const float* v_scale,
               void* workspace, int64_t workspace_bytes, int32_t partition_tokens, void* stream);
 
+/* ---------------------------------------------------------------- decode without allocation
+ *
+ * For callers that cannot allocate device memory or hand the library a workspace: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * computation, arguments and results as pa_decode (bit for bit: the same kernels and
+ * partitions) without (workspace, workspace_bytes): the split-K partials and merge tickets live
+ * in a static device array of PA_NOALLOC_SCRATCH_BYTES inside the library, which every device
+ * the library runs on holds until the process ends.
+ *  - Sizes whose pa_decode_workspace_bytes(...) exceeds PA_NOALLOC_SCRATCH_BYTES return
+ *    PA_ERR_INVALID with nothing enqueued (128 MiB holds, for example, 256 requests x 32 q heads
+ *    up to 8192 tokens in 512-token partitions, or 2 x 64 heads at 131072 tokens).
+ *  - Nothing is allocated or freed: no hipMalloc, hipFree or allocating library routine.  The
+ *    first call on a device, with that device current, looks the array's address up once.
+ *  - Every call on one device shares that device's array, which keeps the last call's
+ *    contents.  When a call's ticket counters reach past the bytes earlier calls left at zero,
+ *    the call first clears them with a store kernel on `stream` (no memset node).
+ *  - Calls that overlap on one device (on different streams, or from several threads without
+ *    ordering on one stream) race on the array and give undefined results. */
+#define PA_NOALLOC_SCRATCH_BYTES (128 * 1024 * 1024)
+
+int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                      int32_t block_size, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq,
+                      int32_t max_seq_len, int32_t q_dtype, int32_t cache_dtype,
+                      const float* k_scale, const float* v_scale, int32_t partition_tokens, void* stream);
+
 /* ---------------------------------------------------------------- prefill attention
  *
  * Attention of several new tokens per request through the block table, causal: the step

@@ -26,7 +26,7 @@ EXPORTED = [
     "pa_batch_append", "pa_seq_fork", "pa_seq_free", "pa_block_tables", "pa_alloc_stats",
     "pa_alloc_dump", "pa_alloc_set_host_blocks", "pa_swap_out", "pa_swap_in", "pa_seq_is_swapped",
     "pa_alloc_dump_host", "pa_swap_blocks", "pa_seq_add_prompt", "pa_seq_append_tokens", "pa_alloc_dump_cached",
-    "pa_prefill", "pa_upload",
+    "pa_prefill", "pa_upload", "pa_decode_noalloc",
 ]
 
 
@@ -91,6 +91,8 @@ def load(path: str = LIB_PATH):
         "pa_alloc_dump_host": (ctypes.c_int, [P, P, P, P]),
         "pa_swap_blocks": (ctypes.c_int, [P, P, P, P, P, I32, I64, I64, I32, I32, I32, I32, P]),
         "pa_upload": (ctypes.c_int, [P, P, I64, P]),
+        "pa_decode_noalloc": (ctypes.c_int, [P, P, P, P, P, P, F32, I32, I32, I32, I32, I32, I64, I32, I32, I32,
+                                             I32, P, P, I32, P]),
         "pa_seq_add_prompt": (ctypes.c_int, [P, I64, P, I32, P, P]),
         "pa_seq_append_tokens": (ctypes.c_int, [P, I64, P, I32, P, P, P]),
         "pa_alloc_dump_cached": (ctypes.c_int, [P, P]),
@@ -293,6 +295,26 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, block_siz
                           _dtype_code(q, "q"), cdt,
                           _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), ws_ptr, ws_bytes,
                           int(partition_tokens), _stream(stream))
+    _check(rc)
+
+
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, seq_lens, scale, block_size, *, max_seq_len=None,
+                      k_scale=None, v_scale=None, partition_tokens=0, stream=None):
+    """pa_decode with the library's fixed device scratch instead of a workspace, for callers that
+    cannot allocate (see pa_decode_noalloc in include/pagedkv.h): same arguments and results
+    as pa_decode without `workspace`; calls that overlap on one device race on the scratch."""
+    B, Hq, d = q.shape
+    N, Hkv, bs, dc, cdt = _cache_geom(k_cache, "k_cache")
+    if out.shape != q.shape or v_cache.shape != k_cache.shape or dc != d or bs != block_size:
+        raise ValueError("shape mismatch")
+    max_blocks = block_tables.shape[1]
+    if max_seq_len is None:
+        max_seq_len = max_blocks * block_size
+    rc = load().pa_decode_noalloc(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                  _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), float(scale),
+                                  block_size, B, Hq, Hkv, d, N, max_blocks, int(max_seq_len), _dtype_code(q, "q"), cdt,
+                                  _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), int(partition_tokens),
+                                  _stream(stream))
     _check(rc)
 
 

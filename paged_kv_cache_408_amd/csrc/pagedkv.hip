@@ -43,6 +43,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <cstdint>
 #include <type_traits>
 
@@ -1656,6 +1657,14 @@ __global__ __launch_bounds__(256) void zero_kernel(uint32_t* __restrict__ p, int
         p[i] = 0u;
 }
 
+// ------------------------------------------------------------------ fixed scratch (pa_decode_noalloc)
+//
+// Split-K partials and merge tickets of pa_decode_noalloc: a file-scope device array, which
+// every device the library runs on holds until the process ends.  In host code this name
+// denotes a host-side stand-in, not device memory: host code uses only the device address that
+// hipGetSymbolAddress returns for the current device (kept per device below).
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
 // ------------------------------------------------------------------ host helpers
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -1827,6 +1836,16 @@ bool supported_pair(int qdt, int cdt) {
            (qdt == PA_DTYPE_BF16 && cdt == PA_DTYPE_FP8_E4M3) || (qdt == PA_DTYPE_BF16 && cdt == PA_DTYPE_MXFP4);
 }
 
+// Per device: the fixed scratch's device address and how many of its leading bytes are zero once
+// the device has passed the calls enqueued so far (the next call's tickets must start at zero).
+struct ScratchDevice {
+    void* ptr = nullptr;
+    int64_t zero_bytes = 0;
+};
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+ScratchDevice g_scratch[kMaxScratchDevices];
+
 }  // namespace
 
 // ====================================================================== C ABI
@@ -1989,6 +2008,60 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     if (cache_dtype == PA_DTYPE_MXFP4)
         return dispatch_d<PA_DTYPE_MXFP4, PA_DTYPE_BF16>(head_dim, block_size, G, a, num_seqs, st);
     return dispatch_d<PA_DTYPE_FP8_E4M3, PA_DTYPE_BF16>(head_dim, block_size, G, a, num_seqs, st);
+}
+
+int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                      int32_t block_size, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq,
+                      int32_t max_seq_len, int32_t q_dtype, int32_t cache_dtype,
+                      const float* k_scale, const float* v_scale, int32_t partition_tokens, void* stream) {
+    pagedkv::clear_error();
+    const int64_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                                   partition_tokens, block_size, cache_dtype);
+    if (need <= 0 || num_seqs == 0)   // a single partition per request (no scratch), or sizes pa_decode rejects
+        return pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, block_size, num_seqs, num_q_heads,
+                         num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_seq_len, q_dtype, cache_dtype,
+                         k_scale, v_scale, nullptr, 0, partition_tokens, stream);
+    if (need > int64_t(PA_NOALLOC_SCRATCH_BYTES))
+        return fail(PA_ERR_INVALID,
+                    "pa_decode_noalloc: these sizes need %lld bytes of split-K scratch, more than the fixed %lld "
+                    "(call pa_decode with a workspace)", (long long)need, (long long)PA_NOALLOC_SCRATCH_BYTES);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) {
+        (void)hipGetLastError();
+        return fail(PA_ERR_DEVICE, "pa_decode_noalloc: no current device below %d", kMaxScratchDevices);
+    }
+    const int64_t pt = resolve_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens, block_size, cache_dtype);
+    const int64_t parts = (int64_t(max_seq_len) + pt - 1) / pt;
+    const int64_t tickets = ws_layout(int64_t(num_seqs) * num_q_heads, max_seq_len, parts, head_dim).m_off;
+
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ScratchDevice& sd = g_scratch[dev];
+    if (!sd.ptr) {   // first call on this device, with it current: look the array's address up once
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(PA_ERR_DEVICE, "pa_decode_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+        }
+        sd.ptr = p;
+        sd.zero_bytes = 0;   // the contents at load are not relied on
+    }
+    char* base = static_cast<char*>(sd.ptr);
+    if (sd.zero_bytes < tickets) {   // the tickets must start at zero: clear what earlier calls left there
+        const int64_t words = (tickets - sd.zero_bytes) / 4;
+        hipLaunchKernelGGL(zero_kernel, dim3(grid_for(words, 256)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                           reinterpret_cast<uint32_t*>(base + sd.zero_bytes), words);
+        if (int rc = check_launch("pa_decode_noalloc")) return rc;
+        sd.zero_bytes = tickets;
+    }
+    const int rc = pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, block_size, num_seqs,
+                             num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_seq_len, q_dtype,
+                             cache_dtype, k_scale, v_scale, base, int64_t(PA_NOALLOC_SCRATCH_BYTES), partition_tokens,
+                             stream);
+    if (rc == PA_OK) sd.zero_bytes = tickets;   // partial rows follow the tickets, which the launch leaves at zero
+    return rc;
 }
 
 int pa_decode_workspace_init(void* workspace, int64_t workspace_bytes, void* stream) {
