@@ -125,10 +125,12 @@ def test_ragged_prefix_full():
 
 @pytest.mark.parametrize("bs,fmt", workloads.sweep_settings())
 def test_block_dtype_sweep(bs, fmt):
-    """Block size x KV dtype sweep on a ragged batch with a shared prefix (64 requests, 16 of
-    them sharing a 1024-token prefix)."""
-    run_pair(workloads.ragged_prefix(bs=bs, fmt=fmt, B=64, n_shared=16, seed_index=30 + bs,
-                                     name=f"sweep_bs{bs}_{fmt}"))
+    """Block size x KV dtype sweep on the ragged batch itself (256 requests, 64 of them sharing a
+    1024-token prefix: the batch bench.py times for each setting): slots, tables, the whole K
+    and V caches bit for bit, and every request's output against the oracle."""
+    g, *_ = run_pair(workloads.ragged_prefix(bs=bs, fmt=fmt))
+    ref, _ = g.alloc.dump()
+    assert int((ref == 64).sum()) == 1024 // bs          # the shared prefix: 64 holders per block
 
 
 def test_long_context_scaled():
@@ -150,6 +152,46 @@ def test_merge_paths_bit_identical(ptok):
     for _ in range(20):
         again = g.decode()
         assert torch.equal(again.view(torch.int16), first.view(torch.int16)), "merge result depends on the path"
+
+
+def test_merge_paths_both_taken_and_identical():
+    """Both merge paths run, and give the same bits.  The early path's merger writes no partial
+    row, while on the ticket path every member writes its row before taking a ticket.  So with
+    the workspace's level-1 rows filled with a NaN sentinel before each launch (tickets zero),
+    the rows still holding it afterwards count the early merges.  Over 30 launches of a bf16
+    batch with two partitions per (request, KV head) (the automatic size for 16 requests x 8 KV
+    heads; 128 merges per launch) both paths must occur, and every output must equal the first
+    bit for bit and match the oracle."""
+    w = workloads.gqa_uniform(B=16, L=1500, layers=1, seed_index=48, name="merge_path_count")
+    vals = workloads.host_values(w)
+    g, o = GpuSide(w, vals), OracleSide(w, vals)
+    maxL = int(g.lens_np.max())
+    ptok = pk.pa_decode_partition_tokens(w.B, w.Hkv, maxL, 0, w.bs)
+    parts = -(-maxL // ptok)
+    assert parts == 2
+    nbytes = pk.pa_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, maxL, 0, w.bs)
+    stride = -(-(-(-maxL // 64)) // 16) + 1                 # tickets per (request, KV head), as laid out
+    m_off = (w.B * w.Hq * stride * 4 + 255) // 256 * 256    # level-1 row maxima follow the tickets
+    rows = w.B * w.Hq * parts
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    first, early_counts = None, []
+    for _ in range(30):
+        ws[:m_off].zero_()
+        ws[m_off:].fill_(0xFF)                               # NaN sentinel in every partial row
+        out = torch.empty_like(g.q)
+        pk.pa_decode(out, g.q, g.kc, g.vc, g.tables, g.lens, g.scale, w.bs, max_seq_len=maxL, workspace=ws)
+        torch.cuda.synchronize()
+        m1 = ws[m_off:m_off + 4 * rows].view(torch.int32).view(w.B, w.Hkv, w.Hq // w.Hkv, parts).cpu().numpy()
+        unwritten = (m1 == -1).all(axis=2)                   # all heads of a (request, KV head, partition)
+        early_counts.append(int(unwritten.sum()))
+        assert int(unwritten.sum(axis=2).max()) <= 1         # at most the merger of each pair skips its row
+        if first is None:
+            first = out.clone()
+            print(check_close(out_f64(out), o.decode(), w.q_fmt, w.name), flush=True)
+        assert torch.equal(out.view(torch.int16), first.view(torch.int16)), "merge result depends on the path"
+    merges = w.B * w.Hkv * 30
+    print(f"early merges {sum(early_counts)} of {merges}; per launch {early_counts}", flush=True)
+    assert 0 < sum(early_counts) < merges, "both merge paths must occur"
 
 
 def test_workspace_shared_across_cache_types():
