@@ -273,6 +273,54 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst, int32_t
  * per step in flight). */
 int pa_upload(void* dst, const void* src, int64_t bytes, void* stream);
 
+/* ---------------------------------------------------------------- tensor-view entry points
+ *
+ * pa_kv_write and pa_decode over non-owning tensor views, for callers that hold shapes and
+ * strides rather than loose sizes.  Each view is checked on the host -- dtype, rank, shape
+ * agreement between the arguments, C-contiguity -- before the plain entry point is called with
+ * the sizes read from the views; a mismatch returns PA_ERR_INVALID (or PA_ERR_UNSUPPORTED)
+ * naming the argument, with nothing enqueued.  Same computation and results as the plain calls.
+ *
+ *  pa_tensor  data: device pointer; dtype: PA_DTYPE_*; ndim, shape[0 .. ndim), stride[0 .. ndim)
+ *             in elements (C-contiguous: stride[ndim-1] = 1, stride[i] = stride[i+1] * shape[i+1]).
+ *             An MXFP4 cache is given as dtype PA_DTYPE_MXFP4 with the logical shape
+ *             [num_blocks][num_kv_heads][block_size][head_dim] and all strides 0 (its tiles are
+ *             packed as the cache layout above states).
+ *  pa_opts    nullable; zero fields take the defaults: stream NULL, no workspace (one partition
+ *             per request), partition_tokens 0 (automatic), max_seq_len 0 (the table's capacity,
+ *             max_blocks_per_seq * block_size), k_scale / v_scale NULL (required for fp8 caches).
+ */
+#define PA_DTYPE_I32 4          /* int32 index tensor (block tables, lengths)                */
+#define PA_DTYPE_I64 5          /* int64 index tensor (slot mapping)                         */
+
+typedef struct {
+    void* data;
+    int32_t dtype;
+    int32_t ndim;
+    int64_t shape[4];
+    int64_t stride[4];
+} pa_tensor;
+
+typedef struct {
+    void* stream;
+    void* workspace;
+    int64_t workspace_bytes;
+    int32_t partition_tokens;
+    int32_t max_seq_len;
+    const float* k_scale;
+    const float* v_scale;
+} pa_opts;
+
+/* k, v: [num_tokens][num_kv_heads][head_dim]; slot_mapping: int64 [num_tokens]; caches as above. */
+int pa_kv_write_t(const pa_tensor* k, const pa_tensor* v, const pa_tensor* slot_mapping, pa_tensor* k_cache,
+                  pa_tensor* v_cache, const pa_opts* opts);
+
+/* out, q: [num_seqs][num_q_heads][head_dim]; caches [num_blocks][num_kv_heads][block_size][head_dim];
+ * block_tables: int32 [num_seqs][max_blocks_per_seq]; seq_lens: int32 [num_seqs]. */
+int pa_decode_t(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                const pa_tensor* block_tables, const pa_tensor* seq_lens, float scale, int32_t block_size,
+                const pa_opts* opts);
+
 /* ---------------------------------------------------------------- host block allocator
  *
  * CPU-only bookkeeping of the block pool; never touches the device.  One handle is used

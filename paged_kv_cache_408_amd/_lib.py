@@ -26,7 +26,7 @@ EXPORTED = [
     "pa_batch_append", "pa_seq_fork", "pa_seq_free", "pa_block_tables", "pa_alloc_stats",
     "pa_alloc_dump", "pa_alloc_set_host_blocks", "pa_swap_out", "pa_swap_in", "pa_seq_is_swapped",
     "pa_alloc_dump_host", "pa_swap_blocks", "pa_seq_add_prompt", "pa_seq_append_tokens", "pa_alloc_dump_cached",
-    "pa_prefill", "pa_upload", "pa_decode_noalloc",
+    "pa_prefill", "pa_upload", "pa_decode_noalloc", "pa_kv_write_t", "pa_decode_t",
 ]
 
 
@@ -50,6 +50,20 @@ class pa_alloc_stats_t(ctypes.Structure):
                  "host_free_blocks", "host_used_blocks", "swapped_seqs", "cached_blocks", "cache_hit_blocks",
                  "cache_evictions")]
 
+
+class pa_tensor(ctypes.Structure):
+    """Non-owning tensor view of include/pagedkv.h (shape and strides in elements)."""
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class pa_opts(ctypes.Structure):
+    _fields_ = [("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
+                ("partition_tokens", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+
+
+PA_DTYPE_I32, PA_DTYPE_I64 = 4, 5
 
 _lib = None
 
@@ -91,6 +105,8 @@ def load(path: str = LIB_PATH):
         "pa_alloc_dump_host": (ctypes.c_int, [P, P, P, P]),
         "pa_swap_blocks": (ctypes.c_int, [P, P, P, P, P, I32, I64, I64, I32, I32, I32, I32, P]),
         "pa_upload": (ctypes.c_int, [P, P, I64, P]),
+        "pa_kv_write_t": (ctypes.c_int, [ctypes.POINTER(pa_tensor)] * 5 + [ctypes.POINTER(pa_opts)]),
+        "pa_decode_t": (ctypes.c_int, [ctypes.POINTER(pa_tensor)] * 6 + [F32, I32, ctypes.POINTER(pa_opts)]),
         "pa_decode_noalloc": (ctypes.c_int, [P, P, P, P, P, P, F32, I32, I32, I32, I32, I32, I64, I32, I32, I32,
                                              I32, P, P, I32, P]),
         "pa_seq_add_prompt": (ctypes.c_int, [P, I64, P, I32, P, P]),
@@ -356,6 +372,33 @@ def pa_upload(dst, src, *, stream=None):
         raise ValueError("pa_upload: src must be a contiguous pinned host or device tensor")
     rc = load().pa_upload(_dev(dst, "dst"), ctypes.c_void_p(src.data_ptr()), nbytes, _stream(stream))
     _check(rc)
+
+
+def tensor_view(t, dtype=None):
+    """A pa_tensor view of a device tensor (dtype code from the tensor unless given; an MXFP4 cache
+    is viewed with its logical head_dim and zero strides)."""
+    torch = _torch()
+    v = pa_tensor()
+    v.data = t.data_ptr()
+    if dtype is None:
+        if t.dtype == torch.int32:
+            dtype = PA_DTYPE_I32
+        elif t.dtype == torch.int64:
+            dtype = PA_DTYPE_I64
+        elif t.dim() == 4:
+            dtype = _cache_geom(t, "cache")[4]
+        else:
+            dtype = _dtype_code(t, "tensor")
+    v.dtype, v.ndim = dtype, t.dim()
+    shape = list(t.shape)
+    if dtype == PA_DTYPE_MXFP4:
+        shape[3] = _cache_geom(t, "cache")[3]
+        strides = [0] * t.dim()
+    else:
+        strides = list(t.stride())
+    for i in range(t.dim()):
+        v.shape[i], v.stride[i] = shape[i], strides[i]
+    return v
 
 
 def pa_copy_blocks(k_cache, v_cache, src_dst, *, stream=None):

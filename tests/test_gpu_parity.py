@@ -558,3 +558,37 @@ def test_workspace_reuse_across_shapes():
         for i in order:
             g, _ = sides[i]
             check_close(out_f64(g.decode()), refs[i], "bf16", g.w.name)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_tensor_view_entry_points(fmt):
+    """pa_kv_write_t and pa_decode_t (tensor views, checked on the host) write the same cache
+    bytes and decode the same bits as the plain calls, through the C ABI."""
+    import ctypes
+    lib = pk.load()
+    r = ctypes.byref
+    w = workloads.ragged_prefix(bs=16, fmt=fmt, B=24, n_shared=4, seed_index=49, name=f"views_{fmt}")
+    vals = workloads.host_values(w)
+    g = GpuSide(w, vals)
+    # the step token's rows again, through the view entry point, into copies of the caches
+    kc2, vc2 = g.kc.clone(), g.vc.clone()
+    kn, vn = to_dev(vals["k_new"], w.in_fmt), to_dev(vals["v_new"], w.in_fmt)
+    slots = torch.from_numpy(np.asarray(g.step_slots, dtype=np.int64)).to(DEV)
+    opts = pk._lib.pa_opts()
+    opts.stream = torch.cuda.current_stream().cuda_stream
+    if g.ks is not None:
+        opts.k_scale, opts.v_scale = g.ks.data_ptr(), g.vs.data_ptr()
+    tv = pk._lib.tensor_view
+    assert lib.pa_kv_write_t(r(tv(kn)), r(tv(vn)), r(tv(slots)), r(tv(kc2)), r(tv(vc2)), r(opts)) == 0, \
+        lib.pa_last_error().decode()
+    torch.cuda.synchronize()
+    assert torch.equal(kc2.view(torch.uint8), g.kc.view(torch.uint8)) and torch.equal(vc2.view(torch.uint8), g.vc.view(torch.uint8))
+    maxL = int(g.lens_np.max())
+    n = pk.pa_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, maxL, 0, w.bs, g.kc)
+    ws = torch.zeros(max(n, 256), dtype=torch.uint8, device=DEV)
+    opts.workspace, opts.workspace_bytes, opts.max_seq_len = ws.data_ptr(), ws.numel(), maxL
+    out_t = torch.empty_like(g.q)
+    assert lib.pa_decode_t(r(tv(out_t)), r(tv(g.q)), r(tv(g.kc)), r(tv(g.vc)), r(tv(g.tables)), r(tv(g.lens)),
+                           g.scale, w.bs, r(opts)) == 0, lib.pa_last_error().decode()
+    torch.cuda.synchronize()
+    assert torch.equal(out_t.view(torch.int16), g.decode().view(torch.int16))

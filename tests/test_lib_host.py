@@ -45,7 +45,7 @@ def test_header_symbols_exported():
     out = subprocess.run(["nm", "-D", "--defined-only", pk.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (pa_\w+)", out))
     assert set(names) <= exported
-    assert pk.load().pa_abi_version() == 5
+    assert pk.load().pa_abi_version() == 6
 
 
 def test_errors_are_reported():
@@ -451,3 +451,84 @@ def test_allocator_under_asan_ubsan(tmp_path):
                             f"{s['waste_slots']} {len(o.seqs)} {s['host_free']} {s['host_used']} {s['swapped_seqs']} "
                             f"{s['cached_blocks']} {s['cache_hit_blocks']} {s['cache_evictions']}")
         assert got == want
+
+
+# --------------------------------------------------------------------------- tensor-view entry points
+
+def _view(shape, dtype, data=0x1000, strides=None):
+    v = pk._lib.pa_tensor()
+    v.data, v.dtype, v.ndim = data, dtype, len(shape)
+    if strides is None:
+        strides, acc = [], 1
+        for n in reversed(shape):
+            strides.insert(0, acc)
+            acc *= n
+    for i, (n, st) in enumerate(zip(shape, strides)):
+        v.shape[i], v.stride[i] = n, st
+    return v
+
+
+def _decode_views(B=2, Hq=8, Hkv=2, d=128, N=10, bs=16, mb=4, qdt=pk.PA_DTYPE_BF16, cdt=pk.PA_DTYPE_BF16):
+    return dict(out=_view([B, Hq, d], qdt), q=_view([B, Hq, d], qdt), kc=_view([N, Hkv, bs, d], cdt),
+                vc=_view([N, Hkv, bs, d], cdt), tab=_view([B, mb], pk._lib.PA_DTYPE_I32),
+                lens=_view([B], pk._lib.PA_DTYPE_I32))
+
+
+def _decode_t(v, bs=16):
+    import ctypes
+    lib = pk.load()
+    r = ctypes.byref
+    return lib.pa_decode_t(r(v["out"]), r(v["q"]), r(v["kc"]), r(v["vc"]), r(v["tab"]), r(v["lens"]), 0.1, bs, None)
+
+
+@pytest.mark.parametrize("case,match", [
+    (lambda v: v.update(q=_view([2, 8], pk.PA_DTYPE_BF16)), "q has 2 dims"),
+    (lambda v: v.update(out=_view([2, 8, 64], pk.PA_DTYPE_BF16)), "out and q differ"),
+    (lambda v: v.update(kc=_view([10, 2, 16, 64], pk.PA_DTYPE_BF16), vc=_view([10, 2, 16, 64], pk.PA_DTYPE_BF16)),
+     "head_dim"),
+    (lambda v: v.update(vc=_view([10, 2, 16, 128], pk.PA_DTYPE_FP8_E4M3)), "k_cache and v_cache differ"),
+    (lambda v: v.update(kc=_view([10, 3, 16, 128], pk.PA_DTYPE_BF16), vc=_view([10, 3, 16, 128], pk.PA_DTYPE_BF16)),
+     "not a multiple"),
+    (lambda v: v.update(tab=_view([3, 4], pk._lib.PA_DTYPE_I32)), "table rows"),
+    (lambda v: v.update(tab=_view([2, 4], pk._lib.PA_DTYPE_I64)), "block_tables is int64"),
+    (lambda v: v.update(q=_view([2, 8, 128], pk.PA_DTYPE_BF16, strides=[1024, 1, 8]),
+                        out=_view([2, 8, 128], pk.PA_DTYPE_BF16, strides=[1024, 1, 8])), "not C-contiguous"),
+    (lambda v: v.update(kc=_view([10, 2, 16, 128], pk.PA_DTYPE_MXFP4), vc=_view([10, 2, 16, 128], pk.PA_DTYPE_MXFP4)),
+     "strides as 0"),
+])
+def test_decode_views_checked_on_the_host(case, match):
+    """pa_decode_t rejects views that disagree, naming the argument, before any device call."""
+    v = _decode_views()
+    case(v)
+    assert _decode_t(v) == pk._lib.PA_ERR_INVALID
+    assert match in pk.load().pa_last_error().decode()
+
+
+def test_decode_views_pass_through():
+    """Consistent views reach pa_decode: a block size that disagrees with the cache is refused,
+    and an empty batch (zero requests) is a no-op that succeeds without touching the device."""
+    v = _decode_views()
+    assert _decode_t(v, bs=32) == pk._lib.PA_ERR_INVALID
+    assert "block_size 32" in pk.load().pa_last_error().decode()
+    v0 = _decode_views(B=0)
+    assert _decode_t(v0) == 0
+
+
+def test_kv_write_views_checked_on_the_host():
+    import ctypes
+    lib = pk.load()
+    r = ctypes.byref
+    k, vv = _view([5, 2, 128], pk.PA_DTYPE_BF16), _view([5, 2, 128], pk.PA_DTYPE_BF16)
+    kc, vc = _view([10, 2, 16, 128], pk.PA_DTYPE_BF16), _view([10, 2, 16, 128], pk.PA_DTYPE_BF16)
+    slots = _view([4], pk._lib.PA_DTYPE_I64)
+    assert lib.pa_kv_write_t(r(k), r(vv), r(slots), r(kc), r(vc), None) == pk._lib.PA_ERR_INVALID
+    assert "4 entries for 5 tokens" in lib.pa_last_error().decode()
+    slots = _view([5], pk._lib.PA_DTYPE_I32)
+    assert lib.pa_kv_write_t(r(k), r(vv), r(slots), r(kc), r(vc), None) == pk._lib.PA_ERR_INVALID
+    assert "slot_mapping is int32" in lib.pa_last_error().decode()
+    slots = _view([5], pk._lib.PA_DTYPE_I64)
+    k3 = _view([5, 3, 128], pk.PA_DTYPE_BF16)
+    assert lib.pa_kv_write_t(r(k3), r(k3), r(slots), r(kc), r(vc), None) == pk._lib.PA_ERR_INVALID
+    assert "does not match" in lib.pa_last_error().decode()
+    e = _view([0, 2, 128], pk.PA_DTYPE_BF16)
+    assert lib.pa_kv_write_t(r(e), r(e), r(_view([0], pk._lib.PA_DTYPE_I64)), r(kc), r(vc), None) == 0   # no tokens
