@@ -218,6 +218,8 @@ def run(args):
     L0 = 4096                      # decode length of every request in the first timed step
     grow = steps + warm
     w = workloads.gqa_uniform(B=16, L=L0 - warm, layers=32, spare_blocks=16 * (grow // 16 + 2))
+    if args.placement == "identity":
+        w.free_order = np.arange(w.num_blocks, dtype=np.int32)
     B, Hq, Hkv, d, bs, layers = w.B, w.Hq, w.Hkv, w.d, w.bs, w.layers
     max_blocks = -(-(L0 + grow) // bs)
     max_seq = max_blocks * bs
@@ -395,7 +397,8 @@ def run(args):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1)*0.5 K/V/q drawn on the device; seeded block permutation)",
+        "data": "synthetic (seeded N(0,1)*0.5 K/V/q drawn on the device; %s)" % (
+            "seeded block permutation" if args.placement == "permuted" else "identity block placement"),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "config": {
             "workload": "llama3_8b_gqa_decode: 32 layers x batch 16, 32 q / 8 kv heads, head_dim 128, bf16, "
@@ -403,7 +406,7 @@ def run(args):
                         "split-K partitions of %d tokens" % part_used,
             "layers": layers, "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": d,
             "block_size": bs, "seq_len_start": int(lens_per_step[0][0]), "seq_len_end": int(lens_per_step[-1][0]),
-            "partition_tokens": part_used,
+            "partition_tokens": part_used, "placement": args.placement,
             "kv_cache_gb": round(2 * layers * kc[0].numel() * 2 / 1e9, 3),
             "launch": "two HIP graphs per step" if args.graph else "one host launch per kernel",
         },
@@ -448,9 +451,16 @@ def run_workload(name, args):
     elif name == "mxfp4":   # the 4-bit cache on the ragged batch and on one Llama-shaped layer
         settings = [workloads.ragged_prefix(bs=16, fmt="mxfp4"),
                     workloads.gqa_uniform(B=16, L=4096, fmt="mxfp4", layers=1, name="llama3_8b_layer_mxfp4")]
+    elif name == "fp8":     # the fp8 cache on the ragged batch and on one Llama-shaped layer
+        settings = [workloads.ragged_prefix(bs=16, fmt="fp8"),
+                    workloads.gqa_uniform(B=16, L=4096, fmt="fp8", layers=1, name="llama3_8b_layer_fp8")]
+    elif name == "llama_layer":   # one layer of the benchmark batch on its own
+        settings = [workloads.gqa_uniform(B=16, L=4096, layers=1, name="llama3_8b_layer_bf16")]
     else:  # block-size x KV-dtype sweep on the ragged batch
         settings = [workloads.ragged_prefix(bs=bs, fmt=fmt) for bs, fmt in workloads.sweep_settings()]
     for w in settings:
+        if args.placement == "identity":
+            w.free_order = np.arange(w.num_blocks, dtype=np.int32)
         alloc = pk.Allocator(w.num_blocks, w.bs, w.free_order)
         slots = []
         for op in w.ops:
@@ -528,7 +538,7 @@ def run_workload(name, args):
         reserved = int(sum(-(-int(L) // w.bs) * w.bs for L in lens))
         step_bytes = logical + kv_write_bytes(w.B, w.Hkv, w.d, 2, e)
         print(json.dumps({
-            "workload": w.name, "metric": "decode attention KV GB/s", "unit": "GB/s",
+            "workload": w.name, "metric": "decode attention KV GB/s", "unit": "GB/s", "placement": args.placement,
             "decode_us_median": round(med, 3), "decode_us_min": round(dec_us[0], 3),
             "decode_timing": "HIP events around %d back-to-back launches, median over %d" % (rep, args.steps),
             "decode_us_single_launch_median": round(single_us[len(single_us) // 2], 3),
@@ -813,14 +823,17 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", default="llama3_8b",
-                    choices=["llama3_8b", "ragged_prefix", "long_context", "sweep", "mxfp4", "swap", "prefix_cache",
-                             "prefill"],
+                    choices=["llama3_8b", "ragged_prefix", "long_context", "sweep", "mxfp4", "fp8", "llama_layer",
+                             "swap", "prefix_cache", "prefill"],
                     help="llama3_8b: the benchmark; the others print per-setting measurements instead")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--partition-tokens", type=int, default=0, help="split-K partition size; 0 = automatic")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--placement", default="permuted", choices=["permuted", "identity"],
+                    help="physical block order: a seeded permutation (scattered blocks), or identity (each "
+                         "request's blocks contiguous and in logical order: the indirection's cost is the difference)")
     ap.add_argument("--graph", action="store_true",
                     help="default workload: replay each step's writes and decodes from two HIP graphs")
     ap.add_argument("--calibrate-copy", action="store_true",
