@@ -42,6 +42,7 @@
  *
  * Supported combinations (others return PA_ERR_UNSUPPORTED):
  *   (q / K,V input / out, cache) in {(f32, f32), (bf16, bf16), (bf16, fp8 e4m3), (bf16, mxfp4)},
+ *   and for pa_kv_write also (f32 K,V input, fp8 e4m3 cache),
  *   head_dim in {64, 128}, block_size in {8, 16, 32, 128},
  *   num_q_heads / num_kv_heads in {1, 4, 8}.
  */
@@ -80,7 +81,7 @@ int32_t pa_abi_version(void);
  * scattered).  For every token t with slot_mapping[t] >= 0 and every KV head h:
  *     k_cache[s / block_size][h][s % block_size][:] = enc_h(k[t][h][:]),  s = slot_mapping[t]
  * and the same for v.  enc is a bit copy when cache_dtype == in_dtype; for an fp8 cache
- * (in_dtype bf16) enc_h(x) = e4m3_round_nearest_even_saturate(float32(x / k_scale[h]))
+ * (in_dtype bf16 or f32) enc_h(x) = e4m3_round_nearest_even_saturate(float32(x / k_scale[h]))
  * (v_scale for v): the float32 quotient is correctly rounded, magnitudes beyond 448
  * saturate to 448, NaN stays NaN.  For an MXFP4 cache (in_dtype bf16, k_scale = v_scale =
  * NULL) each 32 dims of a row are one block: E = floor(log2(max |x|)) - 2 clamped to

@@ -46,9 +46,9 @@ def kv_write(k, v, slot_mapping, k_cache, v_cache, block_size: int, fmt: str,
     """Scatter new tokens' K/V rows into the caches, in place.
 
     k, v: [T, Hkv, d] stored inputs ('f32' float32 or 'bf16' uint16 bits).
-    fmt: cache format.  For 'fp8' the inputs are bf16 bits and every value of head h is
-    quantized with that head's scale; otherwise the cache format equals the input format
-    and rows are copied bit for bit.  Token t goes to block slot//block_size, row
+    fmt: cache format.  For 'fp8' the inputs are bf16 bits or float32 values and every value
+    of head h is quantized with that head's scale; otherwise the cache format equals the input
+    format and rows are copied bit for bit.  Token t goes to block slot//block_size, row
     slot%block_size, for every KV head; slots < 0 are skipped.
     """
     slots = np.asarray(slot_mapping, dtype=np.int64)
@@ -69,8 +69,9 @@ def kv_write(k, v, slot_mapping, k_cache, v_cache, block_size: int, fmt: str,
     if fmt == "fp8":
         ks = np.asarray(k_scale, dtype=np.float32)[None, :, None]
         vs = np.asarray(v_scale, dtype=np.float32)[None, :, None]
-        kr = codecs.e4m3_quantize(codecs.bf16_bits_to_f64(kr), ks)
-        vr = codecs.e4m3_quantize(codecs.bf16_bits_to_f64(vr), vs)
+        exact = (lambda a: a.astype(np.float64)) if kr.dtype == np.float32 else codecs.bf16_bits_to_f64
+        kr = codecs.e4m3_quantize(exact(kr), ks)
+        vr = codecs.e4m3_quantize(exact(vr), vs)
     k_cache[blk, :, row] = kr
     v_cache[blk, :, row] = vr
 

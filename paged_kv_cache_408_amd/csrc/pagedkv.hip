@@ -172,18 +172,34 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
                 reinterpret_cast<U4*>(vc + dst)[i] = reinterpret_cast<const U4*>(v + src)[i];
             }
         } else {
-            static_assert(CDT == PA_DTYPE_FP8_E4M3 && IDT == PA_DTYPE_BF16, "unsupported pair");
+            static_assert(CDT == PA_DTYPE_FP8_E4M3 && (IDT == PA_DTYPE_BF16 || IDT == PA_DTYPE_F32), "unsupported pair");
             const float ks = k_scale[h], vs = v_scale[h];
-            const U4 kx = ld16(k + src), vx = ld16(v + src);
+            float kf[8], vf[8];
+            if constexpr (IDT == PA_DTYPE_BF16) {
+                const U4 kx = ld16(k + src), vx = ld16(v + src);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t kw = u4_get(kx, i / 2), vw = u4_get(vx, i / 2);
+                    kf[i] = bf16_to_f32((i & 1) ? (kw >> 16) : (kw & 0xffffu));
+                    vf[i] = bf16_to_f32((i & 1) ? (vw >> 16) : (vw & 0xffffu));
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const U4 kx = ld16(k + src + 4 * j), vx = ld16(v + src + 4 * j);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        kf[4 * j + i] = __uint_as_float(u4_get(kx, i));
+                        vf[4 * j + i] = __uint_as_float(u4_get(vx, i));
+                    }
+                }
+            }
             uint32_t ko[2] = {0, 0}, vo[2] = {0, 0};
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const uint32_t kw = u4_get(kx, i / 2), vw = u4_get(vx, i / 2);
-                const uint32_t kb = (i & 1) ? (kw >> 16) : (kw & 0xffffu);
-                const uint32_t vb = (i & 1) ? (vw >> 16) : (vw & 0xffffu);
                 // correctly rounded float32 quotient (IEEE division, no fast-math)
-                const uint32_t kq = f32_to_e4m3(bf16_to_f32(kb) / ks);
-                const uint32_t vq = f32_to_e4m3(bf16_to_f32(vb) / vs);
+                const uint32_t kq = f32_to_e4m3(kf[i] / ks);
+                const uint32_t vq = f32_to_e4m3(vf[i] / vs);
                 ko[i / 4] |= kq << (8 * (i % 4));
                 vo[i / 4] |= vq << (8 * (i % 4));
             }
@@ -1860,7 +1876,7 @@ int pa_kv_write(const void* k, const void* v, const int64_t* slot_mapping, int64
     if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0)
         return fail(PA_ERR_INVALID, "pa_kv_write: num_tokens=%lld num_blocks=%lld num_kv_heads=%d",
                     (long long)num_tokens, (long long)num_blocks, num_kv_heads);
-    if (!supported_pair(in_dtype, cache_dtype))
+    if (!supported_pair(in_dtype, cache_dtype) && !(in_dtype == PA_DTYPE_F32 && cache_dtype == PA_DTYPE_FP8_E4M3))
         return fail(PA_ERR_UNSUPPORTED, "pa_kv_write: (input dtype %d, cache dtype %d) not supported", in_dtype, cache_dtype);
     if (head_dim != 64 && head_dim != 128)
         return fail(PA_ERR_UNSUPPORTED, "pa_kv_write: head_dim %d not in {64, 128}", head_dim);
@@ -1887,6 +1903,10 @@ int pa_kv_write(const void* k, const void* v, const int64_t* slot_mapping, int64
         hipLaunchKernelGGL((kv_write_kernel<PA_DTYPE_BF16, PA_DTYPE_BF16>), dim3(grid), dim3(256), 0, st,
                            (const uint16_t*)k, (const uint16_t*)v, slot_mapping, num_tokens, (uint16_t*)k_cache,
                            (uint16_t*)v_cache, num_slots, num_kv_heads, head_dim, block_size, k_scale, v_scale);
+    } else if (cache_dtype == PA_DTYPE_FP8_E4M3 && in_dtype == PA_DTYPE_F32) {
+        hipLaunchKernelGGL((kv_write_kernel<PA_DTYPE_F32, PA_DTYPE_FP8_E4M3>), dim3(grid), dim3(256), 0, st,
+                           (const float*)k, (const float*)v, slot_mapping, num_tokens, (uint8_t*)k_cache,
+                           (uint8_t*)v_cache, num_slots, num_kv_heads, head_dim, block_size, k_scale, v_scale);
     } else if (cache_dtype == PA_DTYPE_FP8_E4M3) {
         hipLaunchKernelGGL((kv_write_kernel<PA_DTYPE_BF16, PA_DTYPE_FP8_E4M3>), dim3(grid), dim3(256), 0, st,
                            (const uint16_t*)k, (const uint16_t*)v, slot_mapping, num_tokens, (uint8_t*)k_cache,

@@ -82,6 +82,45 @@ def test_fp8_quantize_all_bf16_inputs():
         assert np.array_equal(got_v[~nan_v], ovc[~nan_v])
 
 
+@pytest.mark.parametrize("quarter", range(4))
+def test_fp8_quantize_all_f32_patterns(quarter):
+    """pa_kv_write's fp8 quantisation (float32 K/V into an fp8 cache) on every float32 bit
+    pattern, a quarter of the 2^32 per case, with scale 1 (the quotient is the pattern itself):
+    the codes equal the oracle's encoder -- nearest code, ties to even, saturation to 448, zero
+    and subnormal signs kept -- and every NaN gives a NaN code (0x7F or 0xFF).  The patterns
+    are made on the device; the oracle encodes them on the host in threads."""
+    import concurrent.futures as cf
+    d, bs, chunk = 128, 16, 1 << 28
+    T = chunk // d                                   # one KV head: the cache rows follow the tokens
+    one = torch.ones(1, dtype=torch.float32, device=DEV)
+    slots = torch.arange(T, dtype=torch.int64, device=DEV)
+    kc = torch.empty((T // bs, 1, bs, d), dtype=torch.uint8, device=DEV)
+    vc = torch.empty_like(kc)
+    sub = 1 << 24
+
+    def oracle(base):
+        x = (np.arange(sub, dtype=np.uint64) + base).astype(np.uint32).view(np.float32)
+        return OC.e4m3_encode(x)
+
+    for c in range(4 * quarter, 4 * quarter + 4):
+        base = c * chunk
+        bits = (torch.arange(chunk, dtype=torch.int64, device=DEV) + base).to(torch.int32)
+        x = bits.view(torch.float32).view(T, 1, d)
+        pk.pa_kv_write(x, x, slots, kc, vc, k_scale=one, v_scale=one)
+        torch.cuda.synchronize()
+        got = kc.view(-1).cpu().numpy()
+        del bits, x
+        with cf.ThreadPoolExecutor(16) as ex:
+            ref = np.concatenate(list(ex.map(oracle, range(base, base + chunk, sub))))
+        xb = (np.arange(chunk, dtype=np.uint64) + base).astype(np.uint32)
+        nan = (xb & 0x7FFFFFFF) > 0x7F800000
+        assert np.array_equal((got[nan] & 0x7F), np.full(int(nan.sum()), 0x7F, np.uint8)), "a NaN lost its NaN code"
+        bad = np.flatnonzero((got != ref) & ~nan)
+        assert bad.size == 0, (f"{bad.size} patterns differ in [{base:#x}, {base + chunk:#x}), first "
+                               f"{int(xb[bad[0]]):#010x}: device {int(got[bad[0]]):#04x}, oracle {int(ref[bad[0]]):#04x}")
+        assert np.array_equal(vc.view(-1).cpu().numpy(), got)
+
+
 def test_fp8_decode_all_codes():
     """Every E4M3FN code placed in the V cache comes back exactly (L = 1, scale 1: the
     output is the decoded V row; bf16 holds every e4m3 value exactly)."""

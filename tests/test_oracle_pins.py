@@ -416,6 +416,32 @@ def test_splitk_merge_equals_single_pass(ptok):
 
 # --------------------------------------------------------------------------- codecs
 
+def test_fp8_write_float32_input_equals_bf16_input():
+    """The oracle's fp8 write from float32 inputs gives, for values that bf16 holds exactly,
+    the same codes as its write from the bf16 bit patterns of those values (same scales);
+    float32 inputs between bf16 neighbours land on one of the two neighbours' codes or between
+    them (the encoder is monotone)."""
+    rng = np.random.default_rng(17)
+    T, H, d, bs = 40, 2, 16, 8
+    x32 = (rng.standard_normal((T, H, d)) * 40).astype(np.float32)
+    xb = C.f32_to_bf16_bits(x32)
+    x_exact = C.bf16_bits_to_f64(xb).astype(np.float32)        # the bf16 values, as float32
+    scales = np.float32([0.37, 1.9])
+    slots = np.arange(T)
+    kb, vb = np.zeros((T // bs, H, bs, d), np.uint8), np.zeros((T // bs, H, bs, d), np.uint8)
+    kf, vf = kb.copy(), vb.copy()
+    A.kv_write(xb, xb, slots, kb, vb, bs, "fp8", scales, scales)
+    A.kv_write(x_exact, x_exact, slots, kf, vf, bs, "fp8", scales, scales)
+    assert np.array_equal(kb, kf) and np.array_equal(vb, vf)
+    # unrounded float32 inputs: codes are monotone in the value, per head
+    kr = np.zeros_like(kb)
+    A.kv_write(x32, x32, slots, kr, kr.copy(), bs, "fp8", scales, scales)
+    vals = C.e4m3_bits_to_f64(kr).transpose(0, 2, 1, 3).reshape(T, H, d)
+    for h in range(H):
+        order = np.argsort(x32[:, h].ravel(), kind="stable")
+        assert np.all(np.diff(vals[:, h].ravel()[order]) >= 0)
+
+
 def test_e4m3_decode_table_from_format():
     D = C.E4M3_DECODE
     assert D[0x00] == 0.0 and D[0x01] == 2.0 ** -9 and D[0x07] == 7 * 2.0 ** -9
