@@ -277,7 +277,14 @@ def run(args):
     log(f"split-K partitions of {part_used} tokens (requested {args.partition_tokens}; 0 = automatic)")
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     pk.pa_decode_workspace_init(ws)
+    fused = args.step == "fused"
+
     def prepared(stream):
+        if fused:   # each layer's write inside its decode launch (pa_decode_append)
+            d_ = [pk.PreparedDecodeAppend(outs[l], q[l], kn[l], vn[l], kc[l], vc[l], tables_d, lens_d, scale, bs,
+                                          max_seq_len=max_seq, workspace=ws, partition_tokens=args.partition_tokens,
+                                          stream=stream) for l in range(layers)]
+            return d_, []
         d_ = [pk.PreparedDecode(outs[l], q[l], kc[l], vc[l], tables_d, lens_d, scale, bs, max_seq_len=max_seq,
                                 workspace=ws, partition_tokens=args.partition_tokens, stream=stream)
               for l in range(layers)]
@@ -289,7 +296,7 @@ def run(args):
     ones = [1] * B
 
     def write_all():                     # each layer's new K/V first ...
-        for l in range(layers):
+        for l in range(len(wr)):
             wr[l]()
 
     def decode_all():                    # ... then the 32 decode launches back to back
@@ -342,7 +349,7 @@ def run(args):
         dec_c, wr_c = prepared(cap)
         g_write, g_decode = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_write, stream=cap, capture_error_mode="thread_local"):
-            for l in range(layers):
+            for l in range(len(wr_c)):
                 wr_c[l]()
         with torch.cuda.graph(g_decode, stream=cap, capture_error_mode="thread_local"):
             for l in range(layers):
@@ -378,8 +385,10 @@ def run(args):
 
     # HIP events on the launch stream around each step's 32 back-to-back decode launches
     dec_ms = [e[2].elapsed_time(e[3]) / layers for e in evs for _ in range(layers)]
-    dec_bytes = [decode_bytes(L, Hq, Hkv, d, bs, 2, 2) for L in lens_per_step for _ in range(layers)]
-    step_bytes = sum(dec_bytes) + steps * layers * kv_write_bytes(B, Hkv, d, 2, 2)
+    # a fused launch also moves its layer's write (the new rows read and written; no slots)
+    wbytes = 2 * B * Hkv * d * (2 + 2) if fused else 0
+    dec_bytes = [decode_bytes(L, Hq, Hkv, d, bs, 2, 2) + wbytes for L in lens_per_step for _ in range(layers)]
+    step_bytes = sum(dec_bytes) + (0 if fused else steps * layers * kv_write_bytes(B, Hkv, d, 2, 2))
     value = step_bytes / wall / 1e9
     avg_launch_s = sum(dec_ms) / len(dec_ms) / 1e3
     avg_bytes = sum(dec_bytes) / len(dec_bytes)
@@ -409,10 +418,12 @@ def run(args):
             "partition_tokens": part_used, "placement": args.placement,
             "kv_cache_gb": round(2 * layers * kc[0].numel() * 2 / 1e9, 3),
             "launch": "two HIP graphs per step" if args.graph else "one host launch per kernel",
+            "step": "pa_decode_append (each layer's KV write inside its decode launch)" if fused else
+                    "pa_kv_write then pa_decode per layer (writes first)",
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": DECODE_KERNEL,
+            "kernel": DECODE_KERNEL + (" (with the layer's KV write: pa_decode_append)" if fused else ""),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -831,6 +842,9 @@ def main():
     ap.add_argument("--partition-tokens", type=int, default=0, help="split-K partition size; 0 = automatic")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step", default="separate", choices=["separate", "fused"],
+                    help="default workload: each layer's KV write as its own launch before the decodes "
+                         "(pa_kv_write, then pa_decode), or inside its decode launch (pa_decode_append)")
     ap.add_argument("--placement", default="permuted", choices=["permuted", "identity"],
                     help="physical block order: a seeded permutation (scattered blocks), or identity (each "
                          "request's blocks contiguous and in logical order: the indirection's cost is the difference)")

@@ -175,6 +175,34 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               const float* k_scale, const float* v_scale,
               void* workspace, int64_t workspace_bytes, int32_t partition_tokens, void* stream);
 
+/* ---------------------------------------------------------------- append and decode in one launch
+ *
+ * One decode step of a layer in one launch: the slot-mapped write of each request's new token
+ * ("The Mechanics of PagedAttention": the new K/V are written into the request's physical
+ * block, wherever it is) and the decode over the tokens including it ("The Math: Block
+ * Attention Calculation").  For every request b with L = seq_lens[b] >= 1 and every KV head h,
+ * the token at logical position L - 1 is written through the block table --
+ *     slot = block_tables[b][(L - 1) / block_size] * block_size + (L - 1) % block_size
+ * -- with k_new[b][h][:] and v_new[b][h][:] exactly as pa_kv_write writes a slot (bit copy,
+ * fp8 quantisation with k_scale / v_scale, or MXFP4), and then out is computed as pa_decode
+ * computes it.  The result (cache bytes and out) is bit-identical to pa_kv_write of those
+ * slots followed by pa_decode with the same arguments.  The one wave that reads position
+ * L - 1 writes it first and waits for its stores; no separate write launch, and no other wave,
+ * touches it.
+ *  k_new, v_new  device, [num_seqs][num_kv_heads][head_dim] of q_dtype (bf16), 16-byte aligned
+ *  the other arguments as pa_decode; the caches are written (position L - 1 only).
+ * Contract: the caller has appended the token in the allocator (pa_seq_append or
+ * pa_batch_append, copy-on-write pairs copied), so position L - 1 maps to a slot that belongs
+ * to this request alone.  Float32 caches are not supported (PA_ERR_UNSUPPORTED: use the two
+ * calls).  A table entry outside [0, num_blocks) at position L - 1 is not written; the request's
+ * output is NaN as in pa_decode. */
+int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                     const int32_t* block_tables, const int32_t* seq_lens, float scale, int32_t block_size,
+                     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_seq_len, int32_t q_dtype,
+                     int32_t cache_dtype, const float* k_scale, const float* v_scale, void* workspace,
+                     int64_t workspace_bytes, int32_t partition_tokens, void* stream);
+
 /* ---------------------------------------------------------------- decode without allocation
  *
  * For callers that cannot allocate device memory or hand the library a workspace: code under

@@ -26,7 +26,7 @@ EXPORTED = [
     "pa_batch_append", "pa_seq_fork", "pa_seq_free", "pa_block_tables", "pa_alloc_stats",
     "pa_alloc_dump", "pa_alloc_set_host_blocks", "pa_swap_out", "pa_swap_in", "pa_seq_is_swapped",
     "pa_alloc_dump_host", "pa_swap_blocks", "pa_seq_add_prompt", "pa_seq_append_tokens", "pa_alloc_dump_cached",
-    "pa_prefill", "pa_upload", "pa_decode_noalloc", "pa_kv_write_t", "pa_decode_t",
+    "pa_prefill", "pa_upload", "pa_decode_noalloc", "pa_kv_write_t", "pa_decode_t", "pa_decode_append",
 ]
 
 
@@ -105,6 +105,8 @@ def load(path: str = LIB_PATH):
         "pa_alloc_dump_host": (ctypes.c_int, [P, P, P, P]),
         "pa_swap_blocks": (ctypes.c_int, [P, P, P, P, P, I32, I64, I64, I32, I32, I32, I32, P]),
         "pa_upload": (ctypes.c_int, [P, P, I64, P]),
+        "pa_decode_append": (ctypes.c_int, [P, P, P, P, P, P, P, P, F32, I32, I32, I32, I32, I32, I64, I32, I32, I32,
+                                            I32, P, P, P, I64, I32, P]),
         "pa_kv_write_t": (ctypes.c_int, [ctypes.POINTER(pa_tensor)] * 5 + [ctypes.POINTER(pa_opts)]),
         "pa_decode_t": (ctypes.c_int, [ctypes.POINTER(pa_tensor)] * 6 + [F32, I32, ctypes.POINTER(pa_opts)]),
         "pa_decode_noalloc": (ctypes.c_int, [P, P, P, P, P, P, F32, I32, I32, I32, I32, I32, I64, I32, I32, I32,
@@ -312,6 +314,63 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, block_siz
                           _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), ws_ptr, ws_bytes,
                           int(partition_tokens), _stream(stream))
     _check(rc)
+
+
+def pa_decode_append(out, q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, scale, block_size, *,
+                     max_seq_len=None, k_scale=None, v_scale=None, workspace=None, partition_tokens=0, stream=None):
+    """One launch: each request's new token (k_new, v_new: [B, Hkv, d], q's dtype) written at its
+    position seq_lens[b] - 1 through the table, then the decode of pa_decode (see
+    pa_decode_append in include/pagedkv.h).  The caches are modified."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    N, Hkv, bs, dc, cdt = _cache_geom(k_cache, "k_cache")
+    if out.shape != q.shape or v_cache.shape != k_cache.shape or dc != d or bs != block_size:
+        raise ValueError("shape mismatch")
+    if k_new.shape != (B, Hkv, d) or v_new.shape != k_new.shape or k_new.dtype != q.dtype or v_new.dtype != q.dtype:
+        raise ValueError(f"k_new, v_new must be [{B}, {Hkv}, {d}] of q's dtype")
+    max_blocks = block_tables.shape[1]
+    if max_seq_len is None:
+        max_seq_len = max_blocks * block_size
+    if workspace is None:
+        nbytes = pa_decode_workspace_bytes(B, Hq, Hkv, d, max_seq_len, partition_tokens, block_size, cdt)
+        key = (B, Hq, Hkv, d, int(max_seq_len), int(partition_tokens), block_size, cdt)
+        workspace = decode_workspace(nbytes, q.device, key, stream=stream) if nbytes > 0 else None
+    elif workspace is False:
+        workspace = None
+    rc = load().pa_decode_append(_dev(out, "out"), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                                 _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
+                                 _dev(seq_lens, "seq_lens"), float(scale), block_size, B, Hq, Hkv, d, N, max_blocks,
+                                 int(max_seq_len), _dtype_code(q, "q"), cdt, _dev(k_scale, "k_scale"),
+                                 _dev(v_scale, "v_scale"), _dev(workspace, "workspace"),
+                                 workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                 int(partition_tokens), _stream(stream))
+    _check(rc)
+
+
+class PreparedDecodeAppend:
+    """pa_decode_append with its arguments marshalled once (see PreparedDecode)."""
+
+    def __init__(self, out, q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, scale, block_size, *,
+                 max_seq_len, workspace, k_scale=None, v_scale=None, partition_tokens=0, stream=None):
+        B, Hq, d = q.shape
+        N, Hkv, bs, dc, cdt = _cache_geom(k_cache, "k_cache")
+        if out.shape != q.shape or v_cache.shape != k_cache.shape or dc != d or bs != block_size or \
+                k_new.shape != (B, Hkv, d) or v_new.shape != k_new.shape:
+            raise ValueError("shape mismatch")
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        self._keep = (out, q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, workspace, k_scale, v_scale)
+        self._args = (_dev(out, "out"), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                      _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
+                      _dev(seq_lens, "seq_lens"), ctypes.c_float(scale), block_size, B, Hq, Hkv, d, N,
+                      block_tables.shape[1], int(max_seq_len), _dtype_code(q, "q"), cdt, _dev(k_scale, "k_scale"),
+                      _dev(v_scale, "v_scale"), _dev(workspace, "workspace"), ws_bytes, int(partition_tokens),
+                      _stream(stream))
+        self._fn = load().pa_decode_append
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc:
+            _check(rc)
 
 
 def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, seq_lens, scale, block_size, *, max_seq_len=None,

@@ -408,6 +408,8 @@ struct DecodeArgs {
     const int32_t* seq_lens;
     const float* k_scale;
     const float* v_scale;
+    const void* k_new;     // pa_decode_append: each request's new token's K and V rows (q's dtype), else null
+    const void* v_new;
     int* ws_ctr;           // merge tickets, ctr_stride per (request, KV head): one per group of partitions
                            // (level 1), the last one for the groups (level 2); zero between calls
     float* ws_m;           // level-1 partials: one row per (request, q head, partition)
@@ -1101,6 +1103,66 @@ struct MCfg<PA_DTYPE_MXFP4, D> {
 constexpr int kMaxListSeqs = 8192;   // batches up to this size use the compact item list
 
 
+// pa_decode_append: the row of request b's new token (logical position pos) for KV head g,
+// written through the block table exactly as pa_kv_write writes a slot: a bit copy (bf16), the
+// fp8 quantisation with the head's scale, or the MXFP4 block quantisation.  Called by the one
+// wave that reads position pos; the new row is loaded together with its block id, so the wave
+// waits for one load and one store.  A block id outside the pool is not written (the decode
+// turns the request's output into NaN).
+template <int CDT, int D, int BS>
+__device__ __forceinline__ void append_row(const DecodeArgs& a, int b, int g, int pos, int lane) {
+    const int64_t src = (int64_t(b) * a.hkv + g) * D;            // the request's row of head g
+    const uint16_t* kn = static_cast<const uint16_t*>(a.k_new) + src;
+    const uint16_t* vn = static_cast<const uint16_t*>(a.v_new) + src;
+    unsigned char* kc = static_cast<unsigned char*>(const_cast<void*>(a.k_cache));
+    unsigned char* vc = static_cast<unsigned char*>(const_cast<void*>(a.v_cache));
+    const int r = pos % BS;
+    if constexpr (CDT == PA_DTYPE_MXFP4) {
+        constexpr int NB = D / 32;                                  // 32-dim blocks per row
+        if (lane >= 2 * NB) return;
+        const bool isv = lane >= NB;
+        const int c = lane % NB;
+        const uint16_t* x16 = (isv ? vn : kn) + 32 * c;
+        uint32_t x[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const U4 u = gld16(x16 + 8 * i);
+            x[4 * i] = u.x; x[4 * i + 1] = u.y; x[4 * i + 2] = u.z; x[4 * i + 3] = u.w;
+        }
+        const int blk = gld_i32(a.block_tables + int64_t(b) * a.max_blocks + pos / BS);
+        if (blk < 0 || blk >= a.num_blocks) return;
+        uint32_t codes[4], scale;
+        mx4_quantize(x, codes, scale);
+        const int64_t tile = (int64_t(blk) * a.hkv + g) * (int64_t(BS) * (D / 2 + D / 32));
+        unsigned char* base = (isv ? vc : kc) + tile;
+        *reinterpret_cast<U4*>(base + r * (D / 2) + 16 * c) = U4{codes[0], codes[1], codes[2], codes[3]};
+        base[int64_t(BS) * (D / 2) + r * (D / 32) + c] = static_cast<unsigned char>(scale);
+    } else {
+        constexpr int LPR = D / 8;                                  // lanes per row, 8 elements each
+        if (lane >= 2 * LPR) return;
+        const bool isv = lane >= LPR;
+        const int c = lane % LPR;
+        const U4 x = gld16((isv ? vn : kn) + 8 * c);
+        const float sc = CDT == PA_DTYPE_BF16 ? 1.0f : gld_f32((isv ? a.v_scale : a.k_scale) + g);
+        const int blk = gld_i32(a.block_tables + int64_t(b) * a.max_blocks + pos / BS);
+        if (blk < 0 || blk >= a.num_blocks) return;
+        const int64_t row = (int64_t(blk) * a.hkv + g) * BS + r;
+        if constexpr (CDT == PA_DTYPE_BF16) {
+            *reinterpret_cast<U4*>((isv ? vc : kc) + row * D * 2 + 16 * c) = x;
+        } else {
+            uint32_t o[2] = {0, 0};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t wd = u4_get(x, i / 2);
+                const uint32_t bits = (i & 1) ? (wd >> 16) : (wd & 0xffffu);
+                // correctly rounded float32 quotient (IEEE division, no fast-math), as pa_kv_write
+                o[i / 4] |= f32_to_e4m3(bf16_to_f32(bits) / sc) << (8 * (i % 4));
+            }
+            *reinterpret_cast<uint2*>((isv ? vc : kc) + row * D + 8 * c) = make_uint2(o[0], o[1]);
+        }
+    }
+}
+
 template <int CDT, int QDT, int D, int BS, int G, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void decode_mfma_kernel(const DecodeArgs a) {
     using M = MCfg<CDT, D>;
@@ -1211,6 +1273,15 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_mfma_kernel(const DecodeArg
             }
         };
         check_entries(0);
+
+        // pa_decode_append: the new token (position L - 1) of KV head g is read by one pass of
+        // the request's last partition, and each wave loads only its own passes, so the wave
+        // that runs that pass writes the row and drains its memory counter (the stores have
+        // completed) before its first load; the other waves do not wait
+        if (a.k_new != nullptr && part == nparts - 1 && w == ((L - 1 - t0) / TPP) % NW) {
+            append_row<CDT, D, BS>(a, b, g, L - 1, lane);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
 
         float m_ref = -INFINITY, l_run = 0.0f;            // head `col`
         f32x4v acc[M::NPV];                               // out[head 4*grp4 + i][16 t + col]
@@ -1862,6 +1933,95 @@ constexpr int kMaxScratchDevices = 64;
 std::mutex g_scratch_mu;
 ScratchDevice g_scratch[kMaxScratchDevices];
 
+int decode_call(const char* fn, void* out, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                int32_t block_size, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq,
+                int32_t max_seq_len, int32_t q_dtype, int32_t cache_dtype,
+                const float* k_scale, const float* v_scale,
+                void* workspace, int64_t workspace_bytes, int32_t partition_tokens, void* stream,
+                const void* k_new, const void* v_new) {
+    if (!supported_pair(q_dtype, cache_dtype))
+        return fail(PA_ERR_UNSUPPORTED, "%s: (q dtype %d, cache dtype %d) not supported", fn, q_dtype, cache_dtype);
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq < 0 ||
+        max_seq_len < 0 || partition_tokens < 0)
+        return fail(PA_ERR_INVALID, "%s: negative or zero size", fn);
+    if (num_q_heads % num_kv_heads != 0)
+        return fail(PA_ERR_INVALID, "%s: num_q_heads %d not a multiple of num_kv_heads %d", fn, num_q_heads, num_kv_heads);
+    if (!(scale == scale)) return fail(PA_ERR_INVALID, "%s: scale is NaN", fn);
+    if (num_seqs == 0) return PA_OK;
+    if (!out || !q || !k_cache || !v_cache || !seq_lens || (max_blocks_per_seq > 0 && !block_tables))
+        return fail(PA_ERR_INVALID, "%s: NULL pointer", fn);
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+        return fail(PA_ERR_INVALID, "%s: out, q and caches must be 16-byte aligned", fn);
+    if (cache_dtype == PA_DTYPE_FP8_E4M3 && (!k_scale || !v_scale))
+        return fail(PA_ERR_INVALID, "%s: fp8 cache needs k_scale and v_scale", fn);
+    if (int64_t(max_blocks_per_seq) * block_size < max_seq_len)
+        return fail(PA_ERR_INVALID, "%s: max_blocks_per_seq * block_size < max_seq_len", fn);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128}", fn, head_dim);
+    if (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 128)
+        return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d not in {8, 16, 32, 128}", fn, block_size);
+
+    DecodeArgs a{};
+    a.out = out;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.score_scale = scale * kLog2e;
+    a.num_seqs = num_seqs;
+    a.hkv = num_kv_heads;
+    a.num_blocks = num_blocks;
+    a.max_blocks = max_blocks_per_seq;
+    a.max_seq_len = max_seq_len;
+
+    const int unit = partition_unit(block_size);
+    int64_t pt = resolve_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens, block_size, cache_dtype);
+    int64_t parts = max_seq_len > 0 ? (int64_t(max_seq_len) + pt - 1) / pt : 1;
+    if (parts > 1) {
+        const WsLayout lay = ws_layout(int64_t(num_seqs) * num_q_heads, max_seq_len, parts, head_dim);
+        if (!workspace) {
+            // no workspace: one partition per request
+            pt = (max_seq_len + unit - 1) / unit * unit;
+            parts = 1;
+        } else if (workspace_bytes < lay.bytes || !aligned16(workspace)) {
+            return fail(PA_ERR_INVALID, "%s: workspace of %lld bytes, %lld needed (16-byte aligned)", fn,
+                        (long long)workspace_bytes, (long long)lay.bytes);
+        } else {
+            char* base = static_cast<char*>(workspace);
+            a.ws_ctr = reinterpret_cast<int*>(base + lay.ctr_off);
+            a.ctr_stride = lay.stride;
+            a.ws_m2 = reinterpret_cast<float*>(base + lay.m2_off);
+            a.ws_l2 = reinterpret_cast<float*>(base + lay.l2_off);
+            a.ws_acc2 = reinterpret_cast<float*>(base + lay.acc2_off);
+            a.ws_m = reinterpret_cast<float*>(base + lay.m_off);
+            a.ws_l = reinterpret_cast<float*>(base + lay.l_off);
+            a.ws_acc = reinterpret_cast<float*>(base + lay.acc_off);
+        }
+    }
+    if (pt > int64_t(max_seq_len) + unit) pt = (int64_t(max_seq_len) + unit - 1) / unit * unit;   // one partition
+    if (pt < unit) pt = unit;
+    if (parts > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: %lld partitions per request", fn, (long long)parts);
+    a.part_tokens = static_cast<int>(pt);
+    a.max_parts = static_cast<int>(parts);
+
+    const int G = num_q_heads / num_kv_heads;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (cache_dtype == PA_DTYPE_F32)
+        return dispatch_d<PA_DTYPE_F32, PA_DTYPE_F32>(head_dim, block_size, G, a, num_seqs, st);
+    if (cache_dtype == PA_DTYPE_BF16)
+        return dispatch_d<PA_DTYPE_BF16, PA_DTYPE_BF16>(head_dim, block_size, G, a, num_seqs, st);
+    if (cache_dtype == PA_DTYPE_MXFP4)
+        return dispatch_d<PA_DTYPE_MXFP4, PA_DTYPE_BF16>(head_dim, block_size, G, a, num_seqs, st);
+    return dispatch_d<PA_DTYPE_FP8_E4M3, PA_DTYPE_BF16>(head_dim, block_size, G, a, num_seqs, st);
+}
+
 }  // namespace
 
 // ====================================================================== C ABI
@@ -1951,83 +2111,27 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               const float* k_scale, const float* v_scale,
               void* workspace, int64_t workspace_bytes, int32_t partition_tokens, void* stream) {
     pagedkv::clear_error();
-    if (!supported_pair(q_dtype, cache_dtype))
-        return fail(PA_ERR_UNSUPPORTED, "pa_decode: (q dtype %d, cache dtype %d) not supported", q_dtype, cache_dtype);
-    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq < 0 ||
-        max_seq_len < 0 || partition_tokens < 0)
-        return fail(PA_ERR_INVALID, "pa_decode: negative or zero size");
-    if (num_q_heads % num_kv_heads != 0)
-        return fail(PA_ERR_INVALID, "pa_decode: num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads, num_kv_heads);
-    if (!(scale == scale)) return fail(PA_ERR_INVALID, "pa_decode: scale is NaN");
-    if (num_seqs == 0) return PA_OK;
-    if (!out || !q || !k_cache || !v_cache || !seq_lens || (max_blocks_per_seq > 0 && !block_tables))
-        return fail(PA_ERR_INVALID, "pa_decode: NULL pointer");
-    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
-        return fail(PA_ERR_INVALID, "pa_decode: out, q and caches must be 16-byte aligned");
-    if (cache_dtype == PA_DTYPE_FP8_E4M3 && (!k_scale || !v_scale))
-        return fail(PA_ERR_INVALID, "pa_decode: fp8 cache needs k_scale and v_scale");
-    if (int64_t(max_blocks_per_seq) * block_size < max_seq_len)
-        return fail(PA_ERR_INVALID, "pa_decode: max_blocks_per_seq * block_size < max_seq_len");
-    if (head_dim != 64 && head_dim != 128)
-        return fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim %d not in {64, 128}", head_dim);
-    if (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 128)
-        return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d not in {8, 16, 32, 128}", block_size);
+    return decode_call("pa_decode", out, q, k_cache, v_cache, block_tables, seq_lens, scale, block_size, num_seqs,
+                       num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_seq_len, q_dtype,
+                       cache_dtype, k_scale, v_scale, workspace, workspace_bytes, partition_tokens, stream, nullptr,
+                       nullptr);
+}
 
-    DecodeArgs a{};
-    a.out = out;
-    a.q = q;
-    a.k_cache = k_cache;
-    a.v_cache = v_cache;
-    a.block_tables = block_tables;
-    a.seq_lens = seq_lens;
-    a.k_scale = k_scale;
-    a.v_scale = v_scale;
-    a.score_scale = scale * kLog2e;
-    a.num_seqs = num_seqs;
-    a.hkv = num_kv_heads;
-    a.num_blocks = num_blocks;
-    a.max_blocks = max_blocks_per_seq;
-    a.max_seq_len = max_seq_len;
-
-    const int unit = partition_unit(block_size);
-    int64_t pt = resolve_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens, block_size, cache_dtype);
-    int64_t parts = max_seq_len > 0 ? (int64_t(max_seq_len) + pt - 1) / pt : 1;
-    if (parts > 1) {
-        const WsLayout lay = ws_layout(int64_t(num_seqs) * num_q_heads, max_seq_len, parts, head_dim);
-        if (!workspace) {
-            // no workspace: one partition per request
-            pt = (max_seq_len + unit - 1) / unit * unit;
-            parts = 1;
-        } else if (workspace_bytes < lay.bytes || !aligned16(workspace)) {
-            return fail(PA_ERR_INVALID, "pa_decode: workspace of %lld bytes, %lld needed (16-byte aligned)",
-                        (long long)workspace_bytes, (long long)lay.bytes);
-        } else {
-            char* base = static_cast<char*>(workspace);
-            a.ws_ctr = reinterpret_cast<int*>(base + lay.ctr_off);
-            a.ctr_stride = lay.stride;
-            a.ws_m2 = reinterpret_cast<float*>(base + lay.m2_off);
-            a.ws_l2 = reinterpret_cast<float*>(base + lay.l2_off);
-            a.ws_acc2 = reinterpret_cast<float*>(base + lay.acc2_off);
-            a.ws_m = reinterpret_cast<float*>(base + lay.m_off);
-            a.ws_l = reinterpret_cast<float*>(base + lay.l_off);
-            a.ws_acc = reinterpret_cast<float*>(base + lay.acc_off);
-        }
-    }
-    if (pt > int64_t(max_seq_len) + unit) pt = (int64_t(max_seq_len) + unit - 1) / unit * unit;   // one partition
-    if (pt < unit) pt = unit;
-    if (parts > 65535) return fail(PA_ERR_UNSUPPORTED, "pa_decode: %lld partitions per request", (long long)parts);
-    a.part_tokens = static_cast<int>(pt);
-    a.max_parts = static_cast<int>(parts);
-
-    const int G = num_q_heads / num_kv_heads;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (cache_dtype == PA_DTYPE_F32)
-        return dispatch_d<PA_DTYPE_F32, PA_DTYPE_F32>(head_dim, block_size, G, a, num_seqs, st);
-    if (cache_dtype == PA_DTYPE_BF16)
-        return dispatch_d<PA_DTYPE_BF16, PA_DTYPE_BF16>(head_dim, block_size, G, a, num_seqs, st);
-    if (cache_dtype == PA_DTYPE_MXFP4)
-        return dispatch_d<PA_DTYPE_MXFP4, PA_DTYPE_BF16>(head_dim, block_size, G, a, num_seqs, st);
-    return dispatch_d<PA_DTYPE_FP8_E4M3, PA_DTYPE_BF16>(head_dim, block_size, G, a, num_seqs, st);
+int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                     const int32_t* block_tables, const int32_t* seq_lens, float scale, int32_t block_size,
+                     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_seq_len, int32_t q_dtype,
+                     int32_t cache_dtype, const float* k_scale, const float* v_scale, void* workspace,
+                     int64_t workspace_bytes, int32_t partition_tokens, void* stream) {
+    pagedkv::clear_error();
+    if (cache_dtype == PA_DTYPE_F32 || q_dtype == PA_DTYPE_F32)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode_append: float32 caches (use pa_kv_write, then pa_decode)");
+    if (num_seqs > 0 && (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)))
+        return fail(PA_ERR_INVALID, "pa_decode_append: k_new and v_new must be non-NULL and 16-byte aligned");
+    return decode_call("pa_decode_append", out, q, k_cache, v_cache, block_tables, seq_lens, scale, block_size,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_seq_len,
+                       q_dtype, cache_dtype, k_scale, v_scale, workspace, workspace_bytes, partition_tokens, stream,
+                       k_new, v_new);
 }
 
 int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -45,7 +45,7 @@ def test_header_symbols_exported():
     out = subprocess.run(["nm", "-D", "--defined-only", pk.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (pa_\w+)", out))
     assert set(names) <= exported
-    assert pk.load().pa_abi_version() == 6
+    assert pk.load().pa_abi_version() == 7
 
 
 def test_errors_are_reported():
