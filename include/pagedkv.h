@@ -186,9 +186,10 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  * -- with k_new[b][h][:] and v_new[b][h][:] exactly as pa_kv_write writes a slot (bit copy,
  * fp8 quantisation with k_scale / v_scale, or MXFP4), and then out is computed as pa_decode
  * computes it.  The result (cache bytes and out) is bit-identical to pa_kv_write of those
- * slots followed by pa_decode with the same arguments.  The one wave that reads position
- * L - 1 writes it first and waits for its stores; no separate write launch, and no other wave,
- * touches it.
+ * slots followed by pa_decode with the same arguments.  Only the one wave that reads position
+ * L - 1 touches the row: over bf16 caches it stores the row when it reaches that position and
+ * uses the new values for it directly; over fp8 and MXFP4 caches it writes the row before its
+ * first load and waits for the stores.
  *  k_new, v_new  device, [num_seqs][num_kv_heads][head_dim] of q_dtype (bf16), 16-byte aligned
  *  the other arguments as pa_decode; the caches are written (position L - 1 only).
  * Contract: the caller has appended the token in the allocator (pa_seq_append or

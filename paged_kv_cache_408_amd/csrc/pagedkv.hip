@@ -1275,10 +1275,15 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_mfma_kernel(const DecodeArg
         check_entries(0);
 
         // pa_decode_append: the new token (position L - 1) of KV head g is read by one pass of
-        // the request's last partition, and each wave loads only its own passes, so the wave
-        // that runs that pass writes the row and drains its memory counter (the stores have
-        // completed) before its first load; the other waves do not wait
-        if (a.k_new != nullptr && part == nparts - 1 && w == ((L - 1 - t0) / TPP) % NW) {
+        // the request's last partition, and each wave loads only its own passes, so only the
+        // wave that runs that pass (`app_wave`) touches the row.  Over the bf16 ring that wave
+        // loads the new row beside its first passes, and when that pass's tile has landed in
+        // LDS it overwrites the row there and stores it to the cache (the tile's load was
+        // complete, so the store cannot race it).  The other cache types write the row first
+        // and drain the memory counter (the stores have completed) before the wave's first load.
+        constexpr bool kPatch = kStages > 0 && M::E == 2;
+        const bool app_wave = a.k_new != nullptr && part == nparts - 1 && w == ((L - 1 - t0) / TPP) % NW;
+        if (!kPatch && app_wave) {
             append_row<CDT, D, BS>(a, b, g, L - 1, lane);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
@@ -1511,6 +1516,9 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_mfma_kernel(const DecodeArg
         PA_LDS unsigned char* ring = tile;                // stage s: K at ring + 2 s KT, V at + KT
         PA_LDS unsigned char* vtile = tile + kStages * 2 * KT;   // fp8: bf16 V tile
         auto stage_k = [&](int st) { return ring + st * (2 * KT); };
+        U4 new_row = U4{0, 0, 0, 0};                     // pa_decode_append over the ring (kPatch)
+        int new_blk = -1;
+        const int new_pass = ((L - 1 - t0) / TPP) / NW;   // app_wave's pass holding position L - 1
 
         auto issue_dma = [&](int k, int st) {
             if ((k & 63) == 0 && k > 0) {   // next 64 passes' block ids (the compiler's wait drains the ring)
@@ -1554,6 +1562,22 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_mfma_kernel(const DecodeArg
             const bool partial = tb + TPP > t1;
             PA_LDS unsigned char* dk = stage_k(st);
             PA_LDS unsigned char* dv = dk + KT;
+            if constexpr (kPatch) {
+                if (app_wave && k == new_pass && lane < 2 * CPR) {
+                    // the new token's row: chunk c of tile row L - 1 - tb, then the cache
+                    const int r = L - 1 - tb, c = lane % CPR;
+                    lds_st16((lane < CPR ? dk : dv) + 16 * (r * CPR + stage_slot(r, c)), new_row);
+                    // the id's test stays here: hoisted out of the loop it would wait for the
+                    // load right after it was issued
+                    int nb = new_blk;
+                    asm volatile("" : "+v"(nb));
+                    if (nb >= 0 && nb < a.num_blocks) {
+                        unsigned char* cache = static_cast<unsigned char*>(const_cast<void*>(lane < CPR ? a.k_cache : a.v_cache));
+                        const int64_t row = (int64_t(nb) * a.hkv + g) * BS + (L - 1) % BS;
+                        *reinterpret_cast<U4*>(cache + row * M::ROWB + 16 * c) = new_row;
+                    }
+                }
+            }
             // V as a bf16 tile the transpose reads understand (rows past the end zeroed)
             PA_LDS unsigned char* vt;
             if constexpr (M::E == 2) {
@@ -1639,6 +1663,21 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_mfma_kernel(const DecodeArg
 #pragma unroll
         for (int i = 0; i < kStages - 1; ++i)
             if (i < nk) issue_dma(i, i);
+        if constexpr (kPatch) {
+            // the new row (lanes [0, CPR): K chunks, [CPR, 2 CPR): V chunks) and its block id,
+            // issued after the first passes: the ring's waits, which leave only newer loads
+            // outstanding, complete them before the pass that needs them
+            if (app_wave) {
+                if (lane < 2 * CPR)
+                    new_row = gld16(static_cast<const uint16_t*>(lane < CPR ? a.k_new : a.v_new) +
+                                    (int64_t(b) * a.hkv + g) * D + 8 * (lane % CPR));
+                // a per-lane index: a uniform one lets the compiler move the id into a scalar
+                // register at once, which waits for this load and the passes just issued
+                int e = (L - 1) / BS;
+                asm volatile("" : "+v"(e));
+                new_blk = gld_i32(table + e);
+            }
+        }
         int k = 0;
         int st = 0;                                       // stage of pass k
         for (; k + kStages - 1 < nk; ++k) {               // pass k + kStages - 1 exists
