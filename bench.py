@@ -835,7 +835,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", default="llama3_8b",
                     choices=["llama3_8b", "ragged_prefix", "long_context", "sweep", "mxfp4", "fp8", "llama_layer",
-                             "swap", "prefix_cache", "prefill"],
+                             "swap", "prefix_cache", "prefill", "read_ceiling"],
                     help="llama3_8b: the benchmark; the others print per-setting measurements instead")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
@@ -876,6 +876,9 @@ def main():
     if args.workload == "prefill":
         run_prefill(args)
         return
+    if args.workload == "read_ceiling":
+        run_read_ceiling(args)
+        return
     if args.workload != "llama3_8b":
         run_workload(args.workload, args)
         return
@@ -886,6 +889,113 @@ def main():
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+
+
+def decode_tile_order(w, part_tokens):
+    """The 4 KiB (block, KV head) tiles the uniform-grid decode reads, per work-group, in pass
+    order: work-group j = part + parts * (g + Hkv * b) reads, for each 16-token pass of its
+    partition, the K tile then the V tile of block table[b][...] and head g.  Tile indices count
+    K tiles from 0 and V tiles from num_blocks * Hkv (the probe's buffer holds the K cache, then
+    the V cache).  Every request has the same length and the partitions split it evenly."""
+    import numpy as np
+    alloc = pk_allocator(w)
+    tab, lens = alloc.block_tables(list(range(w.B)), w.max_blocks)
+    L = int(lens[0])
+    assert (lens == L).all() and L % part_tokens == 0 and part_tokens % w.bs == 0
+    parts, per = L // part_tokens, part_tokens // w.bs
+    order = []
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            for part in range(parts):
+                blocks = tab[b, part * per:(part + 1) * per].astype(np.int64)
+                kt = blocks * w.Hkv + g
+                order.append(np.stack([kt, kt + w.num_blocks * w.Hkv], 1).reshape(-1))
+    # grid order of the work-groups: x = part fastest, then y = g, then z = b
+    return np.concatenate(order).astype(np.int32)
+
+
+def pk_allocator(w):
+    import paged_kv_cache_408_amd as pk
+    alloc = pk.Allocator(w.num_blocks, w.bs, w.free_order)
+    for op in w.ops:
+        if op[0] == "add":
+            alloc.add(op[1])
+        else:
+            alloc.append(op[1], op[2])
+    alloc.batch_append(list(range(w.B)), [1] * w.B)
+    return alloc
+
+
+def run_read_ceiling(args):
+    """The decode's rate beside plain streaming reads of the same memory (pa_probe_read: every
+    byte loaded once, nothing written, one four-wave work-group per compute unit).  32 layers of
+    the Llama-shaped cache at 4096 tokens, each layer's K and V caches in one allocation (K
+    first), the benchmark's seeded block tables; every case runs back to back over the 32
+    layers in turn (nothing stays in the last-level cache between launches), timed with HIP
+    events:
+      - pa_decode of each layer (automatic partitions);
+      - tiles, the decode's order: the K and V tiles of every pass the decode reads, split over
+        work-groups and waves as the decode splits them, moved to LDS with no arithmetic;
+      - ranges: each work-group its own contiguous range of the layer's tiles;
+      - grid: a grid-stride sweep of the layer's K and V caches; and of one 4 GiB buffer.
+    A reference for the decode's rate, not a benchmark line."""
+    import math
+    import numpy as np
+    import torch
+    import paged_kv_cache_408_amd as pk
+    import workloads
+    dev = torch.device("cuda:0")
+    w = workloads.gqa_uniform(B=16, L=4096, layers=1, name="read_ceiling")
+    N, Hkv, bs, d = w.num_blocks, w.Hkv, w.bs, w.d
+    L = 4096
+    pt = pk.pa_decode_partition_tokens(w.B, Hkv, L, 0, bs)
+    alloc = pk_allocator(w)
+    tab, lens = alloc.block_tables(list(range(w.B)), w.max_blocks)
+    tables, lens_d = torch.from_numpy(tab).to(dev), torch.from_numpy(lens).to(dev)
+    order = torch.from_numpy(decode_tile_order(w, pt)).to(dev)
+    layers = [torch.zeros((2, N, Hkv, bs, d), dtype=torch.bfloat16, device=dev) for _ in range(32)]
+    flat = [t.view(-1) for t in layers]
+    q = torch.zeros((w.B, w.Hq, d), dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(q)
+    ws = torch.zeros(max(pk.pa_decode_workspace_bytes(w.B, w.Hq, Hkv, d, L, 0, bs), 256), dtype=torch.uint8, device=dev)
+    decs = [pk.PreparedDecode(out, q, t[0], t[1], tables, lens_d, 1 / math.sqrt(d), bs, max_seq_len=L, workspace=ws)
+            for t in layers]
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+    dec_bytes = decode_bytes([L] * w.B, w.Hq, Hkv, d, bs, 2, 2)
+    log(f"32 layers of {2 * N * Hkv * bs * d * 2} bytes; the decode reads {order.numel()} tiles of 4 KiB per layer "
+        f"({pt}-token partitions)")
+
+    def timed(fn, n=32, reps=64):
+        for i in range(n):
+            fn(i)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(reps):
+                fn(i % n)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3 / reps)
+        return sorted(times)[len(times) // 2]
+
+    def report(name, moved, us):
+        print(json.dumps({"workload": "read_ceiling", "case": name, "bytes": moved, "us_per_launch": round(us, 2),
+                          "GB_s": round(moved / us / 1e3, 1), "pct_of_8000": round(moved / us / 1e3 / 80, 1)}), flush=True)
+
+    report("pa_decode (algorithmic bytes)", dec_bytes, timed(lambda i: decs[i]()))
+    report("tiles, the decode's order", order.numel() * 4096,
+           timed(lambda i: pk.pa_probe_read(flat[i], sink, pattern=pk.PA_PROBE_TILES, tile_order=order)))
+    report("ranges, the layer's K and V", flat[0].numel() * 2,
+           timed(lambda i: pk.pa_probe_read(flat[i], sink, pattern=pk.PA_PROBE_RANGES)))
+    report("grid, the layer's K and V", flat[0].numel() * 2,
+           timed(lambda i: pk.pa_probe_read(flat[i], sink, pattern=pk.PA_PROBE_GRID)))
+    report("pa_decode again", dec_bytes, timed(lambda i: decs[i]()))
+    del layers, flat, decs
+    torch.cuda.empty_cache()
+    big = torch.zeros(1 << 30, dtype=torch.float32, device=dev)
+    report("grid, one 4 GiB buffer", 4 << 30, timed(lambda i: pk.pa_probe_read(big, sink), n=1, reps=10))
 
 
 def calibrate_copy():

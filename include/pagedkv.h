@@ -303,6 +303,34 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst, int32_t
  * per step in flight). */
 int pa_upload(void* dst, const void* src, int64_t bytes, void* stream);
 
+/* ---------------------------------------------------------------- measurement reference
+ *
+ * Plain streaming reads, the references the decode's HBM rate is set against on the same device
+ * and at the same sizes (the decode is a bandwidth-bound read of the cache, "The Math: Block
+ * Attention Calculation": every step reads each request's whole cached history).  Every byte of
+ * [src, src + bytes) is loaded once with non-temporal 16-byte loads by one work-group of four
+ * waves per compute unit; the loaded words are folded per lane and nothing is written (the sink
+ * is written only when a fold equals one fixed constant, which keeps the loads live).
+ *  pattern     PA_PROBE_GRID: a grid-stride sweep (the whole device reads one compact window at
+ *              a time); PA_PROBE_RANGES: work-group j reads its own contiguous range of 4 KiB
+ *              tiles (the decode's partitions, without a block table); PA_PROBE_TILES: passes of
+ *              two tiles taken through tile_order, split over work-groups and waves as the
+ *              decode's uniform grid splits its passes, each pass moved straight to LDS (given
+ *              the K and V tiles of every pass of a decode, its memory traffic without its
+ *              arithmetic)
+ *  src         device, 16-byte aligned; bytes a multiple of 16 (GRID) or of 4096 (RANGES,
+ *              TILES), else PA_ERR_INVALID
+ *  tile_order, order_len  PA_PROBE_TILES: device, int32 [order_len] (even), the indices of src's
+ *              4 KiB tiles to read, two per pass (entries outside [0, bytes / 4096) are clamped
+ *              into it); else ignored
+ *  sink        device, at least 4 x (compute units) bytes (else PA_ERR_INVALID)
+ * Enqueued on `stream`; computes nothing the caller reads. */
+#define PA_PROBE_GRID 0
+#define PA_PROBE_RANGES 1
+#define PA_PROBE_TILES 2
+int pa_probe_read(const void* src, int64_t bytes, int32_t pattern, const int32_t* tile_order, int64_t order_len,
+                  void* sink, int64_t sink_bytes, void* stream);
+
 /* ---------------------------------------------------------------- tensor-view entry points
  *
  * pa_kv_write and pa_decode over non-owning tensor views, for callers that hold shapes and

@@ -13,6 +13,6 @@ from ._lib import (  # noqa: F401
     pa_alloc_stats, pa_batch_append, pa_block_tables, pa_copy_blocks, pa_decode,
     pa_decode_workspace_bytes, pa_decode_partition_tokens, pa_decode_workspace_init, decode_workspace, pa_kv_write, pa_seq_add, pa_seq_append, pa_seq_fork, pa_seq_free,
     pa_alloc_set_host_blocks, pa_swap_out, pa_swap_in, pa_seq_is_swapped, pa_alloc_dump_host, pa_swap_blocks,
-    pa_seq_add_prompt, pa_seq_append_tokens, pa_alloc_dump_cached, pa_prefill, pa_upload, pa_decode_noalloc, pa_decode_append,
-    PreparedDecodeAppend,
+    pa_seq_add_prompt, pa_seq_append_tokens, pa_alloc_dump_cached, pa_prefill, pa_upload, pa_probe_read, pa_decode_noalloc, pa_decode_append,
+    PreparedDecodeAppend, PA_PROBE_GRID, PA_PROBE_RANGES, PA_PROBE_TILES,
 )

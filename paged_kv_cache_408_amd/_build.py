@@ -29,7 +29,7 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}"]
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-munsafe-fp-atomics"]
-SOURCES = ["pagedkv.hip", "prefill.hip", "allocator.cpp", "pa_error.cpp", "tensor_api.cpp"]
+SOURCES = ["pagedkv.hip", "prefill.hip", "probe.hip", "allocator.cpp", "pa_error.cpp", "tensor_api.cpp"]
 HEADERS = ["pa_error.h", "pa_device.h", "pa_layout.h"]
 
 

@@ -26,7 +26,7 @@ EXPORTED = [
     "pa_batch_append", "pa_seq_fork", "pa_seq_free", "pa_block_tables", "pa_alloc_stats",
     "pa_alloc_dump", "pa_alloc_set_host_blocks", "pa_swap_out", "pa_swap_in", "pa_seq_is_swapped",
     "pa_alloc_dump_host", "pa_swap_blocks", "pa_seq_add_prompt", "pa_seq_append_tokens", "pa_alloc_dump_cached",
-    "pa_prefill", "pa_upload", "pa_decode_noalloc", "pa_kv_write_t", "pa_decode_t", "pa_decode_append",
+    "pa_prefill", "pa_upload", "pa_probe_read", "pa_decode_noalloc", "pa_kv_write_t", "pa_decode_t", "pa_decode_append",
 ]
 
 
@@ -68,11 +68,14 @@ PA_DTYPE_I32, PA_DTYPE_I64 = 4, 5
 _lib = None
 
 
-def load(path: str = LIB_PATH):
-    """Load (once) and return the library handle; raises if it is missing."""
+def load(path: str | None = None):
+    """Load (once) and return the library handle; raises if it is missing.  `path` defaults to
+    the module's LIB_PATH as it is when the library is first loaded."""
     global _lib
     if _lib is not None:
         return _lib
+    if path is None:
+        path = LIB_PATH
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m paged_kv_cache_408_amd._build` "
                           "(or __graft_entry__.build()); there is no fallback path")
@@ -105,6 +108,7 @@ def load(path: str = LIB_PATH):
         "pa_alloc_dump_host": (ctypes.c_int, [P, P, P, P]),
         "pa_swap_blocks": (ctypes.c_int, [P, P, P, P, P, I32, I64, I64, I32, I32, I32, I32, P]),
         "pa_upload": (ctypes.c_int, [P, P, I64, P]),
+        "pa_probe_read": (ctypes.c_int, [P, I64, I32, P, I64, P, I64, P]),
         "pa_decode_append": (ctypes.c_int, [P, P, P, P, P, P, P, P, F32, I32, I32, I32, I32, I32, I64, I32, I32, I32,
                                             I32, P, P, P, I64, I32, P]),
         "pa_kv_write_t": (ctypes.c_int, [ctypes.POINTER(pa_tensor)] * 5 + [ctypes.POINTER(pa_opts)]),
@@ -417,6 +421,20 @@ def pa_prefill(out, q, k_cache, v_cache, block_tables, seq_lens, query_start, sc
                            _dtype_code(q, "q"), cdt, _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"),
                            _stream(stream))
     _check(rc)
+
+
+PA_PROBE_GRID, PA_PROBE_RANGES, PA_PROBE_TILES = 0, 1, 2
+
+
+def pa_probe_read(src, sink, *, pattern=PA_PROBE_GRID, tile_order=None, stream=None):
+    """A plain streaming read of a contiguous device tensor in one of three patterns (see
+    pa_probe_read in include/pagedkv.h): the references the decode's HBM rate is compared with."""
+    nbytes = src.numel() * src.element_size()
+    n_order = tile_order.numel() if tile_order is not None else 0
+    rc = load().pa_probe_read(_dev(src, "src"), nbytes, int(pattern), _dev(tile_order, "tile_order"), n_order,
+                              _dev(sink, "sink"), sink.numel() * sink.element_size(), _stream(stream))
+    if rc:
+        _check(rc)
 
 
 def pa_upload(dst, src, *, stream=None):

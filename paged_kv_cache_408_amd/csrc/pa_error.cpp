@@ -25,4 +25,4 @@ void clear_error() { g_msg[0] = '\0'; }
 
 extern "C" const char* pa_last_error(void) { return g_msg; }
 
-extern "C" int32_t pa_abi_version(void) { return 7; }
+extern "C" int32_t pa_abi_version(void) { return 8; }

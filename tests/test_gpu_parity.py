@@ -631,3 +631,20 @@ def test_tensor_view_entry_points(fmt):
                            g.scale, w.bs, r(opts)) == 0, lib.pa_last_error().decode()
     torch.cuda.synchronize()
     assert torch.equal(out_t.view(torch.int16), g.decode().view(torch.int16))
+
+
+def test_probe_read_runs_and_writes_nothing():
+    """pa_probe_read (the streaming-read references bench.py times the decode against), in each
+    pattern, reads a buffer whose words fold to zero and leaves its sink untouched; a tile order
+    with entries outside the buffer is clamped into it."""
+    x = torch.ones(1 << 20, dtype=torch.float32, device=DEV)     # 4 MiB: an even count of equal words
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=DEV)
+    pk.pa_probe_read(x, sink)
+    pk.pa_probe_read(x[: (1 << 20) - 4], sink)                   # a tail shorter than the unrolled stride
+    pk.pa_probe_read(x, sink, pattern=pk.PA_PROBE_RANGES)
+    order = torch.arange(1024, dtype=torch.int32, device=DEV).flip(0)
+    pk.pa_probe_read(x, sink, pattern=pk.PA_PROBE_TILES, tile_order=order)
+    wild = torch.tensor([-5, 0, 1023, 1024, 1 << 30, 7] * 8, dtype=torch.int32, device=DEV)
+    pk.pa_probe_read(x, sink, pattern=pk.PA_PROBE_TILES, tile_order=wild)
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum()) == 0

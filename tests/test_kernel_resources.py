@@ -1,8 +1,8 @@
 """Every kernel compiles for gfx950 with no scratch memory and no spilled vector registers
 (CPU only).  Scalar registers spilled into vector-register lanes cost no memory traffic, only a
 lane read where the value is used: up to 96 are allowed.  The decode kernels spill kernel
-arguments and loop-invariant addresses there (the most, 95, in the one-head-per-group
-instances); their launch times did not change when the count rose from 64 to that.
+arguments and loop-invariant addresses there (the most in the one-head-per-group instances); a
+build without the code that raised the count from 64 timed within 1% of them.
 
 A register array indexed by a per-lane value, or too many live values, makes the compiler
 place data in scratch memory: each access is then a memory round trip behind a full wait,

@@ -45,7 +45,7 @@ def test_header_symbols_exported():
     out = subprocess.run(["nm", "-D", "--defined-only", pk.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (pa_\w+)", out))
     assert set(names) <= exported
-    assert pk.load().pa_abi_version() == 7
+    assert pk.load().pa_abi_version() == 8
 
 
 def test_errors_are_reported():
@@ -80,6 +80,14 @@ def test_errors_are_reported():
     assert lib.pa_upload(None, None, 24, None) == pk._lib.PA_ERR_INVALID           # not a multiple of 16
     assert lib.pa_upload(None, None, 32, None) == pk._lib.PA_ERR_INVALID           # NULL pointers
     assert lib.pa_upload(16, 32, 32, None) == pk._lib.PA_ERR_INVALID               # overlapping ranges
+    assert lib.pa_probe_read(None, 0, 0, None, 0, None, 0, None) == 0                # nothing to do
+    assert lib.pa_probe_read(None, 32, 0, None, 0, None, 0, None) == pk._lib.PA_ERR_INVALID   # NULL source
+    assert lib.pa_probe_read(16, 24, 0, None, 0, None, 0, None) == pk._lib.PA_ERR_INVALID     # not a multiple of 16
+    assert lib.pa_probe_read(16, 8192, 3, None, 0, None, 0, None) == pk._lib.PA_ERR_INVALID   # unknown pattern
+    assert lib.pa_probe_read(16, 4112, 1, None, 0, None, 0, None) == pk._lib.PA_ERR_INVALID   # not whole tiles
+    assert lib.pa_probe_read(16, 8192, 2, None, 4, None, 0, None) == pk._lib.PA_ERR_INVALID   # tiles without an order
+    assert lib.pa_probe_read(16, 8192, 2, 16, 3, None, 0, None) == pk._lib.PA_ERR_INVALID     # an odd order
+    assert lib.pa_probe_read(16, 32, 0, None, 0, None, 0, None) == pk._lib.PA_ERR_INVALID     # no sink
 
 
 def test_workspace_bytes():
