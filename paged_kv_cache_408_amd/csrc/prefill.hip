@@ -68,27 +68,29 @@ struct PrefillArgs {
 #ifndef PA_PREFILL_STAGES
 #define PA_PREFILL_STAGES 2
 #endif
-constexpr int kPWaves = PA_PREFILL_WAVES;  // waves per work-group (4 or 8): 8 measured faster
 constexpr int kStages = PA_PREFILL_STAGES; // K/V tiles in the LDS ring (2 or 3): alike
-static_assert(kPWaves == 4 || kPWaves == 8, "4 or 8 waves per work-group");
+static_assert(PA_PREFILL_WAVES == 4 || PA_PREFILL_WAVES == 8, "4 or 8 waves per work-group");
 static_assert(kStages == 2 || kStages == 3, "2 or 3 stages");
-constexpr int kPThreads = 64 * kPWaves;
 constexpr int kWRows = 32;             // query rows (token, head) per wave
-constexpr int kPRows = kWRows * kPWaves;   // query rows per work-group
 constexpr int kKvTile = 64;            // KV tokens per LDS tile
-constexpr int kRW = kKvTile / kPWaves; // token rows of a tile each wave loads
+// Waves per work-group: PA_PREFILL_WAVES over bf16 caches; 8 over fp8 and 4-bit ones, whose tile
+// loads take 8 token rows per wave.
+__host__ __device__ constexpr int pwaves(int cdt) { return cdt == PA_DTYPE_BF16 ? PA_PREFILL_WAVES : 8; }
 
 // NaN-propagating maximum (v_maximum3_f32 on gfx950: no canonicalising moves before it)
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 template <int CDT, int D, int BS, int G>
-__global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(64 * pwaves(CDT), 2) void prefill_kernel(const PrefillArgs a) {
     // bf16 caches: tiles straight from HBM into LDS by DMA.  fp8 and 4-bit caches: each wave
     // loads its rows of the next tile into registers one tile ahead and writes them to the
     // same LDS tile widened to bf16 (exactly: every E4M3 value, and every E2M1 value times its
     // block's power of two, is a bf16 number); fp8's per-head scales go into the score scale
     // and the output.
     constexpr bool kQ = CDT != PA_DTYPE_BF16;
+    constexpr int kPWaves = pwaves(CDT);         // waves per work-group
+    constexpr int kPRows = kWRows * kPWaves;    // query rows per work-group
+    constexpr int kRW = kKvTile / kPWaves;      // token rows of a tile each wave loads
     constexpr bool kMx = CDT == PA_DTYPE_MXFP4;
     static_assert(CDT == PA_DTYPE_BF16 || CDT == PA_DTYPE_FP8_E4M3 || CDT == PA_DTYPE_MXFP4, "cache type");
     constexpr int ROWB = D * 2;                 // bytes of one bf16 token row
@@ -463,9 +465,9 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const PrefillArgs
 template <int CDT, int D, int BS>
 int launch_g(int G, const PrefillArgs& a, dim3 grid, hipStream_t st) {
     switch (G) {
-        case 1: hipLaunchKernelGGL((prefill_kernel<CDT, D, BS, 1>), grid, dim3(kPThreads), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((prefill_kernel<CDT, D, BS, 4>), grid, dim3(kPThreads), 0, st, a); break;
-        case 8: hipLaunchKernelGGL((prefill_kernel<CDT, D, BS, 8>), grid, dim3(kPThreads), 0, st, a); break;
+        case 1: hipLaunchKernelGGL((prefill_kernel<CDT, D, BS, 1>), grid, dim3(64 * pwaves(CDT)), 0, st, a); break;
+        case 4: hipLaunchKernelGGL((prefill_kernel<CDT, D, BS, 4>), grid, dim3(64 * pwaves(CDT)), 0, st, a); break;
+        case 8: hipLaunchKernelGGL((prefill_kernel<CDT, D, BS, 8>), grid, dim3(64 * pwaves(CDT)), 0, st, a); break;
         default: return fail(PA_ERR_UNSUPPORTED, "pa_prefill: %d query heads per KV head not in {1, 4, 8}", G);
     }
     const hipError_t e = hipGetLastError();
@@ -524,7 +526,7 @@ extern "C" int pa_prefill(void* out, const void* q, const void* k_cache, const v
     const int G = num_q_heads / num_kv_heads;
     if (G != 1 && G != 4 && G != 8)
         return fail(PA_ERR_UNSUPPORTED, "pa_prefill: %d query heads per KV head not in {1, 4, 8}", G);
-    const int TQ = kPRows / G;
+    const int TQ = kWRows * pwaves(cache_dtype) / G;   // new tokens per work-group
     const int64_t qtiles = (int64_t(max_query_len) + TQ - 1) / TQ;
     if (qtiles * num_seqs > 0x7fffffff || num_kv_heads > 65535)
         return fail(PA_ERR_UNSUPPORTED, "pa_prefill: grid of %lld x %d work-groups", (long long)(qtiles * num_seqs),
