@@ -1456,14 +1456,29 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_mfma_kernel(const DecodeArg
                     pw[h] = __builtin_bit_cast(uint32_t, pr);
                 }
                 const i16x4v pa = __builtin_bit_cast(i16x4v, make_uint2(pw[0], pw[1]));
-                // out[head][dims] += P . V, V read back token-major per dim
+                // out[head][dims] += P . V, V read back token-major per dim.  The transposed reads
+                // are issued NB at a time ahead of their products (scheduling barriers keep the
+                // compiler from pairing each read with its product behind a wait of its own, as it
+                // does at this register pressure); fp8 takes batches of four (two under 16-token
+                // blocks), which fit its registers, the 4-bit path all of them
                 const int vrow = 4 * grp4 + ((lane & 15) >> 2);
-    #pragma unroll
-                for (int t = 0; t < M::NPV; ++t) {
+                constexpr int NB = (M::NPV > 4 && !kMx) ? (BS < 16 ? 2 : 4) : M::NPV;
+                i16x4v vts[M::NPV];
+                auto read_vt = [&](int t) {
                     const int c = 2 * t + ((lane & 3) >> 1);
                     PA_LDS unsigned char* src = tile + vrow * M::TROWB + 16 * vt_slot<D>(vrow, c) + 8 * (lane & 1);
-                    const i16x4v vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4v*)src);
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vt, acc[t], 0, 0, 0);
+                    vts[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4v*)src);
+                };
+    #pragma unroll
+                for (int t = 0; t < NB; ++t) read_vt(t);
+    #pragma unroll
+                for (int t0 = 0; t0 < M::NPV; t0 += NB) {
+                    __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                    for (int t = t0 + NB; t < min(t0 + 2 * NB, M::NPV); ++t) read_vt(t);
+    #pragma unroll
+                    for (int t = t0; t < t0 + NB; ++t)
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vts[t], acc[t], 0, 0, 0);
                 }
                 };
                 if (tb + TPP > t1) body(std::true_type{});
@@ -1648,14 +1663,19 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_mfma_kernel(const DecodeArg
                 l_run += bf16_to_f32(pw[i]);
             }
             const i16x4v pa = __builtin_bit_cast(i16x4v, make_uint2(pw[0] | (pw[1] << 16), pw[2] | (pw[3] << 16)));
+            // the transposed reads all issued before their products (see the register path)
             const int vrow = 4 * grp4 + ((lane & 15) >> 2);
+            i16x4v vts[M::NPV];
 #pragma unroll
             for (int t = 0; t < M::NPV; ++t) {
                 const int c = 2 * t + ((lane & 3) >> 1);
                 PA_LDS unsigned char* src = vt + vrow * M::TROWB + 16 * dma_slot<D>(vrow, c) + 8 * (lane & 1);
-                const i16x4v vtr = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4v*)src);
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vtr, acc[t], 0, 0, 0);
+                vts[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4v*)src);
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < M::NPV; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vts[t], acc[t], 0, 0, 0);
         };
 
         // the compiler's own loads (q, table, length) complete before the ring starts
