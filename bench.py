@@ -12,15 +12,16 @@ One step is one pass of the whole hot path over the batch:
      are copied with pa_copy_blocks in every layer),
   2. block-table export: the table rows, lengths and the new tokens' slots staged in one
      pinned host buffer and moved to the device by one pa_upload kernel on the launch stream,
-  3. pa_kv_write of the 16 new tokens' K/V for each of the 32 layers, then the 32 layers'
-     pa_decode launches back to back.
+  3. the 32 layers' pa_decode_append launches back to back: each writes its layer's 16 new
+     tokens' K/V into the cache and decodes over it in one launch (`--step separate`: the 32
+     layers' pa_kv_write first, then the 32 pa_decode launches).
 Requests grow by one token per step, as in generation.
 
 Reported (one JSON line): `value` = algorithmic bytes of the whole step (every request's
 cached K/V once per KV head, q, out, table entries, lengths; plus the write's rows and
-slots) / wall time per step.  `roofline` = pa_decode (a single kernel launch per layer)
-measured with HIP events on the launch stream around each step's 32 back-to-back decode
-launches (the layers' K/V writes are issued first).  `cpu_baseline` = the float64 oracle
+slots) / wall time per step.  `roofline` = the decode kernel (one launch per layer, with the
+layer's write in it) measured with HIP events on the launch stream around each step's 32
+back-to-back decode launches.  `cpu_baseline` = the float64 oracle
 timed on a bounded sample of the same per-request work on the host.  Each run also prints,
 on stderr, where a step's time goes: host microseconds per phase and HIP-event microseconds
 of the upload, the writes, the decodes and the device's idle time between steps.
@@ -51,6 +52,7 @@ METRIC = "decode attention KV GB/s and % of HBM peak (GQA 32q/8kv d128, bf16)"
 HBM_PEAK_GBPS = 8000.0
 DECODE_KERNEL = "decode_mfma_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama3_8b_bf16_traffic.md")
+TRAFFIC_FILE_FUSED = os.path.join(ROOT, "profiles", "decode_append_llama3_8b_bf16_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_408_amd", "csrc", f) for f in ("pagedkv.hip", "pa_device.h", "pa_layout.h")]
 
 
@@ -107,12 +109,12 @@ def kernel_source_hash():
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it was
-    taken with the current kernel source; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(path=TRAFFIC_FILE):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary `path`, if it
+    was taken with the current kernel source; else None."""
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     h = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
     t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not h or not t or h.group(1) != kernel_source_hash():
@@ -348,14 +350,15 @@ def run(args):
         cap = torch.cuda.Stream()
         dec_c, wr_c = prepared(cap)
         g_write, g_decode = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_write, stream=cap, capture_error_mode="thread_local"):
-            for l in range(len(wr_c)):
-                wr_c[l]()
+        if wr_c:                         # the fused step has no separate writes
+            with torch.cuda.graph(g_write, stream=cap, capture_error_mode="thread_local"):
+                for l in range(len(wr_c)):
+                    wr_c[l]()
         with torch.cuda.graph(g_decode, stream=cap, capture_error_mode="thread_local"):
             for l in range(layers):
                 dec_c[l]()
         torch.cuda.synchronize()
-        launch = (g_write.replay, g_decode.replay)
+        launch = (g_write.replay if wr_c else (lambda: None), g_decode.replay)
     log(f"warmup done ({warm} steps); timing {steps} steps ({'HIP graphs' if args.graph else 'host launches'})")
 
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(steps)]
@@ -393,7 +396,7 @@ def run(args):
     avg_launch_s = sum(dec_ms) / len(dec_ms) / 1e3
     avg_bytes = sum(dec_bytes) / len(dec_bytes)
     achieved = avg_bytes / avg_launch_s / 1e9
-    traffic = measured_traffic()
+    traffic = measured_traffic(TRAFFIC_FILE_FUSED if fused else TRAFFIC_FILE)
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -842,9 +845,9 @@ def main():
     ap.add_argument("--partition-tokens", type=int, default=0, help="split-K partition size; 0 = automatic")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--step", default="separate", choices=["separate", "fused"],
-                    help="default workload: each layer's KV write as its own launch before the decodes "
-                         "(pa_kv_write, then pa_decode), or inside its decode launch (pa_decode_append)")
+    ap.add_argument("--step", default="fused", choices=["separate", "fused"],
+                    help="default workload: each layer's KV write inside its decode launch (pa_decode_append), "
+                         "or as its own launch before the decodes (pa_kv_write, then pa_decode)")
     ap.add_argument("--placement", default="permuted", choices=["permuted", "identity"],
                     help="physical block order: a seeded permutation (scattered blocks), or identity (each "
                          "request's blocks contiguous and in logical order: the indirection's cost is the difference)")
