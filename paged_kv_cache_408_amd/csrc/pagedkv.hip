@@ -1188,8 +1188,7 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_mfma_kernel(const DecodeArg
     __shared__ __align__(16) unsigned char s_tile[NW][WAVE_LDS];
     __shared__ float s_m[NW][G];
     __shared__ float s_l[NW][G];
-    extern __shared__ int s_pref[];                       // compact item list: B + 1 prefix sums,
-    int* const s_len = s_pref + a.num_seqs + 1;           // then the B request lengths
+    extern __shared__ int s_pref[];                       // compact item list: B + 1 prefix sums
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, uniform per wave
@@ -1734,9 +1733,9 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_mfma_kernel(const DecodeArg
                                     reinterpret_cast<float*>(&s_tile[0][0]), int(sizeof(s_tile[0]) / 4));
     };
 
-    // ---- work items: the compact list (prefix sums of each request's full partitions, all but
-    // its last, and the request lengths, in LDS), or one item per work-group of the (partition,
-    // KV head, request) grid
+    // ---- work items: the compact list (in LDS, the prefix sums of each request's full
+    // partitions, all but its last, whose differences also give each request's last partition),
+    // or one item per work-group of the (partition, KV head, request) grid
     int F = 0;
     int64_t total = 1;
     if (a.list) {
@@ -1744,10 +1743,10 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_mfma_kernel(const DecodeArg
         const int per = (B + NT - 1) / NT;
         const int i0 = min(B, int(threadIdx.x) * per), i1 = min(B, i0 + per);
         int local = 0;
-        for (int i = i0; i < i1; ++i) {
-            const int Li = gld_i32(a.seq_lens + i);
-            s_len[i] = Li;
-            local += nparts_of(Li) - 1;
+        for (int i = i0; i < i1; ++i) {                   // each request's full partitions, in place
+            const int full = nparts_of(gld_i32(a.seq_lens + i)) - 1;
+            s_pref[i] = full;
+            local += full;
         }
         __shared__ int s_wsum[NW];
         int incl = local;                                 // work-group exclusive scan of `local`
@@ -1760,9 +1759,10 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_mfma_kernel(const DecodeArg
         __syncthreads();
         int run = incl - local;
         for (int ww = 0; ww < w; ++ww) run += s_wsum[ww];
-        for (int i = i0; i < i1; ++i) {
+        for (int i = i0; i < i1; ++i) {                   // -> exclusive prefix sums
+            const int full = s_pref[i];
             s_pref[i] = run;
-            run += nparts_of(s_len[i]) - 1;
+            run += full;
         }
         if (threadIdx.x == NT - 1) s_pref[B] = run;
         __syncthreads();
@@ -1784,7 +1784,7 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_mfma_kernel(const DecodeArg
                 part = u - s_pref[lo];
             } else {
                 b = u - F;
-                part = nparts_of(s_len[b]) - 1;
+                part = s_pref[b + 1] - s_pref[b];         // its full partitions precede it
             }
         } else {
             b = blockIdx.z;
@@ -1930,7 +1930,7 @@ int launch_decode(DecodeArgs a, int B, hipStream_t st) {
         // them is empty); otherwise, up to kMaxListSeqs requests, the compact item list on
         // about one kListWaves-wave work-group per slot.
         const int64_t grid_items = int64_t(B) * a.max_parts * a.hkv;
-        const int lds = (2 * B + 1) * 4;
+        const int lds = (B + 1) * 4;
         const int64_t cus = device_cu_count();
         const int64_t grid_slots = B <= kMaxListSeqs ? cus * resident_per_cu<CDT, QDT, D, BS, G, kWaves>(0) : 0;
         if (B <= kMaxListSeqs && grid_items > grid_slots) {
