@@ -197,9 +197,12 @@ def report_phases(host_marks, evs, t0, t1, layers):
     log(f"  gpu  {layers} decodes        {us(g_de)}")
     log(f"  gpu  idle between steps{us(gap)}")
     busy = sum(g_up) + sum(g_wr) + sum(g_de)
-    log(f"  device busy {busy / 1e3:.3f} ms of {(t1 - t0) * 1e3:.3f} ms wall ({100 * busy / 1e3 / ((t1 - t0) * 1e3):.1f}%); "
+    wall_ms, last_ms = (t1 - t0) * 1e3, (host_marks[-1][5] - t0) * 1e3
+    # the host enqueues ahead of the device unless the last step is enqueued near the wall's end
+    bound = "host-bound" if last_ms > 0.9 * wall_ms else "device-bound: the host ran ahead"
+    log(f"  device busy {busy / 1e3:.3f} ms of {wall_ms:.3f} ms wall ({100 * busy / 1e3 / wall_ms:.1f}%); "
         f"host enqueue per step {st.mean([m[5] - m[0] for m in host_marks]) * 1e6:.1f} us; "
-        f"last step enqueued at {(host_marks[-1][5] - t0) * 1e3:.3f} ms of the wall (near the wall: host-bound)")
+        f"last step enqueued at {last_ms:.3f} ms of the wall ({bound})")
 
 
 
