@@ -138,6 +138,7 @@ int pa_kv_write(const void* k, const void* v, const int64_t* slot_mapping, int64
  *                ticket counters: the last work-group of each group of 16 partitions of a
  *                request and KV head merges that group, and with more than one group the last
  *                group-merger merges the groups, all in the same launch.  The ticket counters
+ *                (and two counters that hand out work items on long, few-request batches)
  *                sit at the start of the workspace, in a region whose place and size depend
  *                only on (num_seqs, num_q_heads, max_seq_len), and every call leaves them at
  *                zero.  Zero the workspace (pa_decode_workspace_init) before its first use and

@@ -1163,7 +1163,7 @@ __device__ __forceinline__ void append_row(const DecodeArgs& a, int b, int g, in
     }
 }
 
-template <int CDT, int QDT, int D, int BS, int G, int NW>
+template <int CDT, int QDT, int D, int BS, int G, int NW, bool DYN>
 __global__ __launch_bounds__(64 * NW, 2) void decode_mfma_kernel(const DecodeArgs a) {
     using M = MCfg<CDT, D>;
     constexpr int NT = 64 * NW;                           // threads per work-group
@@ -1769,7 +1769,43 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_mfma_kernel(const DecodeArg
         F = __builtin_amdgcn_readfirstlane(s_pref[B]);
         total = int64_t(F + B) * a.hkv;
     }
-    for (int64_t it = a.list ? blockIdx.x : 0; it < total; it += a.list ? gridDim.x : 1) {
+    // Items are dealt round robin.  In the DYN instances (launched for item lists of a few long
+    // requests over bf16 caches), when nearly every item is a full partition (all of the same size), the last one
+    // and a half rounds are instead handed out by a counter after the tickets, so that
+    // work-groups on faster compute units take more of them; each claim is issued when a
+    // work-group starts its current item and read when that item ends, and the last work-group
+    // to exit resets the counter and its own.  Items of mixed sizes (ragged batches) stay dealt
+    // round robin: there, long and short items interleaved keep more bytes in flight than a
+    // counter's claims, which also stall the waits of the claiming wave.  The other instances
+    // carry none of this code.
+    int* const queue = (DYN && a.list && a.ws_ctr != nullptr)
+                           ? a.ws_ctr + int64_t(a.num_seqs) * hq * a.ctr_stride : nullptr;
+    const int nslots = a.list ? int(gridDim.x) : 1;
+    const bool dyn = queue != nullptr && int64_t(F) >= 9 * int64_t(a.num_seqs) &&   // >= 90% full partitions
+                     total >= 2 * int64_t(nslots);
+    __shared__ int64_t s_base, s_item;                    // the first counted item; a claimed item
+    int n_left = 1;                                       // round-robin items left to this work-group
+    if (a.list) {
+        const int64_t n_static = dyn ? total - (3 * nslots) / 2 : total;
+        n_left = int64_t(blockIdx.x) < n_static ? int((n_static - 1 - blockIdx.x) / nslots) + 1 : 0;
+        if (threadIdx.x == 0) s_base = n_static;
+    }
+    auto take_claim = [&](int claim) {                    // the item `claim` of the counted ones
+        if (threadIdx.x == 0) s_item = s_base + claim;
+        __syncthreads();
+        const int64_t v = s_item;
+        __syncthreads();
+        return int64_t(__builtin_amdgcn_readfirstlane(int(v >> 32))) << 32 |
+               uint32_t(__builtin_amdgcn_readfirstlane(int(v & 0xffffffff)));
+    };
+    int64_t it = a.list ? blockIdx.x : 0;
+    if (dyn && n_left == 0)                               // no round-robin item: claim the first at once
+        it = take_claim(threadIdx.x == 0 ? __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0);
+    while (it < total) {
+        --n_left;
+        const bool dyn_next = dyn && n_left <= 0;
+        int claim = 0;
+        if (dyn_next && threadIdx.x == 0) claim = __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         int b, g, part;
         if (a.list) {
             const int u = static_cast<int>(it / a.hkv);
@@ -1793,6 +1829,14 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_mfma_kernel(const DecodeArg
         }
         process(__builtin_amdgcn_readfirstlane(b), __builtin_amdgcn_readfirstlane(g),
                 __builtin_amdgcn_readfirstlane(part));
+        it = dyn_next ? take_claim(claim) : it + nslots;
+    }
+    if (DYN && dyn && threadIdx.x == 0) {
+        const int done = __hip_atomic_fetch_add(queue + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == int(gridDim.x) - 1) {                 // every work-group has stopped claiming
+            __hip_atomic_store(queue, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(queue + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
@@ -1869,13 +1913,14 @@ int grid_for(int64_t work, int per_block) {
 
 // Workspace (each region 256-byte aligned):
 //   [tickets: requests x q heads x stride int32]   stride = ticket_groups + 1 per (request, KV
-//                                                   head): level-1 tickets, then the level-2 one
+//                                                   head): level-1 tickets, then the level-2 one;
+//    then 2 int32: the item list's claim counter and its exit counter
 //   [m1, l1: rows1][acc1: rows1 x d]   rows1 = requests x q heads x partitions
 //   [m2, l2: rows2][acc2: rows2 x d]   rows2 = requests x q heads x stride (only with > 1 group)
 // (q heads bound the KV heads the tickets are indexed by.)  ticket_groups bounds the merge
 // groups of every partition size (partitions hold at least 64 tokens), so the tickets' place
-// and size depend only on (requests, q heads, max_seq_len).  Every launch leaves its tickets at
-// zero, so a workspace reused with another partition size, block size, cache type, head dim or
+// and size depend only on (requests, q heads, max_seq_len).  Every launch leaves its tickets
+// and counters at zero, so a workspace reused with another partition size, block size, cache type, head dim or
 // device finds zeros where its tickets are, never a stale partial row.
 struct WsLayout {
     int64_t ctr_off, m_off, l_off, acc_off, m2_off, l2_off, acc2_off, bytes;
@@ -1890,7 +1935,7 @@ WsLayout ws_layout(int64_t seqs_x_heads, int64_t max_seq_len, int64_t parts, int
     w.stride = static_cast<int>((max_parts_any + kMergeGroup - 1) / kMergeGroup) + 1;
     const int64_t rows1 = seqs_x_heads * parts, rows2 = w.groups > 1 ? seqs_x_heads * w.stride : 0;
     w.ctr_off = 0;
-    w.m_off = up(seqs_x_heads * w.stride * 4);
+    w.m_off = up((seqs_x_heads * w.stride + 2) * 4);   // + the item list's claim and exit counters
     w.l_off = w.m_off + up(rows1 * 4);
     w.acc_off = w.l_off + up(rows1 * 4);
     w.m2_off = w.acc_off + up(rows1 * int64_t(d) * 4);
@@ -1904,13 +1949,13 @@ WsLayout ws_layout(int64_t seqs_x_heads, int64_t max_seq_len, int64_t parts, int
 // <CDT, QDT, D, BS, G, NW> at a given dynamic LDS size (cached per instance for the last size
 // asked: every instance has the same function type, so the cache is keyed by the template
 // arguments, not by the type).
-template <int CDT, int QDT, int D, int BS, int G, int NW>
+template <int CDT, int QDT, int D, int BS, int G, int NW, bool DYN>
 int resident_per_cu(int dyn_lds) {
     static std::atomic<int64_t> cache{-1};
     const int64_t c = cache.load(std::memory_order_relaxed);
     if (c >= 0 && int(c >> 32) == dyn_lds) return int(c & 0xffffffff);
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<CDT, QDT, D, BS, G, NW>, 64 * NW,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<CDT, QDT, D, BS, G, NW, DYN>, 64 * NW,
                                                      dyn_lds) != hipSuccess || n <= 0) {
         (void)hipGetLastError();
         n = 1;
@@ -1932,15 +1977,28 @@ int launch_decode(DecodeArgs a, int B, hipStream_t st) {
         const int64_t grid_items = int64_t(B) * a.max_parts * a.hkv;
         const int lds = (B + 1) * 4;
         const int64_t cus = device_cu_count();
-        const int64_t grid_slots = B <= kMaxListSeqs ? cus * resident_per_cu<CDT, QDT, D, BS, G, kWaves>(0) : 0;
+        const int64_t grid_slots = B <= kMaxListSeqs ? cus * resident_per_cu<CDT, QDT, D, BS, G, kWaves, false>(0) : 0;
         if (B <= kMaxListSeqs && grid_items > grid_slots) {
             a.list = 1;
-            const int64_t slots = cus * resident_per_cu<CDT, QDT, D, BS, G, kListWaves>(lds);
-            hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, D, BS, G, kListWaves>), dim3(static_cast<int>(slots)),
-                               dim3(64 * kListWaves), lds, st, a);
+            const int64_t slots = cus * resident_per_cu<CDT, QDT, D, BS, G, kListWaves, false>(lds);
+            // a few long requests (at most a quarter as many (request, KV head) pairs as slots)
+            // over a bf16 cache: the instance that may hand out the last items by a counter
+            bool counted = false;
+            if constexpr (CDT == PA_DTYPE_BF16) {
+                if (int64_t(B) * a.hkv * 4 <= slots) {
+                    const int64_t dslots = cus * resident_per_cu<CDT, QDT, D, BS, G, kListWaves, true>(lds);
+                    hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, D, BS, G, kListWaves, true>),
+                                       dim3(static_cast<int>(dslots)), dim3(64 * kListWaves), lds, st, a);
+                    counted = true;
+                }
+            }
+            if (!counted) {
+                hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, D, BS, G, kListWaves, false>),
+                                   dim3(static_cast<int>(slots)), dim3(64 * kListWaves), lds, st, a);
+            }
         } else {
             a.list = 0;
-            hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, D, BS, G, kWaves>), dim3(a.max_parts, a.hkv, B),
+            hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, D, BS, G, kWaves, false>), dim3(a.max_parts, a.hkv, B),
                                dim3(kThreads), 0, st, a);
         }
     }

@@ -210,7 +210,8 @@ def test_merge_paths_both_taken_and_identical():
     assert parts == 2
     nbytes = pk.pa_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, maxL, 0, w.bs)
     stride = -(-(-(-maxL // 64)) // 16) + 1                 # tickets per (request, KV head), as laid out
-    m_off = (w.B * w.Hq * stride * 4 + 255) // 256 * 256    # level-1 row maxima follow the tickets
+    m_off = ((w.B * w.Hq * stride + 2) * 4 + 255) // 256 * 256   # level-1 row maxima follow the tickets
+                                                            # and the item list's two counters
     rows = w.B * w.Hq * parts
     ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
     first, early_counts = None, []
@@ -231,6 +232,37 @@ def test_merge_paths_both_taken_and_identical():
     merges = w.B * w.Hkv * 30
     print(f"early merges {sum(early_counts)} of {merges}; per launch {early_counts}", flush=True)
     assert 0 < sum(early_counts) < merges, "both merge paths must occur"
+
+
+def test_item_list_counted_tail():
+    """A few long requests on the item list, every unit but the last of each request a full
+    partition (4 requests x 32768 tokens, 32 q / 8 KV heads, bf16, 256-token partitions: 4096
+    items, eight merge groups per request): the list's last items are handed out by a counter.
+    Three launches on one workspace, zeroed once, give the same bits and match the oracle, and
+    each leaves the tickets and both item counters at zero."""
+    w = workloads.gqa_uniform(B=4, L=32768, layers=1, seed_index=49, name="counted_tail")
+    vals = workloads.host_values(w)
+    g, o = GpuSide(w, vals), OracleSide(w, vals)
+    maxL = int(g.lens_np.max())
+    assert maxL == 32768 and pk.pa_decode_partition_tokens(w.B, w.Hkv, maxL, 256, w.bs) == 256
+    nbytes = pk.pa_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, maxL, 256, w.bs)
+    stride = -(-(-(-maxL // 64)) // 16) + 1
+    counters = (w.B * w.Hq * stride + 2) * 4                # the tickets, then the claim and exit counters
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    ref = o.decode(rows=[0, 3])
+    first = None
+    for _ in range(3):
+        out = torch.empty_like(g.q)
+        pk.pa_decode(out, g.q, g.kc, g.vc, g.tables, g.lens, g.scale, w.bs, max_seq_len=maxL, workspace=ws,
+                     partition_tokens=256)
+        torch.cuda.synchronize()
+        assert int(ws[:counters].view(torch.int32).abs().sum()) == 0, "counters left non-zero"
+        if first is None:
+            first = out.clone()
+            got = out_f64(out)
+            print(check_close(got[[0, 3]], ref[[0, 3]], w.q_fmt, w.name), flush=True)
+            assert np.isfinite(got).all()
+        assert torch.equal(out.view(torch.int16), first.view(torch.int16)), "launches differ"
 
 
 def test_workspace_shared_across_cache_types():

@@ -2,7 +2,10 @@
 (CPU only).  Scalar registers spilled into vector-register lanes cost no memory traffic, only a
 lane read where the value is used: up to 96 are allowed.  The decode kernels spill kernel
 arguments and loop-invariant addresses there (the most in the one-head-per-group instances); a
-build without the code that raised the count from 64 timed within 1% of them.
+build without the code that raised the count from 64 timed within 1% of them.  The decode
+instances that hand out an item list's last items by a counter (bf16 caches, launched only for a
+few long requests) may spill up to 112: with that code the long context in 512-token partitions decodes
+in 225 us against 247 us without it.
 
 A register array indexed by a per-lane value, or too many live values, makes the compiler
 place data in scratch memory: each access is then a memory round trip behind a full wait,
@@ -48,6 +51,8 @@ def test_no_scratch_no_spills(tmp_path):
         found = list(ex.map(lambda s: _remarks(s, str(tmp_path)), ["pagedkv.hip", "prefill.hip"]))
     kernels = {**found[0], **found[1]}
     assert any("decode_mfma_kernel" in k for k in kernels) and any("prefill_kernel" in k for k in kernels)
+    def sgpr_limit(name):   # decode_mfma_kernel<..., NW, true>: the counter-fed item list
+        return 112 if re.search(r"decode_mfma_kernelILi\d+ELi\d+ELi\d+ELi\d+ELi\d+ELi\d+ELb1E", name) else 96
     bad = {k: v for k, v in kernels.items()
-           if v.get("ScratchSize [bytes/lane]", 0) or v.get("VGPRs Spill", 0) or v.get("SGPRs Spill", 0) > 96}
+           if v.get("ScratchSize [bytes/lane]", 0) or v.get("VGPRs Spill", 0) or v.get("SGPRs Spill", 0) > sgpr_limit(k)}
     assert not bad, f"{len(bad)} kernels with scratch or spills, e.g. {list(bad.items())[:3]}"

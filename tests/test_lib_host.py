@@ -102,27 +102,27 @@ def test_errors_are_reported():
 
 
 def test_workspace_bytes():
-    """[tickets: seqs x q heads x stride int32][m1][l1][acc1][m2][l2][acc2], each region
-    256-byte aligned.  stride = ceil(ceil(max_seq_len / 64) / 16) + 1 bounds the merge groups
-    of any partition size (plus the level-2 ticket), so the tickets' region depends only on
-    (seqs, q heads, max_seq_len); the level-2 rows (stride per seq and head) exist only with
-    > 1 group."""
+    """[tickets: seqs x q heads x stride int32, then the item list's claim and exit counters]
+    [m1][l1][acc1][m2][l2][acc2], each region 256-byte aligned.  stride = ceil(ceil(max_seq_len
+    / 64) / 16) + 1 bounds the merge groups of any partition size (plus the level-2 ticket), so
+    the tickets' region depends only on (seqs, q heads, max_seq_len); the level-2 rows (stride
+    per seq and head) exist only with > 1 group."""
     up = lambda x: (x + 255) // 256 * 256
     stride = lambda L: -(-(-(-L // 64)) // 16) + 1
     # 16 requests x 32 heads, 4096 tokens in partitions of 512 -> 8 partitions, 1 group
     rows = 16 * 32 * 8
-    want = up(16 * 32 * stride(4096) * 4) + rows * 4 + rows * 4 + rows * 128 * 4
+    want = up((16 * 32 * stride(4096) + 2) * 4) + rows * 4 + rows * 4 + rows * 128 * 4
     assert stride(4096) == 5
     assert pk.pa_decode_workspace_bytes(16, 32, 8, 128, 4096, 512, 16) == want
     # the same sizes with another partition size, block size, head dim or cache type keep the
     # ticket region (the bytes before m1) in place
     for args in [(16, 32, 8, 128, 4096, 1024, 16), (16, 32, 8, 64, 4096, 256, 128), (16, 32, 4, 128, 4096, 0, 16)]:
         n = pk.pa_decode_workspace_bytes(*args, pk.PA_DTYPE_FP8_E4M3)
-        assert n == 0 or n >= up(16 * 32 * stride(4096) * 4)
+        assert n == 0 or n >= up((16 * 32 * stride(4096) + 2) * 4)
     assert pk.pa_decode_workspace_bytes(4, 8, 8, 64, 200, 512, 16) == 0          # one partition
     # 2 requests x 64 heads at 131072 tokens: 256 partitions in 16 groups
     r1, r2 = 2 * 64 * 256, 2 * 64 * stride(131072)
-    want = up(2 * 64 * stride(131072) * 4) + 2 * r1 * 4 + r1 * 128 * 4 + 2 * r2 * 4 + r2 * 128 * 4
+    want = up((2 * 64 * stride(131072) + 2) * 4) + 2 * r1 * 4 + r1 * 128 * 4 + 2 * r2 * 4 + r2 * 128 * 4
     assert stride(131072) == 129
     assert pk.pa_decode_workspace_bytes(2, 64, 8, 128, 131072, 512, 16) == want
     # automatic partitions (256 compute units when no device can be queried, as on MI355X):
@@ -130,7 +130,7 @@ def test_workspace_bytes():
     assert pk.pa_decode_partition_tokens(16, 8, 4101, 0, 16) == 2112
     rows = 16 * 32 * 2
     assert pk.pa_decode_workspace_bytes(16, 32, 8, 128, 4101, 0, 16) == \
-        up(16 * 32 * stride(4101) * 4) + rows * 4 + rows * 4 + rows * 128 * 4
+        up((16 * 32 * stride(4101) + 2) * 4) + rows * 4 + rows * 4 + rows * 128 * 4
     assert pk.pa_decode_partition_tokens(2, 8, 131072, 0, 16) == 8192          # 16 pairs -> 16 partitions
     assert pk.pa_decode_partition_tokens(256, 8, 8192, 0, 16) == 512           # >= 256 pairs: 512
     assert pk.pa_decode_partition_tokens(256, 8, 8192, 0, 128) == 512
