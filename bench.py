@@ -331,7 +331,7 @@ def run(args):
             events[1].record()
         h3 = time.perf_counter()
         launch[0]()
-        if events is not None:
+        if events is not None and events[2] is not events[1]:
             events[2].record()
         h4 = time.perf_counter()
         launch[1]()
@@ -364,7 +364,14 @@ def run(args):
         launch = (g_write.replay if wr_c else (lambda: None), g_decode.replay)
     log(f"warmup done ({warm} steps); timing {steps} steps ({'HIP graphs' if args.graph else 'host launches'})")
 
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(steps)]
+    # events per step: before the upload, after it, after the writes, after the decodes; with no
+    # separate writes (the fused step) the after-upload event stands for the after-writes one, so
+    # that no empty event pair sits in the timed region
+    def step_events():
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        return (e[0], e[1], e[1] if fused else e[2], e[3])
+
+    evs = [step_events() for _ in range(steps)]
     lens_per_step = []
     host_marks.clear()
     torch.cuda.synchronize()
