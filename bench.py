@@ -171,12 +171,13 @@ def cpu_baseline(seconds: float):
 
 # ----------------------------------------------------------------------------- GPU step
 
-def report_phases(host_marks, evs, t0, t1, layers):
+def report_phases(host_marks, evs, t0, t1, layers, phase_evs):
     """Where a timed step's time goes, on stderr: host microseconds per phase (allocator,
-    staging the tables and slots, enqueueing the upload, the writes and the decodes) and
-    HIP-event microseconds on the launch stream (upload, writes, decodes, and the gap between
-    one step's last decode and the next step's upload).  A gap means the device waited for the
-    host; host enqueue times beyond the device's show where."""
+    staging the tables and slots, enqueueing the upload, the writes and the decodes) over the
+    timed steps, the decodes' HIP-event microseconds over the timed steps, and the upload's, the
+    writes' and the gap between one step's last decode and the next step's upload over the
+    last warm-up steps, which carry those events (the timed steps carry only the decodes').  A
+    gap means the device waited for the host; host enqueue times beyond the device's show where."""
     import statistics as st
 
     def us(x):
@@ -188,15 +189,15 @@ def report_phases(host_marks, evs, t0, t1, layers):
     log(f"phase (us)               mean   median      max   over {n} timed steps")
     for nm, x in zip(names, ph):
         log(f"  host {nm:<18s}{us(x)}")
-    g_up = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
-    g_wr = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
+    g_up = [e[0].elapsed_time(e[1]) * 1e3 for e in phase_evs] or [0.0]
+    g_wr = [e[1].elapsed_time(e[2]) * 1e3 for e in phase_evs] or [0.0]
     g_de = [e[2].elapsed_time(e[3]) * 1e3 for e in evs]
-    gap = [evs[i][3].elapsed_time(evs[i + 1][0]) * 1e3 for i in range(len(evs) - 1)] or [0.0]
-    log(f"  gpu  upload            {us(g_up)}")
-    log(f"  gpu  {layers} writes         {us(g_wr)}")
+    gap = [phase_evs[i][3].elapsed_time(phase_evs[i + 1][0]) * 1e3 for i in range(len(phase_evs) - 1)] or [0.0]
+    log(f"  gpu  upload            {us(g_up)}   (last {len(phase_evs)} warm-up steps)")
+    log(f"  gpu  {layers} writes         {us(g_wr)}   (last {len(phase_evs)} warm-up steps)")
     log(f"  gpu  {layers} decodes        {us(g_de)}")
-    log(f"  gpu  idle between steps{us(gap)}")
-    busy = sum(g_up) + sum(g_wr) + sum(g_de)
+    log(f"  gpu  idle between steps{us(gap)}   (last {len(phase_evs)} warm-up steps)")
+    busy = len(evs) * (st.mean(g_up) + st.mean(g_wr)) + sum(g_de)
     wall_ms, last_ms = (t1 - t0) * 1e3, (host_marks[-1][5] - t0) * 1e3
     # the host enqueues ahead of the device unless the last step is enqueued near the wall's end
     bound = "host-bound" if last_ms > 0.9 * wall_ms else "device-bound: the host ran ahead"
@@ -320,14 +321,14 @@ def run(args):
         alloc.block_tables(seq_ids, max_blocks, stage_tab[i], stage_len[i])
         stage_slot[i][:] = s
         h2 = time.perf_counter()
-        if events is not None:
+        if events is not None and events[0] is not None:
             events[0].record()
         pk.pa_upload(meta_d, staging[i])
         if cow:
             pairs = torch.tensor(cow, dtype=torch.int64).to(dev, non_blocking=False)
             for l in range(layers):
                 pk.pa_copy_blocks(kc[l], vc[l], pairs)
-        if events is not None:
+        if events is not None and events[1] is not None:
             events[1].record()
         h3 = time.perf_counter()
         launch[0]()
@@ -341,8 +342,21 @@ def run(args):
         host_marks.append((h0, h1, h2, h3, h4, h5))
         return stage_len[i].copy()
 
+    # events per step: before the upload, after it, after the writes, after the decodes; with no
+    # separate writes (the fused step) the after-upload event stands for the after-writes one.
+    # The last warm-up steps carry all of them, for the report of where a step's device time goes;
+    # the timed steps only the two around the decodes (the roofline's), so that no other event
+    # sits in the timed region.
+    def step_events(full):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        if not full:
+            return (None, None, e[2], e[3])
+        return (e[0], e[1], e[1] if fused else e[2], e[3])
+
+    n_phase = min(3, warm)
+    phase_evs = [step_events(True) for _ in range(n_phase)]
     for i in range(warm):
-        step(i)
+        step(i, phase_evs[i - (warm - n_phase)] if i >= warm - n_phase else None)
     torch.cuda.synchronize()
     launch = (write_all, decode_all)
     if args.graph:
@@ -364,14 +378,7 @@ def run(args):
         launch = (g_write.replay if wr_c else (lambda: None), g_decode.replay)
     log(f"warmup done ({warm} steps); timing {steps} steps ({'HIP graphs' if args.graph else 'host launches'})")
 
-    # events per step: before the upload, after it, after the writes, after the decodes; with no
-    # separate writes (the fused step) the after-upload event stands for the after-writes one, so
-    # that no empty event pair sits in the timed region
-    def step_events():
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        return (e[0], e[1], e[1] if fused else e[2], e[3])
-
-    evs = [step_events() for _ in range(steps)]
+    evs = [step_events(False) for _ in range(steps)]
     lens_per_step = []
     host_marks.clear()
     torch.cuda.synchronize()
@@ -383,7 +390,7 @@ def run(args):
         t1 = time.perf_counter()
     wall = t1 - t0
     log(f"timed {steps} steps in {wall * 1e3:.2f} ms")
-    report_phases(host_marks, evs, t0, t1, layers)
+    report_phases(host_marks, evs, t0, t1, layers, phase_evs)
     if args.graph:
         # the graphs' last outputs against eager launches on the same inputs: bit for bit
         # (decode is deterministic; the write of the same rows again changes nothing)
