@@ -1770,14 +1770,14 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_mfma_kernel(const DecodeArg
         total = int64_t(F + B) * a.hkv;
     }
     // Items are dealt round robin.  In the DYN instances (launched for item lists of a few long
-    // requests over bf16 caches), when nearly every item is a full partition (all of the same size), the last one
-    // and a half rounds are instead handed out by a counter after the tickets, so that
-    // work-groups on faster compute units take more of them; each claim is issued when a
-    // work-group starts its current item and read when that item ends, and the last work-group
-    // to exit resets the counter and its own.  Items of mixed sizes (ragged batches) stay dealt
-    // round robin: there, long and short items interleaved keep more bytes in flight than a
-    // counter's claims, which also stall the waits of the claiming wave.  The other instances
-    // carry none of this code.
+    // requests over bf16 caches), when nearly every item is a full partition (all of one size),
+    // the last one and a half rounds are instead handed out by a counter after the tickets, so
+    // that work-groups on faster compute units take more of them; each claim is issued when a
+    // work-group starts its current item and read when that item ends (a work-group's last claim
+    // has returned before it counts itself out), and the last work-group to exit resets the
+    // counter and its own.  Items of mixed sizes (ragged batches) stay dealt round robin: there,
+    // long and short items interleaved keep more bytes in flight than a counter's claims, which
+    // also stall the waits of the claiming wave.  The other instances carry none of this code.
     int* const queue = (DYN && a.list && a.ws_ctr != nullptr)
                            ? a.ws_ctr + int64_t(a.num_seqs) * hq * a.ctr_stride : nullptr;
     const int nslots = a.list ? int(gridDim.x) : 1;
