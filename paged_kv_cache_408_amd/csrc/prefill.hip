@@ -112,9 +112,17 @@ __global__ __launch_bounds__(64 * pwaves(CDT), 2) void prefill_kernel(const Pref
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c32 = lane & 31, hi = lane >> 5;
     const int hq = a.hkv * G;
-    const int b = blockIdx.x % a.num_seqs;
-    const int qt = a.qtiles - 1 - static_cast<int>(blockIdx.x / a.num_seqs);   // longest tiles first
-    const int g = blockIdx.y;
+    // Work-groups are dealt to the 8 XCDs in turn (work-group i to XCD i % 8).  Work unit
+    // u = (request, KV head) belongs to XCD u % 8, which runs its units one after another, the
+    // longest query tiles of each first: the work-groups resident on an XCD share one or two
+    // units' K/V in that XCD's L2, and a long request's heads go to different XCDs.
+    const int xcd = static_cast<int>(blockIdx.x % 8);
+    const int jx = static_cast<int>(blockIdx.x / 8);
+    const int u = (jx / a.qtiles) * 8 + xcd;
+    if (u >= a.num_seqs * a.hkv) return;                 // the grid is rounded up to 8 units
+    const int qt = a.qtiles - 1 - jx % a.qtiles;
+    const int g = u % a.hkv;
+    const int b = u / a.hkv;
 
     const int q0 = __builtin_amdgcn_readfirstlane(gld_i32(a.query_start + b));
     const int q1 = __builtin_amdgcn_readfirstlane(gld_i32(a.query_start + b + 1));
@@ -372,18 +380,39 @@ __global__ __launch_bounds__(64 * pwaves(CDT), 2) void prefill_kernel(const Pref
         auto scores = [&](int sb) {
             const PA_LDS unsigned char* kp = kt + 32 * sb * ROWB;
             f32x16v acc_s = f32x16v{};
+            U4 kf[NQK];                                // every read in flight before the first product
 #pragma unroll
-            for (int j = 0; j < NQK; ++j) {
-                const U4 kv = lds_ld16(kp + ko[j]);
-                acc_s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v, kv),
+            for (int j = 0; j < NQK; ++j) kf[j] = lds_ld16(kp + ko[j]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < NQK; ++j)
+                acc_s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v, kf[j]),
                                                                 __builtin_bit_cast(bf16x8v, qb[j]), acc_s, 0, 0, 0);
-            }
             return acc_s;
         };
         f32x16v s[2];
-        s[0] = scores(0);
-        if (nsb == 2) s[1] = scores(1);
-        else s[1] = f32x16v{} - INFINITY;             // past every row of the wave
+        if (nsb == 2) {
+            // both halves' K operands read ahead of their products, the two chains interleaved
+            U4 k0[NQK], k1[NQK];
+#pragma unroll
+            for (int j = 0; j < NQK; ++j) {
+                k0[j] = lds_ld16(kt + ko[j]);
+                k1[j] = lds_ld16(kt + 32 * ROWB + ko[j]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            s[0] = f32x16v{};
+            s[1] = f32x16v{};
+#pragma unroll
+            for (int j = 0; j < NQK; ++j) {
+                s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v, k0[j]),
+                                                               __builtin_bit_cast(bf16x8v, qb[j]), s[0], 0, 0, 0);
+                s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v, k1[j]),
+                                                               __builtin_bit_cast(bf16x8v, qb[j]), s[1], 0, 0, 0);
+            }
+        } else {
+            s[0] = scores(0);
+            s[1] = f32x16v{} - INFINITY;              // past every row of the wave
+        }
         // causal mask (tiles that reach past the wave's first row only), then one online-softmax
         // update per tile: the maximum is taken on the raw scores and the scale is folded into
         // the exponent's fused multiply-add
@@ -528,9 +557,9 @@ extern "C" int pa_prefill(void* out, const void* q, const void* k_cache, const v
         return fail(PA_ERR_UNSUPPORTED, "pa_prefill: %d query heads per KV head not in {1, 4, 8}", G);
     const int TQ = kWRows * pwaves(cache_dtype) / G;   // new tokens per work-group
     const int64_t qtiles = (int64_t(max_query_len) + TQ - 1) / TQ;
-    if (qtiles * num_seqs > 0x7fffffff || num_kv_heads > 65535)
-        return fail(PA_ERR_UNSUPPORTED, "pa_prefill: grid of %lld x %d work-groups", (long long)(qtiles * num_seqs),
-                    num_kv_heads);
+    const int64_t units8 = (int64_t(num_seqs) * num_kv_heads + 7) / 8 * 8;   // (request, KV head) units
+    if (qtiles * units8 > 0x7fffffff)
+        return fail(PA_ERR_UNSUPPORTED, "pa_prefill: grid of %lld work-groups", (long long)(qtiles * units8));
 
     PrefillArgs a{};
     a.out = out;
@@ -551,7 +580,7 @@ extern "C" int pa_prefill(void* out, const void* q, const void* k_cache, const v
     a.qtiles = static_cast<int>(qtiles);
     a.num_blocks = num_blocks;
     a.num_query_tokens = num_query_tokens;
-    const dim3 grid(static_cast<unsigned>(qtiles * num_seqs), static_cast<unsigned>(num_kv_heads));
+    const dim3 grid(static_cast<unsigned>(qtiles * units8));
     hipStream_t st = static_cast<hipStream_t>(stream);
     switch (cache_dtype) {
         case PA_DTYPE_FP8_E4M3:
