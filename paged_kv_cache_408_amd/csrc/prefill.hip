@@ -58,6 +58,7 @@ struct PrefillArgs {
     int max_query_len;
     int max_seq_len;
     int qtiles;                 // query tiles per request in the grid
+    int ugrp;                   // units an XCD runs side by side (1 or 2)
     int64_t num_blocks;
     int64_t num_query_tokens;
 };
@@ -113,14 +114,18 @@ __global__ __launch_bounds__(64 * pwaves(CDT), 2) void prefill_kernel(const Pref
     const int c32 = lane & 31, hi = lane >> 5;
     const int hq = a.hkv * G;
     // Work-groups are dealt to the 8 XCDs in turn (work-group i to XCD i % 8).  Work unit
-    // u = (request, KV head) belongs to XCD u % 8, which runs its units one after another, the
-    // longest query tiles of each first: the work-groups resident on an XCD share one or two
-    // units' K/V in that XCD's L2, and a long request's heads go to different XCDs.
+    // u = (request, KV head) belongs to XCD u % 8, which runs its units in groups of ugrp side by
+    // side, one group after another, the longest query tiles of the group first (the group's
+    // units alternating): the work-groups resident on an XCD share one or two units' K/V in that
+    // XCD's L2, a long request's heads go to different XCDs, and the last work-groups an XCD
+    // starts are the group's shortest.
     const int xcd = static_cast<int>(blockIdx.x % 8);
     const int jx = static_cast<int>(blockIdx.x / 8);
-    const int u = (jx / a.qtiles) * 8 + xcd;
-    if (u >= a.num_seqs * a.hkv) return;                 // the grid is rounded up to 8 units
-    const int qt = a.qtiles - 1 - jx % a.qtiles;
+    const int gw = a.qtiles * a.ugrp;                       // work-groups of one group of units
+    const int jr = jx % gw;
+    const int u = ((jx / gw) * a.ugrp + jr % a.ugrp) * 8 + xcd;
+    if (u >= a.num_seqs * a.hkv) return;                 // the grid is rounded up to whole groups
+    const int qt = a.qtiles - 1 - jr / a.ugrp;
     const int g = u % a.hkv;
     const int b = u / a.hkv;
 
@@ -557,7 +562,9 @@ extern "C" int pa_prefill(void* out, const void* q, const void* k_cache, const v
         return fail(PA_ERR_UNSUPPORTED, "pa_prefill: %d query heads per KV head not in {1, 4, 8}", G);
     const int TQ = kWRows * pwaves(cache_dtype) / G;   // new tokens per work-group
     const int64_t qtiles = (int64_t(max_query_len) + TQ - 1) / TQ;
-    const int64_t units8 = (int64_t(num_seqs) * num_kv_heads + 7) / 8 * 8;   // (request, KV head) units
+    const int64_t upx = (int64_t(num_seqs) * num_kv_heads + 7) / 8;          // (request, KV head) units per XCD
+    const int ugrp = upx >= 2 ? 2 : 1;
+    const int64_t units8 = (upx + ugrp - 1) / ugrp * ugrp * 8;    // units, whole groups on every XCD
     if (qtiles * units8 > 0x7fffffff)
         return fail(PA_ERR_UNSUPPORTED, "pa_prefill: grid of %lld work-groups", (long long)(qtiles * units8));
 
@@ -578,6 +585,7 @@ extern "C" int pa_prefill(void* out, const void* q, const void* k_cache, const v
     a.max_query_len = max_query_len;
     a.max_seq_len = max_seq_len;
     a.qtiles = static_cast<int>(qtiles);
+    a.ugrp = ugrp;
     a.num_blocks = num_blocks;
     a.num_query_tokens = num_query_tokens;
     const dim3 grid(static_cast<unsigned>(qtiles * units8));
